@@ -1,0 +1,470 @@
+/* Plain CPU oracle for DeepSeek-V4.1 sparse latent attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the bench's CPU-baseline leg use this file; the
+ * GPU library never includes, links or calls it, and the two share no code. It is written
+ * for reading, not speed: one query at a time, sums in index order, no blocking or fusion.
+ * Citations name the page and the passage (see sa_oracle.h for the page list).
+ */
+#include "sa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------------ */
+/* bf16 <-> f32. [attn-docs] precision paragraph: tensors are bf16, arithmetic is f32.   */
+/* The pages do not name a rounding mode for "returns bf16"; the reading taken is        */
+/* round-to-nearest-even, which is what a torch .to(bfloat16) cast does.                 */
+/* ------------------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+float orc_bf16_to_f32(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+uint16_t orc_f32_to_bf16(float f)
+{
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);          /* NaN stays a (quiet) NaN */
+    uint32_t upper = u >> 16;                             /* truncated result */
+    uint32_t lower = u & 0xffffu;                         /* discarded bits */
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;                                       /* nearest, ties to even */
+    return (uint16_t)upper;
+}
+
+void orc_f32_to_bf16_array(const float *x, uint16_t *y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_bf16(x[i]);
+}
+
+void orc_bf16_to_f32_array(const uint16_t *x, float *y, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_bf16_to_f32(x[i]);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* pow2_ceil. [attn-docs] pow2_ceil: 2**ceil(log2 v) for a positive normal f32, read off  */
+/* the IEEE fields. With biased exponent E and mantissa M, v = 2^(E-127) * (1 + M/2^23); */
+/* log2 v is an integer exactly when M == 0, otherwise its ceiling is E-127+1.           */
+/* ------------------------------------------------------------------------------------ */
+float orc_pow2_ceil(float v)
+{
+    uint32_t u = f32_bits(v);
+    uint32_t e = (u >> 23) & 0xffu;
+    uint32_t m = u & 0x7fffffu;
+    if (m != 0) e += 1;
+    return bits_f32(e << 23);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* e4m3. [attn-docs] act_quant_inplace: values go to e4m3 with round-to-nearest-even,    */
+/* clamped. The 448 bound of the same passage is the OCP "e4m3fn" variant: bias 7,       */
+/* 3 mantissa bits, largest finite 1.75 * 2^8 = 448, subnormal step 2^-9, no infinity.   */
+/* Reading: the clamp to +-448 comes before rounding, so nothing ever maps to NaN.       */
+/* ------------------------------------------------------------------------------------ */
+
+/* round a non-negative float that is exactly representable as k/2 or finer to the       */
+/* nearest integer, ties to even (done by hand so that no rounding mode is assumed)      */
+static float round_half_even(float v)
+{
+    float fl = floorf(v);
+    float frac = v - fl;                  /* exact: v and fl share the exponent range */
+    if (frac > 0.5f) return fl + 1.0f;
+    if (frac < 0.5f) return fl;
+    return (fmodf(fl, 2.0f) == 0.0f) ? fl : fl + 1.0f;
+}
+
+uint8_t orc_e4m3_encode(float x)
+{
+    uint8_t sign = (f32_bits(x) >> 31) ? 0x80 : 0x00;
+    float a = fabsf(x);
+    if (a > 448.0f) a = 448.0f;                               /* clamp */
+    if (a < 0.015625f) {                                      /* below 2^-6: subnormal grid */
+        float q = round_half_even(a * 512.0f);                /* units of 2^-9, exact scaling */
+        return (uint8_t)(sign | (uint8_t)q);                  /* q == 8 is the code of 2^-6 */
+    }
+    int e2;
+    frexpf(a, &e2);                                           /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                                           /* a in [2^e, 2^(e+1)) */
+    float q = round_half_even(ldexpf(a, 3 - e));              /* units of 2^(e-3): q in [8, 16] */
+    if (q == 16.0f) { q = 8.0f; e += 1; }
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)((int)q - 8));
+}
+
+float orc_e4m3_decode(uint8_t c)
+{
+    int sign = c >> 7;
+    int e = (c >> 3) & 0xf;
+    int m = c & 0x7;
+    float v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexpf((float)m, -9);
+    else v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Block-32 ue8m0 round trip. [attn-docs] act_quant_inplace and FP8_BLOCK (32): for each */
+/* block of 32 consecutive elements of a row, scale = pow2_ceil(max(amax, 1e-4) / 448),  */
+/* values to e4m3 (RNE, clamped), dequantised and stored back as bf16. The precision     */
+/* paragraph of the same page states the round trip is bf16-exact.                       */
+/* Reading: the whole row is quantised, rope tail included ("the KV row quantised").     */
+/* The scale byte is the biased exponent of the power-of-two scale (ue8m0).              */
+/* ------------------------------------------------------------------------------------ */
+int orc_act_quant_rows(const uint16_t *x, int64_t rows, int32_t d, uint16_t *y,
+                       uint8_t *codes, uint8_t *scale_bytes)
+{
+    if (!x || !y || rows < 0 || d <= 0 || d % 32 != 0) return -1;
+    const int nb = d / 32;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t *xb = x + r * d + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float v = fabsf(orc_bf16_to_f32(xb[i]));
+                if (v > amax) amax = v;
+            }
+            if (amax < 1e-4f) amax = 1e-4f;
+            float s = orc_pow2_ceil(amax / 448.0f);
+            uint8_t qc[32];
+            for (int i = 0; i < 32; ++i) {
+                float v = orc_bf16_to_f32(xb[i]) / s;          /* exact: s is a power of two */
+                qc[i] = orc_e4m3_encode(v);
+            }
+            uint16_t *yb = y + r * d + b * 32;
+            for (int i = 0; i < 32; ++i)
+                yb[i] = orc_f32_to_bf16(orc_e4m3_decode(qc[i]) * s);
+            if (codes) memcpy(codes + r * d + b * 32, qc, 32);
+            if (scale_bytes) scale_bytes[r * nb + b] = (uint8_t)((f32_bits(s) >> 23) & 0xffu);
+        }
+    }
+    return 0;
+}
+
+int orc_fp8_storage_decode(const uint8_t *codes, const uint8_t *scale_bytes, int64_t rows,
+                           int32_t d, uint16_t *y)
+{
+    if (!codes || !scale_bytes || !y || rows < 0 || d <= 0 || d % 32 != 0) return -1;
+    const int nb = d / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int i = 0; i < d; ++i) {
+            float s = ldexpf(1.0f, (int)scale_bytes[r * nb + i / 32] - 127);
+            y[r * d + i] = orc_f32_to_bf16(orc_e4m3_decode(codes[r * d + i]) * s);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Window index lists. [attn-docs] window_topk_idxs: [queries][cols] of slot indices,    */
+/* -1 for a slot holding nothing; prefill is one causal window per query into the chunk */
+/* itself, decode is the whole ring, oldest first. The ring-cache paragraph fixes the    */
+/* slot of token p as p mod window.                                                      */
+/* Readings: prefill cols = min(seqlen, window) (the list is [queries][cols], not        */
+/* [queries][window]); valid entries come first, oldest first, -1 padding at the end;    */
+/* decode lets every sequence carry its own start position; start_pos > 0 with more than */
+/* one query (chunked prefill) is not defined by the pages and is rejected.              */
+/* ------------------------------------------------------------------------------------ */
+int orc_window_cols(int32_t window, int32_t seqlen, const int32_t *start_pos, int32_t nseq,
+                    int32_t *cols)
+{
+    if (window <= 0 || seqlen <= 0 || nseq <= 0 || !start_pos || !cols) return -1;
+    int any_pos = 0;
+    for (int32_t n = 0; n < nseq; ++n) {
+        if (start_pos[n] < 0) return -1;
+        if (start_pos[n] > 0) any_pos = 1;
+    }
+    if (any_pos && seqlen > 1) return -2;
+    *cols = any_pos ? window : (seqlen < window ? seqlen : window);
+    return 0;
+}
+
+int orc_window_topk_idxs(int32_t window, int32_t seqlen, const int32_t *start_pos, int32_t nseq,
+                         int32_t *idx, int32_t *cols)
+{
+    int32_t c;
+    int rc = orc_window_cols(window, seqlen, start_pos, nseq, &c);
+    if (rc) return rc;
+    if (!idx) return -1;
+    *cols = c;
+    for (int32_t n = 0; n < nseq; ++n) {
+        int32_t P = start_pos[n];
+        for (int32_t t = 0; t < seqlen; ++t) {
+            int32_t *row = idx + ((int64_t)n * seqlen + t) * c;
+            if (P == 0 && seqlen > 1) {
+                /* prefill: chunk rows lo..t, lo = max(0, t - window + 1) */
+                int32_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
+                for (int32_t j = 0; j < c; ++j) row[j] = (lo + j <= t) ? lo + j : -1;
+            } else if (P == 0 && seqlen == 1 && c == 1) {
+                row[0] = 0;                              /* a one-token prefill */
+            } else if (P >= window - 1) {
+                /* full ring: the oldest token P-window+1 sits in slot (P+1) mod window */
+                for (int32_t j = 0; j < c; ++j) row[j] = (P + 1 + j) % window;
+            } else {
+                /* ring holds tokens 0..P in slots 0..P */
+                for (int32_t j = 0; j < c; ++j) row[j] = (j <= P) ? j : -1;
+            }
+        }
+    }
+    return 0;
+}
+
+void orc_ring_prefill(uint16_t *ring, int32_t window, int32_t row_elems,
+                      const uint16_t *chunk_rows, int32_t seqlen)
+{
+    int32_t first = seqlen - window > 0 ? seqlen - window : 0;
+    for (int32_t p = first; p < seqlen; ++p)
+        memcpy(ring + (int64_t)(p % window) * row_elems, chunk_rows + (int64_t)p * row_elems,
+               (size_t)row_elems * 2);
+}
+
+void orc_ring_decode(uint16_t *ring, int32_t window, int32_t row_elems, const uint16_t *row,
+                     int32_t pos)
+{
+    memcpy(ring + (int64_t)(pos % window) * row_elems, row, (size_t)row_elems * 2);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* sparse_attn. [attn-docs] sparse_attn: per query and head, a softmax over the gathered */
+/* rows plus the sink, the sink entering the denominator only, all in f32, output bf16;  */
+/* q [s][h][d], kv [rows][d], idx [s][topk]. [attn-fwd] Attention.forward calls it with  */
+/* the per-head f32 attn_sink and softmax_scale = head_dim^-0.5; the same latent row is   */
+/* key and value. For the gathered set J = {j : idx_j >= 0}:                             */
+/*   s_j = scale * sum_k q[k] kv[idx_j][k]                                               */
+/*   p_j = exp(s_j) / (sum_{j in J} exp(s_j) + exp(sink))                                */
+/*   o   = sum_{j in J} p_j kv[idx_j]        -> bf16                                     */
+/* Readings: the sink is a raw logit (not multiplied by scale); any negative index is a  */
+/* skip; an empty J gives o = 0; a duplicated index counts once per occurrence. The      */
+/* exponentials are taken relative to m = max(sink, max s_j), which leaves every p_j     */
+/* unchanged and keeps them finite.                                                      */
+/* ------------------------------------------------------------------------------------ */
+static int check_problem(const orc_attn_problem *p, const int64_t *qsel, int64_t nsel)
+{
+    if (!p || !p->q || !p->kv || !p->sink || !p->idx) return -1;
+    if (p->b <= 0 || p->s <= 0 || p->h <= 0 || p->d <= 0 || p->topk <= 0 || p->kv_rows <= 0)
+        return -1;
+    int64_t nq = (int64_t)p->b * p->s;
+    if (qsel) {
+        for (int64_t i = 0; i < nsel; ++i)
+            if (qsel[i] < 0 || qsel[i] >= nq) return -1;
+    } else if (nsel != nq) {
+        return -1;
+    }
+    for (int64_t i = 0; i < nsel; ++i) {
+        int64_t qi = qsel ? qsel[i] : i;
+        const int32_t *row = p->idx + (qi / p->s) * p->idx_seq_stride + (qi % p->s) * p->topk;
+        for (int32_t j = 0; j < p->topk; ++j)
+            if (row[j] >= p->kv_rows) return -1;
+    }
+    return 0;
+}
+
+static void attn_one_query_f32(const orc_attn_problem *p, int64_t qi, uint16_t *out,
+                               float *srow, float *acc)
+{
+    const int64_t seq = qi / p->s, t = qi % p->s;
+    const int32_t *idx = p->idx + seq * p->idx_seq_stride + t * p->topk;
+    const uint16_t *kv = p->kv + seq * p->kv_seq_stride;
+    for (int32_t hh = 0; hh < p->h; ++hh) {
+        const uint16_t *q = p->q + seq * p->q_seq_stride + (t * p->h + hh) * (int64_t)p->d;
+        /* scores */
+        float m = p->sink[hh];
+        int any = 0;
+        for (int32_t j = 0; j < p->topk; ++j) {
+            if (idx[j] < 0) continue;
+            const uint16_t *k = kv + (int64_t)idx[j] * p->d;
+            float dot = 0.0f;
+            for (int32_t c = 0; c < p->d; ++c)
+                dot += orc_bf16_to_f32(q[c]) * orc_bf16_to_f32(k[c]);
+            srow[j] = p->scale * dot;
+            if (srow[j] > m) m = srow[j];
+            any = 1;
+        }
+        uint16_t *o = out + (int64_t)hh * p->d;
+        if (!any) {                                       /* no rows: only the sink */
+            for (int32_t c = 0; c < p->d; ++c) o[c] = orc_f32_to_bf16(0.0f);
+            continue;
+        }
+        /* denominator: the gathered rows plus the sink */
+        float l = expf(p->sink[hh] - m);
+        for (int32_t j = 0; j < p->topk; ++j)
+            if (idx[j] >= 0) l += expf(srow[j] - m);
+        /* weighted sum of the same rows */
+        for (int32_t c = 0; c < p->d; ++c) acc[c] = 0.0f;
+        for (int32_t j = 0; j < p->topk; ++j) {
+            if (idx[j] < 0) continue;
+            float pj = expf(srow[j] - m) / l;
+            const uint16_t *v = kv + (int64_t)idx[j] * p->d;
+            for (int32_t c = 0; c < p->d; ++c) acc[c] += pj * orc_bf16_to_f32(v[c]);
+        }
+        for (int32_t c = 0; c < p->d; ++c) o[c] = orc_f32_to_bf16(acc[c]);
+    }
+}
+
+int orc_sparse_attn(const orc_attn_problem *p, const int64_t *qsel, int64_t nsel,
+                    uint16_t *out, int32_t nthreads)
+{
+    if (!out || nsel < 0 || check_problem(p, qsel, nsel)) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        float *srow = (float *)malloc(sizeof(float) * (size_t)p->topk);
+        float *acc = (float *)malloc(sizeof(float) * (size_t)p->d);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < nsel; ++i)
+            attn_one_query_f32(p, qsel ? qsel[i] : i, out + i * (int64_t)p->h * p->d, srow, acc);
+        free(srow);
+        free(acc);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* f64 twin of the same definition, unrounded output; tests only */
+static void attn_one_query_f64(const orc_attn_problem *p, int64_t qi, double *out,
+                               double *srow, double *acc)
+{
+    const int64_t seq = qi / p->s, t = qi % p->s;
+    const int32_t *idx = p->idx + seq * p->idx_seq_stride + t * p->topk;
+    const uint16_t *kv = p->kv + seq * p->kv_seq_stride;
+    for (int32_t hh = 0; hh < p->h; ++hh) {
+        const uint16_t *q = p->q + seq * p->q_seq_stride + (t * p->h + hh) * (int64_t)p->d;
+        double m = p->sink[hh];
+        int any = 0;
+        for (int32_t j = 0; j < p->topk; ++j) {
+            if (idx[j] < 0) continue;
+            const uint16_t *k = kv + (int64_t)idx[j] * p->d;
+            double dot = 0.0;
+            for (int32_t c = 0; c < p->d; ++c)
+                dot += (double)orc_bf16_to_f32(q[c]) * (double)orc_bf16_to_f32(k[c]);
+            srow[j] = (double)p->scale * dot;
+            if (srow[j] > m) m = srow[j];
+            any = 1;
+        }
+        double *o = out + (int64_t)hh * p->d;
+        for (int32_t c = 0; c < p->d; ++c) o[c] = 0.0;
+        if (!any) continue;
+        double l = exp((double)p->sink[hh] - m);
+        for (int32_t j = 0; j < p->topk; ++j)
+            if (idx[j] >= 0) l += exp(srow[j] - m);
+        for (int32_t c = 0; c < p->d; ++c) acc[c] = 0.0;
+        for (int32_t j = 0; j < p->topk; ++j) {
+            if (idx[j] < 0) continue;
+            double pj = exp(srow[j] - m) / l;
+            const uint16_t *v = kv + (int64_t)idx[j] * p->d;
+            for (int32_t c = 0; c < p->d; ++c) acc[c] += pj * (double)orc_bf16_to_f32(v[c]);
+        }
+        for (int32_t c = 0; c < p->d; ++c) o[c] = acc[c];
+    }
+}
+
+int orc_sparse_attn_f64(const orc_attn_problem *p, const int64_t *qsel, int64_t nsel,
+                        double *out, int32_t nthreads)
+{
+    if (!out || nsel < 0 || check_problem(p, qsel, nsel)) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)p->topk);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)p->d);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t i = 0; i < nsel; ++i)
+            attn_one_query_f64(p, qsel ? qsel[i] : i, out + i * (int64_t)p->h * p->d, srow, acc);
+        free(srow);
+        free(acc);
+    }
+    (void)nthreads;
+    return 0;
+}
+
+int orc_sparse_attn_weights_f64(const orc_attn_problem *p, int64_t query, int32_t head,
+                                double *w, double *sink_share)
+{
+    if (!w || !sink_share || check_problem(p, &query, 1) || head < 0 || head >= p->h) return -1;
+    const int64_t seq = query / p->s, t = query % p->s;
+    const int32_t *idx = p->idx + seq * p->idx_seq_stride + t * p->topk;
+    const uint16_t *kv = p->kv + seq * p->kv_seq_stride;
+    const uint16_t *q = p->q + seq * p->q_seq_stride + (t * p->h + head) * (int64_t)p->d;
+    double m = p->sink[head];
+    for (int32_t j = 0; j < p->topk; ++j) {
+        w[j] = 0.0;
+        if (idx[j] < 0) continue;
+        const uint16_t *k = kv + (int64_t)idx[j] * p->d;
+        double dot = 0.0;
+        for (int32_t c = 0; c < p->d; ++c)
+            dot += (double)orc_bf16_to_f32(q[c]) * (double)orc_bf16_to_f32(k[c]);
+        w[j] = (double)p->scale * dot;
+        if (w[j] > m) m = w[j];
+    }
+    double l = exp((double)p->sink[head] - m);
+    for (int32_t j = 0; j < p->topk; ++j)
+        if (idx[j] >= 0) l += exp(w[j] - m);
+    for (int32_t j = 0; j < p->topk; ++j)
+        w[j] = idx[j] >= 0 ? exp(w[j] - m) / l : 0.0;
+    *sink_share = exp((double)p->sink[head] - m) / l;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Rotary table. [attn-fwd] precompute_freqs_cis with original_seq_len = 0 (the no-YaRN  */
+/* form that [attn-docs] freqs_cis names): freq_i = 1 / base^(2i/rd), angle = pos *      */
+/* freq_i, entry = (cos, sin) of the angle. Computed in f32 as the page does.           */
+/* ------------------------------------------------------------------------------------ */
+void orc_freqs_cis(int32_t rd, int32_t max_pos, float base, float *cos_sin)
+{
+    const int32_t half = rd / 2;
+    for (int32_t i = 0; i < half; ++i) {
+        float freq = 1.0f / powf(base, (float)(2 * i) / (float)rd);
+        for (int32_t pos = 0; pos < max_pos; ++pos) {
+            float ang = (float)pos * freq;
+            cos_sin[((int64_t)pos * half + i) * 2 + 0] = cosf(ang);
+            cos_sin[((int64_t)pos * half + i) * 2 + 1] = sinf(ang);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Rotary. [attn-fwd] apply_rotary_emb: adjacent element pairs (x0, x1) are the complex  */
+/* number x0 + i x1, multiplied in f32 by freqs_cis[pos] (its conjugate when inverse)    */
+/* and written back into the bf16 tensor. [attn-fwd] Attention.forward applies the       */
+/* inverse to the last rope_head_dim elements of sparse_attn's output.                   */
+/*   forward: (a, b) -> (a c - b s, a s + b c);  inverse: (a, b) -> (a c + b s, b c - a s) */
+/* ------------------------------------------------------------------------------------ */
+int orc_apply_rotary(uint16_t *x, int64_t n, int32_t h, int32_t d, int32_t rd,
+                     const float *cos_sin, int32_t max_pos, const int32_t *pos, int32_t inverse)
+{
+    if (!x || n < 0 || h <= 0 || d <= 0 || rd < 0 || rd > d || rd % 2) return -1;
+    if (rd == 0) return 0;
+    if (!cos_sin || !pos) return -1;
+    const int32_t half = rd / 2;
+    for (int64_t r = 0; r < n; ++r) {
+        if (pos[r] < 0 || pos[r] >= max_pos) return -1;
+        for (int32_t hh = 0; hh < h; ++hh) {
+            uint16_t *row = x + (r * h + hh) * (int64_t)d + (d - rd);
+            for (int32_t i = 0; i < half; ++i) {
+                float c = cos_sin[((int64_t)pos[r] * half + i) * 2 + 0];
+                float s = cos_sin[((int64_t)pos[r] * half + i) * 2 + 1];
+                if (inverse) s = -s;                     /* conjugate */
+                float a = orc_bf16_to_f32(row[2 * i]);
+                float b = orc_bf16_to_f32(row[2 * i + 1]);
+                float re = a * c - b * s;
+                float im = a * s + b * c;
+                row[2 * i] = orc_f32_to_bf16(re);
+                row[2 * i + 1] = orc_f32_to_bf16(im);
+            }
+        }
+    }
+    return 0;
+}
