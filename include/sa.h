@@ -1,0 +1,149 @@
+/* sa.h -- C ABI of libsa.so, DeepSeek-V4.1 sparse latent attention for AMD MI355X (gfx950).
+ *
+ * The operation is sparse_attn as the attention API docs define it
+ * (docs.atlascybernetics.ai/api/spark_model/layers/deepseek_v41_ref/attn/, "sparse_attn" and
+ * the precision paragraph) and as Attention.forward calls it
+ * (atlas.klimoza.dev/models/deepseek-v4.1/.../attention/output, Attention.forward): for every
+ * query and head, gather the latent KV rows that an index list names (negative = skip),
+ * score them as q.k * softmax_scale with the same row serving as key and value, take a
+ * softmax in f32 whose denominator also holds exp(attn_sink[head]), and return the weighted
+ * sum of the rows in bf16.
+ *
+ * Conventions shared by every entry point:
+ *   - Device pointers are caller-owned (for example PyTorch tensors). The library never
+ *     allocates, frees or retains them, and holds no state between calls apart from a
+ *     per-device cache of the compute-unit count.
+ *   - Strides are counted in elements of the pointed-to type.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the null stream)
+ *     and runs asynchronously. The return value reports host-side argument validation and
+ *     launch errors only; argument checks happen before any HIP call is made.
+ *   - bf16 means the 16-bit bfloat16 format; out-of-kernel values are never converted.
+ *   - Calls are thread-safe. Two calls that write the same output or workspace race.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+/* status codes */
+enum {
+    SA_OK = 0,
+    SA_ERR_INVALID = -1,      /* a null pointer, a negative or zero size, a bad stride ... */
+    SA_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement */
+    SA_ERR_HIP = -3,          /* the HIP runtime reported an error at launch */
+    SA_ERR_WORKSPACE = -4     /* workspace missing or smaller than sa_sparse_attn_workspace */
+};
+
+/* KV storage formats */
+enum {
+    SA_KV_BF16 = 0,           /* kv: bf16 [b][kv_rows][d] */
+    SA_KV_FP8_E4M3_B32 = 1    /* kv: e4m3fn bytes [b][kv_rows][d] + kv_scale: e8m0 bytes
+                                 [b][kv_rows][d/32]; value = e4m3 * 2^(scale_byte - 127),
+                                 the storage form of sa_quant_kv_fp8 */
+};
+
+/* flags */
+enum {
+    SA_FLAG_CHECK_IDX = 1u    /* bounds-check every index on the device: an index >= kv_rows
+                                 is then treated as a skip and sets *err_word to 1 */
+};
+
+typedef struct sa_attn_args {
+    int32_t b;          /* sequences (>= 1) */
+    int32_t s;          /* queries per sequence (>= 1) */
+    int32_t h;          /* heads (>= 1) */
+    int32_t d;          /* latent row width: 64, 128, 256 or 512 */
+    int32_t topk;       /* index columns per query (>= 1) */
+    int32_t kv_rows;    /* rows of kv per sequence (>= 1) */
+
+    const void *q;          int64_t q_seq_stride;        /* bf16 [b][s][h][d]; each
+                                                            sequence's [s][h][d] contiguous */
+    const void *kv;         int64_t kv_seq_stride;       /* see kv_format; each sequence's
+                                                            [kv_rows][d] contiguous */
+    const uint8_t *kv_scale; int64_t kv_scale_seq_stride;/* e8m0 [b][kv_rows][d/32] for
+                                                            SA_KV_FP8_E4M3_B32, else NULL */
+    int32_t kv_format;                                   /* SA_KV_* */
+    const float *sink;                                   /* f32 [h], shared by all sequences;
+                                                            a raw logit (not scaled) */
+    const int32_t *idx;     int64_t idx_seq_stride;      /* int32 [b][s][topk]; values are rows
+                                                            of the query's own sequence; any
+                                                            negative value skips the column;
+                                                            values >= kv_rows are a caller
+                                                            error (see SA_FLAG_CHECK_IDX) */
+    float scale;                                         /* softmax_scale, e.g. d^-0.5 */
+    void *out;              int64_t out_seq_stride;      /* bf16 [b][s][h][d]; must not alias
+                                                            q, kv or idx */
+
+    /* optional inverse-RoPE epilogue (Attention.forward applies it to the output):
+       rope_dim = 0 disables it; otherwise rope_dim is even and <= d, and the last rope_dim
+       elements of every output row, taken as adjacent (real, imag) pairs, are multiplied
+       in f32 by the conjugate of (cos, sin) = rope_cos_sin[pos][pair] and rounded to bf16
+       again. */
+    int32_t rope_dim;
+    const float *rope_cos_sin; int32_t max_pos;          /* f32 [max_pos][rope_dim/2][2] */
+    const int32_t *pos;     int64_t pos_seq_stride;      /* int32 [b][s] absolute positions,
+                                                            each in [0, max_pos) */
+
+    /* split-K workspace (f32 partial results), sized by sa_sparse_attn_workspace; may be
+       NULL when that function reports 0 bytes */
+    void *workspace;        size_t workspace_bytes;
+
+    uint32_t flags;                                      /* SA_FLAG_* */
+    int32_t *err_word;                                   /* device int32, with
+                                                            SA_FLAG_CHECK_IDX only; the caller
+                                                            clears it beforehand */
+} sa_attn_args;
+
+/* sparse_attn: out[n][t][hh][:] for every sequence n, query t and head hh, as described at
+ * the top of this file, followed by the optional inverse-RoPE epilogue. Queries whose
+ * index list selects nothing produce zeros (the sink takes the whole mass). */
+int sa_sparse_attn(const sa_attn_args *a, void *stream);
+
+/* Bytes of workspace sa_sparse_attn needs for these arguments on the current device (only
+ * the sizes, kv_format and flags are read; pointers may be NULL). Writes *bytes. */
+int sa_sparse_attn_workspace(const sa_attn_args *a, size_t *bytes);
+
+/* Window index lists of the sliding-window ring cache (attention API docs,
+ * "window_topk_idxs" and the ring-cache paragraph; the slot of token p is p mod window).
+ *   start_pos == NULL: prefill of seqlen tokens from position 0 in each of nseq sequences;
+ *       cols = min(seqlen, window); row t lists chunk rows max(0, t-window+1) .. t in
+ *       ascending order, then -1 padding.
+ *   start_pos != NULL: decode, seqlen must be 1; start_pos is a device int32 [nseq] with each
+ *       sequence's position P >= 0; cols = window; the list is the ring's occupied slots
+ *       oldest first: (P+1+j) mod window when P >= window-1, else 0..P then -1 padding.
+ *       A negative P produces a row of -1.
+ *   start_pos != NULL with seqlen > 1 (a chunked prefill) is SA_ERR_UNSUPPORTED.
+ * Writes idx[n * idx_seq_stride + t * idx_row_stride + j] for j < cols and *cols (host).
+ * idx_row_stride >= cols; the columns from cols on are left untouched, so a caller can
+ * append the compressed part of the list in place. */
+int sa_window_topk_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t *start_pos,
+                        int32_t *idx, int64_t idx_seq_stride, int64_t idx_row_stride,
+                        int32_t *cols, void *stream);
+
+/* Block-32 ue8m0 fp8 quantisation of bf16 KV rows (attention API docs, "act_quant_inplace",
+ * "FP8_BLOCK" and "pow2_ceil"): for every 32 consecutive elements of a row,
+ * s = pow2_ceil(max(amax, 1e-4) / 448), codes = e4m3fn(x / s) with round-to-nearest-even
+ * after clamping to +-448. kv: bf16 [rows][d], d a multiple of 32.
+ *   e4m3_out (nullable): bytes [rows][d];   e8m0_out (nullable): bytes [rows][d/32] holding
+ *   the biased exponent of s;   bf16_out (nullable, may equal kv for in-place): the round
+ *   trip codes * s, which is exact in bf16. At least one output must be given. */
+int sa_quant_kv_fp8(const void *kv, int64_t rows, int32_t d, uint8_t *e4m3_out,
+                    uint8_t *e8m0_out, void *bf16_out, void *stream);
+
+/* A static description of a status code. */
+const char *sa_status_string(int status);
+
+/* SA_ABI_VERSION of the built library. */
+int sa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SA_H */

@@ -1,0 +1,252 @@
+"""MI355X (gfx950) sparse latent attention of DeepSeek-V4.1: Python binding of libsa.so.
+
+This module only marshals arguments: it checks tensor dtypes, shapes and devices, then
+passes raw device pointers and the current HIP stream to the C ABI declared in
+``include/sa.h``. Every step of the computation runs in the library's HIP kernels. The
+library must be built (``python -m sparse_latent_attention_attn_amd.build_lib``); importing
+a function from here without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "SaError", "lib", "sparse_attn", "sparse_attn_workspace_bytes", "window_topk_idxs",
+    "quant_kv_fp8", "rope_table", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa.so")
+
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+KV_BF16, KV_FP8 = 0, 1
+FLAG_CHECK_IDX = 1
+
+
+class SaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().sa_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class AttnArgs(C.Structure):
+    """Mirror of sa_attn_args in include/sa.h (field order and types must match)."""
+    _fields_ = [
+        ("b", C.c_int32), ("s", C.c_int32), ("h", C.c_int32), ("d", C.c_int32),
+        ("topk", C.c_int32), ("kv_rows", C.c_int32),
+        ("q", C.c_void_p), ("q_seq_stride", C.c_int64),
+        ("kv", C.c_void_p), ("kv_seq_stride", C.c_int64),
+        ("kv_scale", C.c_void_p), ("kv_scale_seq_stride", C.c_int64),
+        ("kv_format", C.c_int32),
+        ("sink", C.c_void_p),
+        ("idx", C.c_void_p), ("idx_seq_stride", C.c_int64),
+        ("scale", C.c_float),
+        ("out", C.c_void_p), ("out_seq_stride", C.c_int64),
+        ("rope_dim", C.c_int32),
+        ("rope_cos_sin", C.c_void_p), ("max_pos", C.c_int32),
+        ("pos", C.c_void_p), ("pos_seq_stride", C.c_int64),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+        ("flags", C.c_uint32), ("err_word", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libsa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_latent_attention_attn_amd.build_lib`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
+        L.sa_abi_version.restype = C.c_int
+        L.sa_abi_version.argtypes = []
+        L.sa_status_string.restype = C.c_char_p
+        L.sa_status_string.argtypes = [C.c_int]
+        L.sa_sparse_attn.restype = C.c_int
+        L.sa_sparse_attn.argtypes = [C.POINTER(AttnArgs), P]
+        L.sa_sparse_attn_workspace.restype = C.c_int
+        L.sa_sparse_attn_workspace.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
+        L.sa_window_topk_idxs.restype = C.c_int
+        L.sa_window_topk_idxs.argtypes = [I32, I32, I32, P, P, I64, I64, C.POINTER(I32), P]
+        L.sa_quant_kv_fp8.restype = C.c_int
+        L.sa_quant_kv_fp8.argtypes = [P, I64, I32, P, P, P, P]
+        if L.sa_abi_version() != 1:
+            raise RuntimeError("libsa.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(fn, status):
+    if status != SA_OK:
+        raise SaError(fn, status)
+
+
+def _need(t, dtype, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _seq_major(t, name, inner_ndim):
+    """Per-sequence blocks must be contiguous; the sequence stride may be anything."""
+    inner = t[0] if t.shape[0] > 0 else t
+    if not inner.is_contiguous():
+        raise ValueError(f"{name}: each sequence's block must be contiguous")
+    return t.stride(0)
+
+
+def make_args(q, kv, sink, idx, scale, out, *, kv_scale=None, rope=None, workspace=None,
+              err_word=None, check_idx=False) -> AttnArgs:
+    """Build sa_attn_args from tensors. q [b][s][h][d] bf16, kv [b][R][d] bf16 or uint8
+    (fp8 codes, with kv_scale uint8 [b][R][d/32]), sink f32 [h], idx int32 [b][s][topk],
+    out like q. rope = (cos_sin f32 [max_pos][rd/2][2], pos int32 [b][s]) or None."""
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    _need(out, torch.bfloat16, "out", dev)
+    _need(sink, torch.float32, "sink", dev)
+    _need(idx, torch.int32, "idx", dev)
+    if q.dim() != 4 or kv.dim() != 3 or idx.dim() != 3 or out.shape != q.shape:
+        raise ValueError("shapes: q/out [b][s][h][d], kv [b][R][d], idx [b][s][topk]")
+    b, s, h, d = q.shape
+    fmt = KV_BF16
+    if kv.dtype == torch.bfloat16:
+        _need(kv, torch.bfloat16, "kv", dev)
+    else:
+        _need(kv, torch.uint8, "kv", dev)
+        if kv_scale is None:
+            raise ValueError("fp8 kv needs kv_scale")
+        _need(kv_scale, torch.uint8, "kv_scale", dev)
+        fmt = KV_FP8
+    if kv.shape[0] != b or kv.shape[2] != d or idx.shape[:2] != (b, s) or sink.shape != (h,):
+        raise ValueError("inconsistent shapes")
+    a = AttnArgs()
+    a.b, a.s, a.h, a.d, a.topk, a.kv_rows = b, s, h, d, idx.shape[2], kv.shape[1]
+    a.q, a.q_seq_stride = _ptr(q), _seq_major(q, "q", 3)
+    a.kv, a.kv_seq_stride = _ptr(kv), _seq_major(kv, "kv", 2)
+    if fmt == KV_FP8:
+        a.kv_scale, a.kv_scale_seq_stride = _ptr(kv_scale), _seq_major(kv_scale, "kv_scale", 2)
+    a.kv_format = fmt
+    if not sink.is_contiguous():
+        raise ValueError("sink must be contiguous")
+    a.sink = _ptr(sink)
+    a.idx, a.idx_seq_stride = _ptr(idx), _seq_major(idx, "idx", 2)
+    a.scale = float(scale)
+    a.out, a.out_seq_stride = _ptr(out), _seq_major(out, "out", 3)
+    if rope is not None:
+        cs, pos = rope
+        _need(cs, torch.float32, "rope cos_sin", dev)
+        _need(pos, torch.int32, "pos", dev)
+        if not cs.is_contiguous() or cs.dim() != 3 or pos.shape != (b, s):
+            raise ValueError("rope table [max_pos][rd/2][2] contiguous, pos [b][s]")
+        a.rope_dim = cs.shape[1] * 2
+        a.rope_cos_sin, a.max_pos = _ptr(cs), cs.shape[0]
+        a.pos, a.pos_seq_stride = _ptr(pos), _seq_major(pos, "pos", 1)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    if check_idx:
+        if err_word is None:
+            raise ValueError("check_idx needs err_word")
+        _need(err_word, torch.int32, "err_word", dev)
+        a.flags, a.err_word = FLAG_CHECK_IDX, _ptr(err_word)
+    return a
+
+
+def sparse_attn_workspace_bytes(args: AttnArgs) -> int:
+    n = C.c_size_t(0)
+    _check("sa_sparse_attn_workspace", lib().sa_sparse_attn_workspace(C.byref(args), C.byref(n)))
+    return n.value
+
+
+def sparse_attn(q, kv, sink, idx, scale, *, out=None, kv_scale=None, rope=None,
+                workspace=None, err_word=None, check_idx=False):
+    """sparse_attn on the GPU (see include/sa.h). Returns out (bf16, like q). A workspace
+    is allocated with torch when none is given and the plan needs one."""
+    if out is None:
+        out = torch.empty_like(q)
+    a = make_args(q, kv, sink, idx, scale, out, kv_scale=kv_scale, rope=rope,
+                  err_word=err_word, check_idx=check_idx)
+    need = sparse_attn_workspace_bytes(a)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("sa_sparse_attn", lib().sa_sparse_attn(C.byref(a), C.c_void_p(_stream(q.device))))
+    return out
+
+
+def window_topk_idxs(window: int, seqlen: int, nseq: int, start_pos=None, *, out=None,
+                     device=None):
+    """Window index lists (include/sa.h). start_pos None: prefill from position 0, returns
+    int32 [nseq][seqlen][min(seqlen, window)]. start_pos (device int32 [nseq]): decode
+    (seqlen 1), returns [nseq][1][window]. With `out` (int32 [nseq][seqlen][>= cols]) the
+    lists are written into its first cols columns and out is returned."""
+    if start_pos is not None:
+        _need(start_pos, torch.int32, "start_pos")
+        device = start_pos.device
+        cols = window
+    else:
+        cols = min(seqlen, window)
+    if out is None:
+        out = torch.empty(nseq, seqlen, cols, dtype=torch.int32, device=device or "cuda")
+    _need(out, torch.int32, "out")
+    if out.dim() != 3 or out.stride(2) != 1 or out.shape[0] != nseq or out.shape[1] != seqlen:
+        raise ValueError("out must be [nseq][seqlen][>=cols] with unit column stride")
+    c = C.c_int32(0)
+    _check("sa_window_topk_idxs", lib().sa_window_topk_idxs(
+        window, seqlen, nseq, _ptr(start_pos), _ptr(out), out.stride(0), out.stride(1),
+        C.byref(c), C.c_void_p(_stream(out.device))))
+    assert c.value == cols
+    return out
+
+
+def quant_kv_fp8(kv, *, codes=None, scales=None, roundtrip=None, want=("codes", "scales")):
+    """Block-32 ue8m0 fp8 quantisation of bf16 rows kv [..., d]. Returns the tuple of the
+    requested outputs among codes (uint8 like kv), scales (uint8 [..., d/32]) and
+    roundtrip (bf16 like kv; may be kv itself for in-place)."""
+    _need(kv, torch.bfloat16, "kv")
+    if not kv.is_contiguous():
+        raise ValueError("kv must be contiguous")
+    d = kv.shape[-1]
+    rows = kv.numel() // d
+    if "codes" in want and codes is None:
+        codes = torch.empty(kv.shape, dtype=torch.uint8, device=kv.device)
+    if "scales" in want and scales is None:
+        scales = torch.empty(kv.shape[:-1] + (d // 32,), dtype=torch.uint8, device=kv.device)
+    if "roundtrip" in want and roundtrip is None:
+        roundtrip = torch.empty_like(kv)
+    _check("sa_quant_kv_fp8", lib().sa_quant_kv_fp8(
+        _ptr(kv), rows, d, _ptr(codes), _ptr(scales), _ptr(roundtrip),
+        C.c_void_p(_stream(kv.device))))
+    res = {"codes": codes, "scales": scales, "roundtrip": roundtrip}
+    return tuple(res[w] for w in want)
+
+
+def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda"):
+    """The caller's (cos, sin) table of the inverse-RoPE epilogue, f32 [max_pos][rd/2][2]:
+    precompute_freqs_cis without YaRN (Attention.__init__ for ratio-0 layers), evaluated as
+    the page does, in f32 torch arithmetic, then copied to the device."""
+    freqs = 1.0 / (base ** (torch.arange(0, rope_dim, 2, dtype=torch.float32) / rope_dim))
+    ang = torch.outer(torch.arange(max_pos, dtype=torch.float32), freqs)
+    fc = torch.polar(torch.ones_like(ang), ang)
+    return torch.view_as_real(fc).contiguous().to(device)

@@ -1,0 +1,534 @@
+// sparse_attn for gfx950: one workgroup per (query, block of heads, split of the index
+// columns). The operation follows the attention API docs ("sparse_attn", precision
+// paragraph) and the call in Attention.forward: per query and head, a softmax in f32 over
+// the gathered latent rows plus the sink (denominator only), bf16 output.
+//
+// Work inside a workgroup of NW waves (NW = 1, 2 or 4), 16 heads per wave:
+//   * key tiles of 32 index columns are gathered row by row from HBM straight into LDS
+//     (global_load_lds_dwordx4, 16 B per lane), double-buffered, so the gather of tile t+1
+//     overlaps the matrix work on tile t. All waves of the workgroup read the same tile:
+//     one gather serves 16*NW heads of the query. Rows carry a 16-byte-chunk XOR swizzle so
+//     that both LDS read patterns below avoid bank conflicts.
+//   * scores are computed transposed, S^T[key][head] = K . Q^T, on v_mfma_f32_16x16x32_bf16:
+//     K comes from LDS as the A operand, Q stays in registers as the B operand. In the
+//     accumulator layout each lane holds one head and 4 keys per 16-key block, so the
+//     online softmax needs in-lane work plus two exchanges across the 4 lane groups.
+//   * the probabilities are rounded to bf16 in registers and are already the B operand of
+//     O^T[d][head] += V^T . P^T (a 32-key step); V^T is read from the same LDS tile with the
+//     transposing ds_read_b64_tr_b16, so the tile is stored once and is both K and V.
+//   * O^T stays in accumulator registers (4 f32 per lane per 16-wide slice of d); each lane
+//     holds a single head, so the softmax rescale is a per-lane scalar multiply.
+//   * the running max starts at the sink logit and the running sum at exp(0) = 1 (counted
+//     in one lane group only and in split 0 only), which puts the sink in the denominator.
+//   * with more than one split, unnormalised partials (O, m, l) go to the workspace and a
+//     small combine kernel merges them; otherwise the epilogue (divide, bf16, optional
+//     inverse RoPE) runs here.
+// At d = 512 a wave keeps Q (64 VGPRs) and O (128 accumulators) resident for the whole key
+// loop; 16 heads per wave is what fits beside them without spilling.
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte chunk swizzle of LDS row r: for 16 consecutive rows read at one chunk (the K
+// operand) the swizzled chunks are all different, and so are they for the 4 rows x 2
+// adjacent chunks a 16-lane group touches in a transposing read. The swizzle only changes
+// the low four bits of the chunk index.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+    return ((((r & 3) << 2) | ((r >> 2) & 3))) & (CH - 1);
+}
+
+template <int D>
+struct Geo {
+    static constexpr int kRowBytes = D * 2;                 // one bf16 row in LDS
+    static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+    static constexpr int kRowsPerInst = 64 / kChunks;       // rows one wave load covers
+    static constexpr int kKSteps = D / 32;                  // QK k-steps (32 d each)
+    static constexpr int kDBlocks = D / 16;                 // 16-wide slices of d for PV
+    static constexpr int kTileBytes = kTileKeys * kRowBytes;
+};
+
+// Indices of one tile: lane j < 32 of every wave holds column col0 + j as a row of kv
+// (-1 when the column is a skip, lies beyond the split, or is out of range). Loaded one
+// tile ahead so the gather itself never waits on an index load.
+__device__ __forceinline__ int load_tile_idx(const KParams& p, const int32_t* idx_row, int col0,
+                                             int col1, int lane) {
+    const int col = col0 + lane;
+    int row = (lane < kTileKeys && col < col1) ? idx_row[col] : -1;
+    if (row >= p.kv_rows) {
+        if (p.flags & 1u) atomicOr(p.err_word, 1);
+        row = -1;
+    }
+    return row < 0 ? -1 : row;
+}
+
+// Issue the gather of one key tile into LDS (bf16 storage). Every lane either starts a
+// 16-byte direct-to-LDS load of its chunk or, for a skipped column, writes zeros into that
+// chunk (so the tile never holds stale or non-finite data where the probability is zero).
+// The loads are dealt round-robin to the waves.
+template <int D, int NW>
+__device__ __forceinline__ void gather_tile_bf16(const uint8_t* kv_seq, int tidx,
+                                                 SA_LDS uint8_t* buf, int wid, int lane) {
+    using G = Geo<D>;
+    constexpr int kInsts = kTileKeys / G::kRowsPerInst;
+    static_assert(kTileKeys % G::kRowsPerInst == 0, "tile split");
+    const int sub = lane / G::kChunks;          // row within one load
+    const int pc = lane % G::kChunks;           // physical chunk this lane fills
+#pragma unroll
+    for (int j = 0; j < (kInsts + NW - 1) / NW; ++j) {
+        const int i = wid + j * NW;
+        if (i >= kInsts) break;
+        const int r0 = i * G::kRowsPerInst;
+        const int r = r0 + sub;
+        const int row = __shfl(tidx, r, kWave);
+        if (row >= 0) {
+            const int lc = pc ^ swz<G::kChunks>(r);
+            const uint8_t* src = kv_seq + (int64_t)row * G::kRowBytes + lc * 16;
+            __builtin_amdgcn_global_load_lds((const void*)src, (SA_LDS void*)(buf + r0 * G::kRowBytes),
+                                             16, 0, 0);
+        } else {
+            *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+// fp8 storage: the same gather, of e4m3 codes (D bytes per row) and the row's D/32 scale
+// bytes, into a raw staging tile; converted to the bf16 tile by convert_tile_fp8.
+template <int D, int NW>
+__device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uint8_t* sc_seq, int tidx,
+                                                SA_LDS uint8_t* raw, SA_LDS uint8_t* raw_sc, int wid,
+                                                int lane) {
+    constexpr int kCodeChunks = D / 16;                    // 16-byte chunks of codes per row
+    constexpr int kRowsPerInst = 64 / kCodeChunks;
+    constexpr int kInsts = kTileKeys / kRowsPerInst;
+    static_assert(kTileKeys % kRowsPerInst == 0, "tile split");
+    const int sub = lane / kCodeChunks;
+    const int pc = lane % kCodeChunks;
+#pragma unroll
+    for (int j = 0; j < (kInsts + NW - 1) / NW; ++j) {
+        const int i = wid + j * NW;
+        if (i >= kInsts) break;
+        const int r0 = i * kRowsPerInst;
+        const int r = r0 + sub;
+        const int row = __shfl(tidx, r, kWave);
+        if (row >= 0) {
+            const uint8_t* src = kv_seq + (int64_t)row * D + pc * 16;
+            __builtin_amdgcn_global_load_lds((const void*)src, (SA_LDS void*)(raw + r0 * D), 16, 0, 0);
+        } else {
+            *(SA_LDS u32x4*)(raw + r * D + pc * 16) = u32x4{0, 0, 0, 0};
+        }
+    }
+    // scale bytes: D/32 per row, wave 0 one lane per row (zeros for a skipped row make
+    // every value of the row decode to zero)
+    constexpr int kSc = D / 32;
+    const int row = __shfl(tidx, lane & 63, kWave);
+    if (wid == 0 && lane < kTileKeys) {
+        for (int j = 0; j < kSc; ++j)
+            raw_sc[lane * kSc + j] = row >= 0 ? sc_seq[(int64_t)row * kSc + j] : (uint8_t)0;
+    }
+}
+
+// e4m3fn code -> f32 (exact): placing the 7 magnitude bits at f32 bits 20..26 gives the
+// code's value times 2^-120 for normal and subnormal codes alike.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    return bits_f32(((c & 0x80u) << 24) | ((c & 0x7fu) << 20)) * 0x1p120f;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void convert_tile_fp8(SA_LDS const uint8_t* raw, SA_LDS const uint8_t* raw_sc,
+                                                 SA_LDS uint8_t* buf, int tid) {
+    using G = Geo<D>;
+    constexpr int kUnits = kTileKeys * D / 8;              // 8 codes -> one 16-byte bf16 chunk
+    for (int u = tid; u < kUnits; u += NW * kWave) {
+        const int r = u / (D / 8);
+        const int c8 = u % (D / 8);                         // logical 16-byte chunk of the row
+        const u32x2 codes = *(SA_LDS const u32x2*)(raw + r * D + c8 * 8);
+        const float s = bits_f32((uint32_t)raw_sc[r * (D / 32) + (c8 * 8) / 32] << 23);
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w = codes[k >> 1] >> ((k & 1) * 16);
+            // the product of an e4m3 value and a power of two has at most 4 significant
+            // bits, so dropping the low half of the f32 is the exact bf16 value
+            const uint32_t lo = f32_bits(e4m3_to_f32(w & 0xffu) * s) >> 16;
+            const uint32_t hi = f32_bits(e4m3_to_f32((w >> 8) & 0xffu) * s) >> 16;
+            o[k] = lo | (hi << 16);
+        }
+        const int pcn = c8 ^ swz<G::kChunks>(r);
+        *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pcn * 16) = o;
+    }
+}
+
+// Epilogue for 4 consecutive output elements d0..d0+3 of one head: o = acc * inv_l rounded
+// to bf16; with `rot`, the inverse rotation of the pairs that fall in the last rope_dim
+// elements (apply_rotary_emb with inverse=True: multiply by the conjugate in f32, back to
+// bf16). A pair outside the rope tail is rotated by (1, 0), which returns it unchanged.
+// `cs` points at the position's row of the (cos, sin) table. Returns two packed bf16 pairs.
+__device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a3, float inv_l,
+                                           bool rot, int d0, int r0, const float* cs) {
+    uint32_t w[2] = {pack_bf16x2(a0 * inv_l, a1 * inv_l), pack_bf16x2(a2 * inv_l, a3 * inv_l)};
+    if (rot) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int dk = d0 + 2 * k;
+            const bool in = dk >= r0;
+            const float2 t = *(const float2*)(cs + (in ? (dk - r0) : 0));
+            const float c = in ? t.x : 1.0f, sn = in ? t.y : 0.0f;
+            const float x = bf16_lo(w[k]), y = bf16_hi(w[k]);
+            w[k] = pack_bf16x2(x * c + y * sn, y * c - x * sn);
+        }
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// Position of query t of sequence seq and its (cos, sin) row, or nullptr when the epilogue
+// is off or the position has no row in the table (then no rotation is applied; bit 2 of
+// the error word records it when checking is on).
+__device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int t, bool report) {
+    if (p.rope_dim == 0) return nullptr;
+    const int pos = p.pos[(int64_t)seq * p.pos_seq_stride + t];
+    if (pos < 0 || pos >= p.max_pos) {
+        if (report && (p.flags & 1u)) atomicOr(p.err_word, 2);
+        return nullptr;
+    }
+    return p.rope_cs + (int64_t)pos * p.rope_dim;
+}
+
+__device__ __forceinline__ float sum4groups(float v) {
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+__device__ __forceinline__ float max4groups(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    return v;
+}
+
+template <int D, bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
+    using G = Geo<D>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
+    // bf16: two tiles. fp8: one bf16 tile, then two raw staging tiles of codes, then two
+    // of scale bytes.
+    auto tile = [&](int i) { return smem + i * G::kTileBytes; };
+    auto raw = [&](int i) { return smem + G::kTileBytes + i * (kTileKeys * D); };
+    auto raw_sc = [&](int i) { return smem + G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
+
+    const int tid = threadIdx.x;
+    const int wid = tid / kWave;
+    const int lane = tid % kWave;
+    const int l16 = lane & 15;                  // this lane's head within the wave
+    const int q4 = lane >> 4;                   // lane group 0..3
+
+    // work item: ((query * head_blocks) + head block) * splits + split
+    int item = blockIdx.x;
+    const int split = item % p.splits;
+    item /= p.splits;
+    const int hblk = item % p.head_blocks;
+    const int qi = item / p.head_blocks;
+    const int seq = qi / p.s;
+    const int t = qi % p.s;
+
+    const int head = hblk * NW * kHeadsPerWave + wid * kHeadsPerWave + l16;
+    const bool head_ok = head < p.h;
+
+    const int32_t* idx_row = p.idx + (int64_t)seq * p.idx_seq_stride + (int64_t)t * p.topk;
+    const int col_begin = split * p.cols_per_split;
+    const int col_end = min(p.topk, col_begin + p.cols_per_split);
+    const int ntiles = col_end > col_begin ? (col_end - col_begin + kTileKeys - 1) / kTileKeys : 0;
+
+    const uint8_t* kv_seq = p.kv + (int64_t)seq * p.kv_seq_stride_bytes;
+    const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
+
+    // Q as the B operand of the 16x16x32 product: lane holds head l16, d = 32*kk + 8*q4 + 0..7
+    u32x4 qreg[G::kKSteps];
+    {
+        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + head) * D;
+#pragma unroll
+        for (int kk = 0; kk < G::kKSteps; ++kk)
+            qreg[kk] = head_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
+    }
+
+    const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+    float m_run = sink2;                                       // log2 domain
+    float l_run = (q4 == 0 && split == 0) ? 1.0f : 0.0f;       // the sink's exp(0)
+    f32x4 o_acc[G::kDBlocks];
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Per-lane LDS byte offsets of the two operand reads (the swizzle only touches the low
+    // four bits of a chunk index, so each read is one of these plus a multiple of 256 B):
+    //   K operand, block mb, step kk: qk_off[mb][kk % 4] + 256 * (kk / 4)
+    //   V operand, read ab, d slice db: pv_off[ab][db % 8] + 256 * (db / 8)
+    int qk_off[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int r = mb * 16 + l16;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            qk_off[mb][k] = r * G::kRowBytes + 16 * ((4 * k + q4) ^ swz<G::kChunks>(r));
+    }
+    int pv_off[2][8];
+    {
+        // 16-lane group q4 reads keys 4*q4 + (0..3) (then 16 + ...) of d columns
+        // 16*db + (0..15); lane i of the group names row i/4 and columns 4*(i%4)..+3 of that
+        // 4 x 16 block and receives column i.
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab) {
+            const int rr = 16 * ab + 4 * q4 + (l16 >> 2);
+#pragma unroll
+            for (int b8 = 0; b8 < 8; ++b8) {
+                const int col = 16 * b8 + 4 * (l16 & 3);       // bf16 column within 128
+                pv_off[ab][b8] = rr * G::kRowBytes + (col & 7) * 2 +
+                                 16 * ((col >> 3) ^ swz<G::kChunks>(rr));
+            }
+        }
+    }
+
+    // first gather; the index vector of the following tile is fetched one tile ahead
+    int tidx = ntiles > 0 ? load_tile_idx(p, idx_row, col_begin, col_end, lane) : -1;
+    if (ntiles > 0) {
+        if constexpr (FP8)
+            gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx, raw(0), raw_sc(0), wid, lane);
+        else
+            gather_tile_bf16<D, NW>(kv_seq, tidx, tile(0), wid, lane);
+    }
+    int nidx = ntiles > 1 ? load_tile_idx(p, idx_row, col_begin + kTileKeys, col_end, lane) : -1;
+
+    for (int it = 0; it < ntiles; ++it) {
+        // which columns of this tile are real rows (one bit per key)
+        const uint32_t valid = (uint32_t)__ballot(tidx >= 0);
+        tidx = nidx;
+
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        SA_LDS uint8_t* cur;
+        if constexpr (FP8) {
+            if (it + 1 < ntiles)
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
+            convert_tile_fp8<D, NW>(raw(it & 1), raw_sc(it & 1), tile(0), tid);
+            __syncthreads();
+            cur = tile(0);
+        } else {
+            if (it + 1 < ntiles)
+                gather_tile_bf16<D, NW>(kv_seq, tidx, tile((it + 1) & 1), wid, lane);
+            cur = tile(it & 1);
+        }
+        if (it + 2 < ntiles)
+            nidx = load_tile_idx(p, idx_row, col_begin + (it + 2) * kTileKeys, col_end, lane);
+
+        // Opaque to the optimiser: addresses derived from the offsets are then formed next
+        // to their reads inside the loop instead of being hoisted (and spilled) in bulk.
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(qk_off[mb][k]));
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[ab][k]));
+
+        // ---- S^T = K . Q^T over the tile's two 16-key blocks; the K operand of step kk+1
+        //      is read while step kk multiplies, and scheduling fences keep the compiler
+        //      from hoisting every read of the unrolled loop.
+        f32x4 s_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        {
+            u32x4 an0 = *(SA_LDS const u32x4*)(cur + qk_off[0][0]);
+            u32x4 an1 = *(SA_LDS const u32x4*)(cur + qk_off[1][0]);
+#pragma unroll
+            for (int kk = 0; kk < G::kKSteps; ++kk) {
+                const u32x4 a0 = an0, a1 = an1;
+                if (kk + 1 < G::kKSteps) {
+                    const int nk = kk + 1;
+                    an0 = *(SA_LDS const u32x4*)(cur + qk_off[0][nk & 3] + 256 * (nk >> 2));
+                    an1 = *(SA_LDS const u32x4*)(cur + qk_off[1][nk & 3] + 256 * (nk >> 2));
+                }
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[kk]);
+                s_acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb, s_acc[0], 0, 0, 0);
+                s_acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb, s_acc[1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        // ---- online softmax (log2 domain); this lane: head l16, keys 16*mb + 4*q4 + r.
+        //      The running max is only moved when the tile max exceeds it by more than 8
+        //      (a factor 256): until then the stale max keeps every exp2 below 256 and the
+        //      result is the same softmax (the common factor cancels in O / l), so the O
+        //      rescale is rare.
+        const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sv = ((lm >> (16 * mb + r)) & 1u) ? s_acc[mb][r] * p.scale_log2 : -INFINITY;
+                s_acc[mb][r] = sv;
+                tmax = fmaxf(tmax, sv);
+            }
+        tmax = max4groups(tmax);
+        const bool grow = tmax > m_run + 8.0f;
+        if (__ballot(grow) != 0) {
+            const float m_new = grow ? tmax : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] *= alpha;
+        }
+        // a running max still at -inf (sink -inf, nothing seen yet) means every score of
+        // the tile is -inf as well: exponentiate against 0 so that they give exact zeros
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        u32x4 pb;                                              // P as the PV B operand
+        float psum = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const float p0 = fast_exp2(s_acc[mb][0] - m_use), p1 = fast_exp2(s_acc[mb][1] - m_use);
+            const float p2 = fast_exp2(s_acc[mb][2] - m_use), p3 = fast_exp2(s_acc[mb][3] - m_use);
+            psum += (p0 + p1) + (p2 + p3);
+            pb[2 * mb] = pack_bf16x2(p0, p1);
+            pb[2 * mb + 1] = pack_bf16x2(p2, p3);
+        }
+        l_run += psum;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time
+        {
+            const bf16x8 pk = __builtin_bit_cast(bf16x8, pb);
+            bf16x4v va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][0]));
+            bf16x4v vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][0]));
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                const bf16x8 a = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+                if (db + 1 < G::kDBlocks) {
+                    const int nb = db + 1;
+                    va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][nb & 7] + 256 * (nb >> 3)));
+                    vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][nb & 7] + 256 * (nb >> 3)));
+                }
+                o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk, o_acc[db], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    // ---- finish: the four lane groups share m_run; their partial sums add up
+    const float l_tot = sum4groups(l_run);
+    if (!head_ok) return;
+    // O^T accumulator layout: lane holds head l16, d = 16*db + 4*q4 + (0..3)
+    if (p.splits == 1) {
+        const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        const float* cs = rope_row(p, seq, t, lane == 0);
+        const int r0 = D - p.rope_dim;
+        uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head) * D;
+#pragma unroll
+        for (int db = 0; db < G::kDBlocks; ++db) {
+            const int d0 = 16 * db + 4 * q4;
+            const bool rot = cs != nullptr && 16 * db + 16 > r0;    // slice meets the rope tail
+            *(u32x2*)(orow + d0) = epilogue4(o_acc[db][0], o_acc[db][1], o_acc[db][2], o_acc[db][3],
+                                             inv_l, rot, d0, r0, cs);
+        }
+    } else {
+        const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head;
+        float* wo = p.ws_o + slot * D;
+#pragma unroll
+        for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db];
+        if (q4 == 0) {
+            p.ws_ml[slot * 2 + 0] = m_run;
+            p.ws_ml[slot * 2 + 1] = l_tot;
+        }
+    }
+}
+
+// Merge the split partials of one (query, head): m = max m_i, l = sum l_i 2^(m_i - m),
+// o = sum O_i 2^(m_i - m) / l (the sink is in l_0 only). One wave per (query, head); each
+// lane owns max(D/64, 4) consecutive elements of d.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
+    const int wave = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (wave >= p.b * p.s * p.h) return;
+    const int head = wave % p.h;
+    const int qi = wave / p.h;
+    const int seq = qi / p.s, t = qi % p.s;
+    constexpr int kPer = D / 64 >= 4 ? D / 64 : 4;             // elements per lane
+    constexpr int kLanes = D / kPer;
+    float m = -INFINITY;
+    for (int i = 0; i < p.splits; ++i)
+        m = fmaxf(m, p.ws_ml[(((int64_t)qi * p.splits + i) * p.h_pad + head) * 2]);
+    if (m == -INFINITY) m = 0.0f;        // no split saw a row and the sink is -inf: all weights 0
+    float l = 0.0f;
+    float acc[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
+    for (int i = 0; i < p.splits; ++i) {
+        const int64_t slot = ((int64_t)qi * p.splits + i) * p.h_pad + head;
+        const float wgt = fast_exp2(p.ws_ml[slot * 2] - m);
+        l += p.ws_ml[slot * 2 + 1] * wgt;
+        if (lane < kLanes) {
+            const float* src = p.ws_o + slot * D + lane * kPer;
+#pragma unroll
+            for (int k = 0; k < kPer; k += 4) {
+                const f32x4 v = *(const f32x4*)(src + k);
+                acc[k] += v[0] * wgt; acc[k + 1] += v[1] * wgt;
+                acc[k + 2] += v[2] * wgt; acc[k + 3] += v[3] * wgt;
+            }
+        }
+    }
+    if (lane >= kLanes) return;
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+    const float* cs = rope_row(p, seq, t, lane == 0);
+    const int r0 = D - p.rope_dim;
+    uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head) * D;
+#pragma unroll
+    for (int k = 0; k < kPer; k += 4) {
+        const int d0 = lane * kPer + k;
+        *(u32x2*)(orow + d0) = epilogue4(acc[k], acc[k + 1], acc[k + 2], acc[k + 3], inv_l,
+                                         cs != nullptr && d0 + 4 > r0, d0, r0, cs);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <int D, bool FP8, int NW>
+static hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
+    using G = Geo<D>;
+    const size_t lds = FP8 ? G::kTileBytes + 2 * kTileKeys * D + 2 * kTileKeys * (D / 32)
+                           : 2 * (size_t)G::kTileBytes;
+    auto k = attn_fwd_kernel<D, FP8, NW>;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(NW * kWave), lds, st, p);
+    return hipGetLastError();
+}
+
+template <int D, bool FP8>
+static hipError_t launch_fwd_nw(const KParams& p, int nw, int blocks, hipStream_t st) {
+    if (nw == 1) return launch_fwd<D, FP8, 1>(p, blocks, st);
+    if (nw == 2) return launch_fwd<D, FP8, 2>(p, blocks, st);
+    return launch_fwd<D, FP8, 4>(p, blocks, st);
+}
+
+template <int D>
+static hipError_t launch_all(const KParams& p, bool fp8, int nw, int blocks, hipStream_t st) {
+    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, blocks, st) : launch_fwd_nw<D, false>(p, nw, blocks, st);
+    if (e != hipSuccess || p.splits == 1) return e;
+    const int waves = p.b * p.s * p.h;
+    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((waves + 3) / 4), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, hipStream_t st) {
+    const int blocks = p.b * p.s * p.head_blocks * p.splits;
+    switch (p.d) {
+        case 64: return launch_all<64>(p, fp8, nw, blocks, st);
+        case 128: return launch_all<128>(p, fp8, nw, blocks, st);
+        case 256: return launch_all<256>(p, fp8, nw, blocks, st);
+        case 512: return launch_all<512>(p, fp8, nw, blocks, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sa

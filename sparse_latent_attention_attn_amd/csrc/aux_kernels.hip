@@ -1,0 +1,141 @@
+// The two helpers around sparse_attn: the ring-cache window index lists and the block-32
+// ue8m0 fp8 quantisation of KV rows.
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+// ------------------------------------------------------------------ window index lists
+// Attention API docs, "window_topk_idxs" and the ring-cache paragraph: the slot of token p
+// is p mod window; prefill lists a causal window into the chunk itself, decode lists the
+// whole ring oldest first, -1 marking a slot that holds nothing. One thread per entry.
+__global__ void window_idxs_kernel(int32_t window, int32_t seqlen, int32_t nseq,
+                                   const int32_t* __restrict__ start_pos, int32_t* __restrict__ idx,
+                                   int64_t seq_stride, int64_t row_stride, int32_t cols) {
+    const int64_t total = (int64_t)nseq * seqlen * cols;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t j = (int32_t)(e % cols);
+        const int64_t rt = e / cols;
+        const int32_t t = (int32_t)(rt % seqlen);
+        const int32_t n = (int32_t)(rt / seqlen);
+        int32_t v;
+        if (start_pos == nullptr) {
+            // prefill from position 0: chunk rows lo..t, lo = max(0, t - window + 1)
+            const int32_t lo = max(0, t - window + 1);
+            v = lo + j <= t ? lo + j : -1;
+        } else {
+            const int32_t P = start_pos[n];
+            if (P < 0) v = -1;
+            else if (P >= window - 1) v = (int32_t)(((int64_t)P + 1 + j) % window);  // full ring
+            else v = j <= P ? j : -1;                                              // slots 0..P
+        }
+        idx[(int64_t)n * seq_stride + (int64_t)t * row_stride + j] = v;
+    }
+}
+
+hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
+                              int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
+                              hipStream_t st) {
+    const int64_t total = (int64_t)nseq * seqlen * cols;
+    const int threads = 256;
+    const int64_t want = (total + threads - 1) / threads;
+    const int blocks = (int)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(window_idxs_kernel, dim3(blocks), dim3(threads), 0, st, window, seqlen, nseq,
+                       start_pos, idx, seq_stride, row_stride, cols);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ block-32 fp8 quant
+// Attention API docs, "act_quant_inplace", "FP8_BLOCK", "pow2_ceil": per 32 consecutive
+// elements, s = pow2_ceil(max(amax, 1e-4) / 448); codes = e4m3fn(x / s), round to nearest
+// even after clamping to +-448; the round trip codes * s is exact in bf16.
+
+// 2^ceil(log2 v) for a positive normal f32, from its fields: exponent + (mantissa != 0).
+__device__ __forceinline__ float pow2_ceil_f32(float v) {
+    const uint32_t u = f32_bits(v);
+    const uint32_t e = ((u >> 23) & 0xffu) + ((u & 0x7fffffu) != 0u ? 1u : 0u);
+    return bits_f32(e << 23);
+}
+
+// |a| <= 448 (already clamped), finite. e4m3fn: bias 7, 3 mantissa bits, subnormal step
+// 2^-9. Round to nearest, ties to even.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t sign = (f32_bits(x) >> 24) & 0x80u;
+    const float a = fminf(fabsf(x), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        // subnormal grid of 2^-9: a * 512 is exact, rint rounds half to even
+        code = (uint32_t)__builtin_rintf(a * 512.0f);          // 0..8; 8 is the code of 2^-6
+    } else {
+        // keep 3 mantissa bits: add half an ulp of the target (minus one if the kept lsb is
+        // 0) and truncate; a carry into the exponent is the correct rounding up
+        uint32_t u = f32_bits(a);
+        u += 0x7ffffu + ((u >> 20) & 1u);
+        u &= 0xfff00000u;
+        const uint32_t e = (u >> 23) - 127u + 7u;             // 1..15
+        code = (e << 3) | ((u >> 20) & 7u);
+    }
+    return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float v = e == 0 ? (float)m * 0x1p-9f : bits_f32(((e + 120u) << 23) | (m << 20));
+    return (c & 0x80u) ? -v : v;
+}
+
+// One block of 32 elements per 4 lanes (8 elements = 16 bytes each); 16 blocks per wave.
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ kv, int64_t nblocks,
+                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                        uint16_t* rt) {
+    const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t blk = gtid >> 2;
+    const int part = (int)(gtid & 3);
+    const bool live = blk < nblocks;
+    u32x4 v = live ? *(const u32x4*)(kv + blk * 32 + part * 8) : u32x4{0, 0, 0, 0};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { x[2 * k] = bf16_lo(v[k]); x[2 * k + 1] = bf16_hi(v[k]); }
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, 1e-4f);
+    const float s = pow2_ceil_f32(amax / 448.0f);
+    if (!live) return;
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] / s);   // exact division by 2^k
+    if (codes) {
+        u32x2 w;
+        w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        *(u32x2*)(codes + blk * 32 + part * 8) = w;
+    }
+    if (scales && part == 0) scales[blk] = (uint8_t)((f32_bits(s) >> 23) & 0xffu);
+    if (rt) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // value * 2^k has at most 4 significant bits: the upper f32 half is exact bf16
+            const uint32_t lo = f32_bits(e4m3_decode(c[2 * k]) * s) >> 16;
+            const uint32_t hi = f32_bits(e4m3_decode(c[2 * k + 1]) * s) >> 16;
+            o[k] = lo | (hi << 16);
+        }
+        *(u32x4*)(rt + blk * 32 + part * 8) = o;
+    }
+}
+
+hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
+                            uint8_t* scales, uint16_t* rt, hipStream_t st) {
+    const int64_t nblocks = rows * (d / 32);
+    const int64_t threads = nblocks * 4;
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)grid), dim3(256), 0, st, kv, nblocks, codes, scales, rt);
+    return hipGetLastError();
+}
+
+}  // namespace sa

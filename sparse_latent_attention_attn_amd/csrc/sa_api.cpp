@@ -1,0 +1,181 @@
+// C-ABI entry points of libsa.so (declared in include/sa.h). Each call validates its
+// arguments on the host before making any HIP call, then plans and launches the kernels on
+// the caller's stream. Nothing is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/sa.h"
+#include "sa_internal.hpp"
+
+#define SA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// compute units of the current device (cached per device)
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape and stride checks of sa_attn_args that need no pointer (shared with the workspace
+// query). Returns SA_OK or an error status.
+int check_shape(const sa_attn_args* a) {
+    if (!a) return SA_ERR_INVALID;
+    if (a->b < 1 || a->s < 1 || a->h < 1 || a->topk < 1 || a->kv_rows < 1) return SA_ERR_INVALID;
+    if (a->d != 64 && a->d != 128 && a->d != 256 && a->d != 512) return SA_ERR_UNSUPPORTED;
+    if (a->kv_format != SA_KV_BF16 && a->kv_format != SA_KV_FP8_E4M3_B32) return SA_ERR_INVALID;
+    if ((a->flags & ~(uint32_t)SA_FLAG_CHECK_IDX) != 0) return SA_ERR_INVALID;
+    if (a->rope_dim < 0 || a->rope_dim > a->d || (a->rope_dim & 1)) return SA_ERR_INVALID;
+    const int64_t shd = (int64_t)a->s * a->h * a->d;
+    if (a->b > 1) {
+        const int64_t kv_row_elems = a->d;   // elements of the storage type per row
+        if (a->q_seq_stride < shd || a->out_seq_stride < shd) return SA_ERR_INVALID;
+        if (a->kv_seq_stride < (int64_t)a->kv_rows * kv_row_elems) return SA_ERR_INVALID;
+        if (a->idx_seq_stride < (int64_t)a->s * a->topk) return SA_ERR_INVALID;
+        if (a->kv_format == SA_KV_FP8_E4M3_B32 &&
+            a->kv_scale_seq_stride < (int64_t)a->kv_rows * (a->d / 32))
+            return SA_ERR_INVALID;
+        if (a->rope_dim > 0 && a->pos_seq_stride < a->s) return SA_ERR_INVALID;
+    }
+    // 16-byte vector access of q, out and kv rows needs strides in whole 16-byte units
+    if (a->q_seq_stride % 8 || a->out_seq_stride % 8) return SA_ERR_INVALID;
+    if (a->kv_format == SA_KV_BF16 ? (a->kv_seq_stride % 8) : (a->kv_seq_stride % 16)) return SA_ERR_INVALID;
+    if (!std::isfinite(a->scale)) return SA_ERR_INVALID;
+    return SA_OK;
+}
+
+int check_pointers(const sa_attn_args* a) {
+    if (!a->q || !a->kv || !a->sink || !a->idx || !a->out) return SA_ERR_INVALID;
+    if (!aligned(a->q, 16) || !aligned(a->kv, 16) || !aligned(a->out, 16) || !aligned(a->idx, 4) ||
+        !aligned(a->sink, 4))
+        return SA_ERR_INVALID;
+    if (a->kv_format == SA_KV_FP8_E4M3_B32 && !a->kv_scale) return SA_ERR_INVALID;
+    if (a->rope_dim > 0) {
+        if (!a->rope_cos_sin || !a->pos || a->max_pos < 1 || !aligned(a->rope_cos_sin, 8)) return SA_ERR_INVALID;
+    }
+    if ((a->flags & SA_FLAG_CHECK_IDX) && !a->err_word) return SA_ERR_INVALID;
+    return SA_OK;
+}
+
+sa::Plan make_plan(const sa_attn_args* a, int cus) {
+    sa::Plan pl{};
+    using sa::kHeadsPerWave;
+    using sa::kTileKeys;
+    const int waves_needed = (a->h + kHeadsPerWave - 1) / kHeadsPerWave;
+    pl.nw = waves_needed >= sa::kMaxWaves ? sa::kMaxWaves : waves_needed <= 1 ? 1 : 2;
+    pl.head_blocks = (a->h + pl.nw * kHeadsPerWave - 1) / (pl.nw * kHeadsPerWave);
+    pl.h_pad = pl.head_blocks * pl.nw * kHeadsPerWave;
+    const int ntiles = (a->topk + kTileKeys - 1) / kTileKeys;
+    const int64_t wgs = (int64_t)a->b * a->s * pl.head_blocks;
+    int splits = 1;
+    if (wgs < cus) splits = (int)std::min<int64_t>(ntiles, (cus + wgs - 1) / wgs);
+    const int tiles_per_split = (ntiles + splits - 1) / splits;
+    pl.cols_per_split = tiles_per_split * kTileKeys;
+    pl.splits = (a->topk + pl.cols_per_split - 1) / pl.cols_per_split;
+    pl.ws_bytes = 0;
+    if (pl.splits > 1) {
+        const size_t slots = (size_t)a->b * a->s * pl.splits * pl.h_pad;
+        pl.ws_bytes = slots * a->d * sizeof(float) + slots * 2 * sizeof(float);
+    }
+    return pl;
+}
+
+}  // namespace
+
+SA_EXPORT int sa_abi_version(void) { return SA_ABI_VERSION; }
+
+SA_EXPORT const char* sa_status_string(int status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported argument combination";
+        case SA_ERR_HIP: return "HIP runtime error";
+        case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+SA_EXPORT int sa_sparse_attn_workspace(const sa_attn_args* a, size_t* bytes) {
+    if (!bytes) return SA_ERR_INVALID;
+    const int rc = check_shape(a);
+    if (rc != SA_OK) return rc;
+    *bytes = make_plan(a, cu_count()).ws_bytes;
+    return SA_OK;
+}
+
+SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
+    int rc = check_shape(a);
+    if (rc != SA_OK) return rc;
+    rc = check_pointers(a);
+    if (rc != SA_OK) return rc;
+    const sa::Plan pl = make_plan(a, cu_count());
+    if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 16)))
+        return SA_ERR_WORKSPACE;
+    const int64_t blocks = (int64_t)a->b * a->s * pl.head_blocks * pl.splits;
+    if (blocks > INT32_MAX) return SA_ERR_UNSUPPORTED;
+
+    sa::KParams p{};
+    p.b = a->b; p.s = a->s; p.h = a->h; p.d = a->d; p.topk = a->topk; p.kv_rows = a->kv_rows;
+    p.q = (const uint16_t*)a->q; p.q_seq_stride = a->q_seq_stride;
+    p.kv = (const uint8_t*)a->kv;
+    p.kv_seq_stride_bytes = a->kv_format == SA_KV_BF16 ? a->kv_seq_stride * 2 : a->kv_seq_stride;
+    p.kv_scale = a->kv_scale; p.kv_scale_seq_stride = a->kv_scale_seq_stride;
+    p.sink = a->sink;
+    p.idx = a->idx; p.idx_seq_stride = a->idx_seq_stride;
+    p.scale_log2 = a->scale * 1.4426950408889634f;
+    p.out = (uint16_t*)a->out; p.out_seq_stride = a->out_seq_stride;
+    p.rope_dim = a->rope_dim; p.rope_cs = a->rope_cos_sin; p.max_pos = a->max_pos;
+    p.pos = a->pos; p.pos_seq_stride = a->pos_seq_stride;
+    p.splits = pl.splits; p.cols_per_split = pl.cols_per_split;
+    p.head_blocks = pl.head_blocks; p.h_pad = pl.h_pad;
+    if (pl.splits > 1) {
+        const size_t slots = (size_t)a->b * a->s * pl.splits * pl.h_pad;
+        p.ws_o = (float*)a->workspace;
+        p.ws_ml = p.ws_o + slots * a->d;
+    }
+    p.flags = a->flags; p.err_word = a->err_word;
+    const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+SA_EXPORT int sa_window_topk_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
+                                  int32_t* idx, int64_t idx_seq_stride, int64_t idx_row_stride,
+                                  int32_t* cols, void* stream) {
+    if (window < 1 || seqlen < 1 || nseq < 1 || !idx || !cols) return SA_ERR_INVALID;
+    if (start_pos && seqlen > 1) return SA_ERR_UNSUPPORTED;
+    const int32_t c = start_pos ? window : (seqlen < window ? seqlen : window);
+    if (idx_row_stride < c) return SA_ERR_INVALID;
+    if (nseq > 1 && idx_seq_stride < (int64_t)(seqlen - 1) * idx_row_stride + c) return SA_ERR_INVALID;
+    if (!aligned(idx, 4) || (start_pos && !aligned(start_pos, 4))) return SA_ERR_INVALID;
+    *cols = c;
+    const hipError_t e = sa::launch_window_idxs(window, seqlen, nseq, start_pos, idx, idx_seq_stride,
+                                                idx_row_stride, c, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+SA_EXPORT int sa_quant_kv_fp8(const void* kv, int64_t rows, int32_t d, uint8_t* e4m3_out,
+                              uint8_t* e8m0_out, void* bf16_out, void* stream) {
+    if (!kv || rows < 0 || d < 32 || d % 32 != 0) return SA_ERR_INVALID;
+    if (!e4m3_out && !e8m0_out && !bf16_out) return SA_ERR_INVALID;
+    if (!aligned(kv, 16) || (e4m3_out && !aligned(e4m3_out, 8)) || (bf16_out && !aligned(bf16_out, 16)))
+        return SA_ERR_INVALID;
+    if (rows == 0) return SA_OK;
+    const hipError_t e = sa::launch_quant_fp8((const uint16_t*)kv, rows, d, e4m3_out, e8m0_out,
+                                              (uint16_t*)bf16_out, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI entry points (sa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Tiling shared by the planner (sa_api.cpp) and the kernels (attn_fwd.hip).
+constexpr int kTileKeys = 32;       // index columns per key tile
+constexpr int kHeadsPerWave = 16;   // heads one wave owns
+constexpr int kMaxWaves = 4;        // waves per workgroup
+
+// Everything one sparse_attn launch needs, passed by value as the kernel argument.
+struct KParams {
+    int32_t b, s, h, d, topk, kv_rows;
+    const uint16_t* q;       int64_t q_seq_stride;          // elements
+    const uint8_t* kv;       int64_t kv_seq_stride_bytes;   // bytes
+    const uint8_t* kv_scale; int64_t kv_scale_seq_stride;   // bytes
+    const float* sink;
+    const int32_t* idx;      int64_t idx_seq_stride;        // elements
+    float scale_log2;                                      // softmax_scale * log2(e)
+    uint16_t* out;           int64_t out_seq_stride;        // elements
+    int32_t rope_dim;
+    const float* rope_cs;    int32_t max_pos;
+    const int32_t* pos;      int64_t pos_seq_stride;
+    float* ws_o;                                           // [b*s][splits][h_pad][d]
+    float* ws_ml;                                          // [b*s][splits][h_pad][2]
+    int32_t splits, cols_per_split, head_blocks, h_pad;
+    uint32_t flags;
+    int32_t* err_word;
+};
+
+// Split plan shared by sa_sparse_attn and sa_sparse_attn_workspace.
+struct Plan {
+    int nw;             // waves per workgroup (32 heads each)
+    int head_blocks;
+    int h_pad;
+    int splits;
+    int cols_per_split; // a multiple of the 64-column key tile
+    size_t ws_bytes;
+};
+
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, hipStream_t st);
+hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
+                              int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
+                              hipStream_t st);
+hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
+                            uint8_t* scales, uint16_t* rt, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,106 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/sa.h declares,
+and rejects bad arguments on the host before making any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import sparse_latent_attention_attn_amd as sa
+    if not os.path.exists(sa.LIB_PATH):
+        from sparse_latent_attention_attn_amd import build_lib
+        build_lib.build()
+    sa.lib()
+    return sa
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("sa_sparse_attn", "sa_sparse_attn_workspace", "sa_window_topk_idxs",
+              "sa_quant_kv_fp8", "sa_status_string", "sa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(sa):
+    L = sa.lib()
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+    assert L.sa_abi_version() == 1
+    assert L.sa_status_string(0) == b"ok"
+    assert b"invalid" in L.sa_status_string(-1)
+
+
+def test_no_symbol_leaks_beyond_the_header(sa):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {n for n in exported if n.startswith("sa_")} == set(_declared_functions())
+
+
+def _args(sa, **kw):
+    a = sa.AttnArgs()
+    a.b, a.s, a.h, a.d, a.topk, a.kv_rows = 1, 1, 16, 64, 8, 8
+    a.q_seq_stride, a.kv_seq_stride, a.idx_seq_stride, a.out_seq_stride = 1024, 512, 8, 1024
+    a.scale = 0.125
+    # non-null, 16-byte aligned fake device pointers: validation never dereferences them
+    for f in ("q", "kv", "sink", "idx", "out"):
+        setattr(a, f, 0x10000)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("b", 0, -1), ("h", 0, -1), ("topk", 0, -1), ("kv_rows", 0, -1),
+    ("d", 96, -2), ("d", 1024, -2), ("kv_format", 7, -1), ("flags", 2, -1),
+    ("rope_dim", 3, -1), ("rope_dim", 128, -1), ("q", 0, -1), ("idx", 0, -1),
+    ("q", 0x10008, -1), ("scale", float("inf"), -1), ("q_seq_stride", 12, -1),
+])
+def test_sparse_attn_rejects_before_any_hip_call(sa, field, value, status):
+    a = _args(sa, **{field: value})
+    assert sa.lib().sa_sparse_attn(C.byref(a), None) == status
+
+
+def test_sparse_attn_requires_scales_for_fp8_and_pointers_for_rope(sa):
+    assert sa.lib().sa_sparse_attn(C.byref(_args(sa, kv_format=1)), None) == -1
+    assert sa.lib().sa_sparse_attn(C.byref(_args(sa, rope_dim=16)), None) == -1
+    assert sa.lib().sa_sparse_attn(C.byref(_args(sa, flags=1)), None) == -1
+    assert sa.lib().sa_sparse_attn(None, None) == -1
+
+
+def test_batched_strides_are_checked(sa):
+    a = _args(sa, b=2, q_seq_stride=8)      # smaller than s*h*d
+    assert sa.lib().sa_sparse_attn(C.byref(a), None) == -1
+
+
+def test_window_idxs_validation(sa):
+    L = sa.lib()
+    cols = C.c_int32(0)
+    fake = C.c_void_p(0x10000)
+    assert L.sa_window_topk_idxs(0, 4, 1, None, fake, 16, 4, C.byref(cols), None) == -1
+    assert L.sa_window_topk_idxs(8, 4, 1, fake, fake, 16, 4, C.byref(cols), None) == -2   # chunked prefill
+    assert L.sa_window_topk_idxs(8, 12, 1, None, fake, 96, 4, C.byref(cols), None) == -1  # row stride < cols
+    assert L.sa_window_topk_idxs(8, 1, 2, fake, fake, 4, 8, C.byref(cols), None) == -1    # seq stride
+    assert L.sa_window_topk_idxs(8, 1, 1, None, None, 8, 8, C.byref(cols), None) == -1
+
+
+def test_quant_validation(sa):
+    L = sa.lib()
+    fake = C.c_void_p(0x10000)
+    assert L.sa_quant_kv_fp8(fake, 4, 48, fake, None, None, None) == -1       # d % 32
+    assert L.sa_quant_kv_fp8(fake, 4, 64, None, None, None, None) == -1       # no output
+    assert L.sa_quant_kv_fp8(None, 4, 64, fake, None, None, None) == -1
+    assert L.sa_quant_kv_fp8(fake, 0, 64, fake, None, None, None) == 0        # nothing to do

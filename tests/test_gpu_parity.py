@@ -1,0 +1,259 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle, on the same
+seeded inputs. Indices and fp8 codes must match bit for bit; bf16 outputs must satisfy
+|gpu - oracle| <= 8e-3 + 1.6e-2 |oracle| elementwise."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sa_workloads as W
+from sa_harness import (ATOL, RTOL, assert_close, gpu_indices, gpu_inputs, gpu_run, oracle_indices,
+                        oracle_run, u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import sparse_latent_attention_attn_amd as sa
+    sa.lib()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return sa
+
+
+# ------------------------------------------------------------------ window index lists
+@pytest.mark.parametrize("window,seqlen", [(1, 5), (8, 12), (8, 3), (128, 1), (128, 130), (128, 4096), (16, 300)])
+def test_prefill_lists_bit_exact(sa, window, seqlen):
+    _say("prefill lists", window, seqlen)
+    got = sa.window_topk_idxs(window, seqlen, 2, device="cuda").cpu().numpy()
+    ref = oracle.window_topk_idxs(window, seqlen, [0, 0])
+    assert np.array_equal(got, ref)
+
+
+def test_decode_lists_bit_exact(sa):
+    g = torch.Generator().manual_seed(0)
+    P = torch.cat([torch.tensor([1, 2, 6, 7, 8, 12, 13, 127, 128, 65535], dtype=torch.int32),
+                   torch.randint(1, 70000, (200,), generator=g, dtype=torch.int32)])
+    for window in (8, 128, 5):
+        _say("decode lists", window)
+        got = sa.window_topk_idxs(window, 1, P.numel(), start_pos=P.cuda()).cpu().numpy()
+        ref = oracle.window_topk_idxs(window, 1, P.numpy())
+        assert np.array_equal(got, ref)
+
+
+def test_decode_lists_zero_and_negative_position(sa):
+    P = torch.tensor([0, -3, 5], dtype=torch.int32)
+    got = sa.window_topk_idxs(8, 1, 3, start_pos=P.cuda()).cpu().numpy()
+    assert got[0, 0].tolist() == [0] + [-1] * 7
+    assert got[1, 0].tolist() == [-1] * 8
+    assert got[2, 0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
+
+
+def test_lists_written_in_place_leave_other_columns(sa):
+    _say("in-place lists")
+    buf = torch.full((4, 1, 640), 777, dtype=torch.int32, device="cuda")
+    P = torch.tensor([65535, 200, 3, 128], dtype=torch.int32)
+    sa.window_topk_idxs(128, 1, 4, start_pos=P.cuda(), out=buf)
+    b = buf.cpu().numpy()
+    assert np.array_equal(b[:, :, :128], oracle.window_topk_idxs(128, 1, P.numpy()))
+    assert np.all(b[:, :, 128:] == 777)
+
+
+# ------------------------------------------------------------------ fp8 quantisation
+def _lognormal(seed, rows, d):
+    g = torch.Generator().manual_seed(seed)
+    mag = torch.exp(torch.randn(rows, d // 32, 1, generator=g) * 6.0)
+    x = (torch.randn(rows, d // 32, 32, generator=g) * mag).reshape(rows, d)
+    x[0, :32] = 0.0                                   # an all-zero block
+    x[1, :32] = 1e-30                                  # below the 1e-4 floor
+    x[2, 5] = 3.0e38                                   # near the bf16 maximum
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,d", [(64, 512), (33, 64), (7, 256), (1000, 128)])
+def test_quant_bit_exact(sa, rows, d):
+    _say("quant", rows, d)
+    x = _lognormal(rows + d, rows, d)
+    codes, scales, rt = sa.quant_kv_fp8(x.cuda(), want=("codes", "scales", "roundtrip"))
+    y, c_ref, s_ref = oracle.act_quant(u16(x))
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(u16(rt), y)
+
+
+def test_quant_in_place(sa):
+    x = _lognormal(5, 16, 512)
+    xd = x.cuda()
+    sa.quant_kv_fp8(xd, roundtrip=xd, want=("roundtrip",))
+    assert np.array_equal(u16(xd), oracle.act_quant(u16(x))[0])
+
+
+# ------------------------------------------------------------------ sparse_attn
+def test_ring_cache_sequence(sa):
+    """Prefill 12 tokens into an 8-slot ring, then decode 12 and 13 with the same ring
+    (the three regimes of the attention API docs' ring-cache example); the output of
+    every step against the oracle, bf16 and fp8 storage."""
+    cfg = W.tiny_ring()
+    Wn, h, d, rd = cfg["window"], cfg["h"], cfg["d"], cfg["rd"]
+    sink = cfg["sink"]
+    for fmt in ("bf16", "fp8"):
+        ring_dev = torch.zeros(1, Wn, d, dtype=torch.bfloat16, device="cuda")
+        ring_orc = np.zeros((Wn, d), np.uint16)
+        table = sa.rope_table(rd, 16, device="cuda")
+        cs = oracle.freqs_cis(rd, 16, 10000.0)
+        for step in cfg["steps"]:
+            _say("ring", fmt, step["kind"], step["start_pos"])
+            q, rows = step["q"], step["kv_rows"]
+            S = q.shape[1]
+            P = step["start_pos"]
+            rows_dev = rows.cuda()
+            rows_orc = u16(rows)
+            if fmt == "fp8":
+                (rows_dev,) = sa.quant_kv_fp8(rows_dev.contiguous(), want=("roundtrip",))
+                rows_orc = oracle.act_quant(rows_orc)[0]
+            if step["kind"] == "prefill":
+                kv_dev = rows_dev.view(1, S, d)
+                idx = sa.window_topk_idxs(Wn, S, 1, device="cuda")
+                kv_orc = rows_orc.reshape(1, S, d)
+                idx_orc = oracle.window_topk_idxs(Wn, S, [0])
+                pos = torch.arange(S, dtype=torch.int32).view(1, S)
+                for p_ in range(max(0, S - Wn), S):             # ring writes of the prefill
+                    ring_dev[0, p_ % Wn] = rows_dev[p_]
+                oracle.ring_prefill(ring_orc, rows_orc)
+            else:
+                ring_dev[0, P % Wn] = rows_dev[0]
+                oracle.ring_decode(ring_orc, rows_orc[0], P)
+                kv_dev = ring_dev
+                idx = sa.window_topk_idxs(Wn, 1, 1, start_pos=torch.tensor([P], dtype=torch.int32, device="cuda"))
+                kv_orc = ring_orc.reshape(1, Wn, d)
+                idx_orc = oracle.window_topk_idxs(Wn, 1, [P])
+                pos = torch.tensor([[P]], dtype=torch.int32)
+            assert np.array_equal(idx.cpu().numpy(), idx_orc)
+            assert np.array_equal(u16(ring_dev[0]), ring_orc)
+            if fmt == "fp8":
+                codes, scales = sa.quant_kv_fp8(kv_dev.contiguous(), want=("codes", "scales"))
+                out = sa.sparse_attn(q.cuda(), codes, sink.cuda(), idx, cfg["scale"], kv_scale=scales,
+                                     rope=(table, pos.cuda()))
+            else:
+                out = sa.sparse_attn(q.cuda(), kv_dev, sink.cuda(), idx, cfg["scale"], rope=(table, pos.cuda()))
+            ref = oracle.sparse_attn(u16(q), kv_orc, sink.numpy(), idx_orc, cfg["scale"])
+            ref = oracle.apply_rotary(ref, rd, cs, pos.numpy().reshape(-1), inverse=True)
+            assert_close(u16(out).reshape(-1, h, d), ref, f"ring {fmt} {step['kind']} {P}")
+
+
+@pytest.mark.parametrize("name", ["decode_window", "prefill_window", "decode_compress", "prefill_compress"])
+@pytest.mark.parametrize("fmt,rope", [("bf16", True), ("bf16", False), ("fp8", True)])
+def test_small_workloads(sa, name, fmt, rope):
+    w = W.small_variant(name)
+    _say("small", name, fmt, rope, tuple(w.q.shape), w.topk)
+    out, idx = gpu_run(w, fmt, rope)
+    assert np.array_equal(idx.cpu().numpy(), oracle_indices(w))
+    ref = oracle_run(w, rope=rope, round_trip=w.kv_roundtrip or fmt == "fp8")
+    assert_close(u16(out).reshape(-1, w.h, w.d), ref, f"{name} {fmt} rope={rope}")
+
+
+@pytest.mark.parametrize("seed,b,s,h,d,rows,topk,hole,dup", [
+    (1, 1, 3, 1, 64, 40, 7, 0.0, False),
+    (2, 2, 5, 20, 128, 100, 33, 0.3, True),
+    (3, 3, 2, 100, 512, 300, 100, 0.1, False),
+    (4, 1, 4, 160, 256, 64, 64, 0.5, True),
+    (5, 2, 1, 128, 512, 2000, 1000, 0.02, False),
+    (6, 1, 2, 64, 64, 9, 1, 0.0, False),
+    (7, 4, 3, 16, 512, 50, 31, 0.9, True),
+])
+def test_random_problems(sa, seed, b, s, h, d, rows, topk, hole, dup):
+    _say("random", seed, b, s, h, d, rows, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, d, rows, topk, hole, dup, sink_std=2.0)
+    scale = float(np.float32(d ** -0.5))
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, d), ref, f"random {seed}")
+
+
+def test_strided_sequences(sa):
+    """Per-sequence blocks inside larger buffers (non-packed sequence strides)."""
+    q, kv, sink, idx = W.rand_problem(21, 3, 2, 32, 128, 50, 40, 0.1, False)
+    qb = torch.zeros(3, 4, 32, 128, dtype=torch.bfloat16)
+    qb[:, :2] = q
+    kvb = torch.zeros(3, 70, 128, dtype=torch.bfloat16)
+    kvb[:, :50] = kv
+    ib = torch.full((3, 5, 40), -1, dtype=torch.int32)
+    ib[:, :2] = idx
+    qd, kvd, idd = qb.cuda(), kvb.cuda(), ib.cuda()
+    outb = torch.zeros(3, 6, 32, 128, dtype=torch.bfloat16, device="cuda")
+    sa.sparse_attn(qd[:, :2], kvd[:, :50], sink.cuda(), idd[:, :2], 0.088, out=outb[:, :2])
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), 0.088)
+    assert_close(u16(outb[:, :2]).reshape(-1, 32, 128), ref, "strided")
+    assert torch.all(outb[:, 2:] == 0)
+
+
+def test_empty_lists_and_no_sink(sa):
+    q, kv, sink, idx = W.rand_problem(31, 1, 3, 16, 64, 20, 40, 0.0, False)
+    idx[0, 1] = -1
+    idx[0, 2, 5:] = -9
+    for sk in (sink, torch.full_like(sink, -math.inf)):
+        out = sa.sparse_attn(q.cuda(), kv.cuda(), sk.cuda(), idx.cuda(), 0.125)
+        o = out.float().cpu()
+        assert torch.isfinite(o).all()
+        assert torch.all(o[0, 1] == 0)
+        ref = oracle.sparse_attn(u16(q), u16(kv), sk.numpy(), idx.numpy(), 0.125)
+        assert_close(u16(out).reshape(-1, 16, 64), ref, "empty/no-sink")
+
+
+def test_check_idx_flag(sa):
+    q, kv, sink, idx = W.rand_problem(41, 1, 2, 16, 64, 20, 10, 0.0, False)
+    bad = idx.clone()
+    bad[0, 1, 3] = 20                      # == kv_rows: out of range
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), bad.cuda(), 0.125, err_word=err, check_idx=True)
+    assert int(err.item()) & 1
+    skip = idx.clone()
+    skip[0, 1, 3] = -1                     # the bad column is treated as a skip
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), skip.numpy(), 0.125)
+    assert_close(u16(out).reshape(-1, 16, 64), ref, "check_idx")
+    err.zero_()
+    sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), 0.125, err_word=err, check_idx=True)
+    assert int(err.item()) == 0
+
+
+def test_deterministic_and_order_free(sa):
+    w = W.small_variant("decode_compress")
+    q, kv, _, sink, idx = gpu_inputs(w)
+    a = sa.sparse_attn(q, kv, sink, idx, w.scale)
+    b = sa.sparse_attn(q, kv, sink, idx, w.scale)
+    assert torch.equal(a, b)
+    perm = torch.randperm(idx.shape[-1], generator=torch.Generator().manual_seed(1)).cuda()
+    c = sa.sparse_attn(q, kv, sink, idx[..., perm].contiguous(), w.scale)
+    assert_close(u16(c), u16(a), "column order")
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+FULL = {
+    "decode_window": [0, 7, 19, 31],
+    "prefill_window": [0, 1, 126, 127, 128, 2047, 4095],
+    "decode_compress": [0, 13, 63],
+    "prefill_compress": [0, 3, 126, 127, 1000, 4097, 8191],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(sa, name):
+    """The workload at its full size in the configuration the bench times (bf16 storage,
+    epilogue on); the oracle computes a sample of queries one by one."""
+    _say("full", name)
+    w = W.make(name)
+    out, idx = gpu_run(w, "bf16", True)
+    sel = np.array(FULL[name], np.int64)
+    ref_idx = oracle_indices(w)
+    got_idx = idx.cpu().numpy()
+    assert np.array_equal(got_idx, ref_idx)
+    ref = oracle_run(w, qsel=sel, rope=True)
+    got = u16(out).reshape(-1, w.h, w.d)[sel]
+    assert_close(got, ref, f"full {name}")
