@@ -70,6 +70,7 @@ def lib():
             "orc_sparse_attn_weights_f64": (C.c_int, [C.POINTER(AttnProblem), I64, I32, P, P]),
             "orc_freqs_cis": (None, [I32, I32, F, P]),
             "orc_apply_rotary": (C.c_int, [P, I64, I32, I32, I32, P, I32, P, I32]),
+            "orc_max_threads": (I32, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -90,6 +91,10 @@ def _u16(a) -> np.ndarray:
     a = np.ascontiguousarray(a)
     assert a.dtype == np.uint16, a.dtype
     return a
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- scalar/vector numerics

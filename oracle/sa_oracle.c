@@ -14,6 +14,15 @@
 #include <omp.h>
 #endif
 
+int32_t orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* bf16 <-> f32. [attn-docs] precision paragraph: tensors are bf16, arithmetic is f32.   */
 /* The pages do not name a rounding mode for "returns bf16"; the reading taken is        */

@@ -104,6 +104,9 @@ void orc_freqs_cis(int32_t rd, int32_t max_pos, float base, float *cos_sin);
 int orc_apply_rotary(uint16_t *x, int64_t n, int32_t h, int32_t d, int32_t rd,
                      const float *cos_sin, int32_t max_pos, const int32_t *pos, int32_t inverse);
 
+/* threads an nthreads <= 0 call uses (the OpenMP default), 1 without OpenMP */
+int32_t orc_max_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,13 +32,15 @@ namespace sa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte chunk swizzle of LDS row r: for 16 consecutive rows read at one chunk (the K
-// operand) the swizzled chunks are all different, and so are they for the 4 rows x 2
-// adjacent chunks a 16-lane group touches in a transposing read. The swizzle only changes
-// the low four bits of the chunk index.
+// 16-byte chunk swizzle of LDS row r. Both operand reads must hit distinct banks:
+//   K operand: 16 consecutive rows at one chunk -> swz must be a bijection on r mod 16;
+//   V operand: a transposing read covers 8 consecutive rows x 2 adjacent chunks (c, c^1)
+//   -> swz(r) >> 1 must differ across every 8 aligned consecutive rows.
+// ((r & 7) << 1) | ((r >> 3) & 1) does both; it only changes the low four bits of a chunk
+// index (for rows narrower than 16 chunks it is cut down to the row).
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
-    return ((((r & 3) << 2) | ((r >> 2) & 3))) & (CH - 1);
+    return (((r & 7) << 1) | ((r >> 3) & 1)) & (CH - 1);
 }
 
 template <int D>
@@ -51,56 +53,68 @@ struct Geo {
     static constexpr int kTileBytes = kTileKeys * kRowBytes;
 };
 
-// Indices of one tile: lane j < 32 of every wave holds column col0 + j as a row of kv
-// (-1 when the column is a skip, lies beyond the split, or is out of range). Loaded one
-// tile ahead so the gather itself never waits on an index load.
-__device__ __forceinline__ int load_tile_idx(const KParams& p, const int32_t* idx_row, int col0,
-                                             int col1, int lane) {
-    const int col = col0 + lane;
-    int row = (lane < kTileKeys && col < col1) ? idx_row[col] : -1;
-    if (row >= p.kv_rows) {
-        if (p.flags & 1u) atomicOr(p.err_word, 1);
-        row = -1;
-    }
-    return row < 0 ? -1 : row;
+// Direct-to-LDS gather of one key tile (bf16 storage). The tile's row indices are read
+// from the index stage in LDS (-1 = skip). Every wave issues exactly kInsts/NW loads per
+// tile, whatever the indices, so that waiting for the oldest tile in flight is an exact
+// vmcnt: a skipped row loads row 0 of the sequence instead, and zero_skipped_rows clears it
+// once it has landed (a zero row can never turn a zero probability into a NaN).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// raw buffer load of 16 bytes per lane straight into LDS (M0 = lds base, lane i -> +16 i)
+__device__ void raw_buffer_load_lds(i32x4 rsrc, SA_LDS void* lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource of one sequence's kv rows: base, no stride, `bytes` records (reads past
+// them return zeros), gfx9 default format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)(a >> 32) & 0xffff;
+    r[2] = (int32_t)bytes;
+    r[3] = 0x00020000;
+    return r;
 }
 
-// Issue the gather of one key tile into LDS (bf16 storage). Every lane either starts a
-// 16-byte direct-to-LDS load of its chunk or, for a skipped column, writes zeros into that
-// chunk (so the tile never holds stale or non-finite data where the probability is zero).
-// The loads are dealt round-robin to the waves.
 template <int D, int NW>
-__device__ __forceinline__ void gather_tile_bf16(const uint8_t* kv_seq, int tidx,
+__device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_t* tidx,
                                                  SA_LDS uint8_t* buf, int wid, int lane) {
     using G = Geo<D>;
     constexpr int kInsts = kTileKeys / G::kRowsPerInst;
-    static_assert(kTileKeys % G::kRowsPerInst == 0, "tile split");
+    static_assert(kTileKeys % G::kRowsPerInst == 0 && kInsts % NW == 0, "tile split");
     const int sub = lane / G::kChunks;          // row within one load
     const int pc = lane % G::kChunks;           // physical chunk this lane fills
 #pragma unroll
-    for (int j = 0; j < (kInsts + NW - 1) / NW; ++j) {
-        const int i = wid + j * NW;
-        if (i >= kInsts) break;
-        const int r0 = i * G::kRowsPerInst;
+    for (int j = 0; j < kInsts / NW; ++j) {
+        const int r0 = (wid + j * NW) * G::kRowsPerInst;   // loads dealt round-robin to waves
         const int r = r0 + sub;
-        const int row = __shfl(tidx, r, kWave);
-        if (row >= 0) {
-            const int lc = pc ^ swz<G::kChunks>(r);
-            const uint8_t* src = kv_seq + (int64_t)row * G::kRowBytes + lc * 16;
-            __builtin_amdgcn_global_load_lds((const void*)src, (SA_LDS void*)(buf + r0 * G::kRowBytes),
-                                             16, 0, 0);
-        } else {
-            *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
-        }
+        const int row = max(tidx[r], 0);
+        const int voff = row * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        raw_buffer_load_lds(rsrc, (SA_LDS void*)(buf + r0 * G::kRowBytes), 16, voff, 0, 0, 0);
     }
 }
 
-// fp8 storage: the same gather, of e4m3 codes (D bytes per row) and the row's D/32 scale
-// bytes, into a raw staging tile; converted to the bf16 tile by convert_tile_fp8.
+// Zero the rows of a landed tile whose column is a skip (only the rows this wave loaded).
 template <int D, int NW>
-__device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uint8_t* sc_seq, int tidx,
-                                                SA_LDS uint8_t* raw, SA_LDS uint8_t* raw_sc, int wid,
-                                                int lane) {
+__device__ __forceinline__ void zero_skipped_rows(SA_LDS const int32_t* tidx, SA_LDS uint8_t* buf,
+                                                  int wid, int lane) {
+    using G = Geo<D>;
+    constexpr int kInsts = kTileKeys / G::kRowsPerInst;
+    const int sub = lane / G::kChunks;
+    const int pc = lane % G::kChunks;
+#pragma unroll
+    for (int j = 0; j < kInsts / NW; ++j) {
+        const int r = (wid + j * NW) * G::kRowsPerInst + sub;
+        if (tidx[r] < 0) *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
+    }
+}
+
+// fp8 storage: the gather of e4m3 codes (D bytes per row) and the row's D/32 scale bytes
+// into a raw staging tile (zeros for skipped rows), converted to the bf16 tile by
+// convert_tile_fp8.
+template <int D, int NW>
+__device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uint8_t* sc_seq,
+                                                SA_LDS const int32_t* tidx, SA_LDS uint8_t* raw,
+                                                SA_LDS uint8_t* raw_sc, int wid, int lane) {
     constexpr int kCodeChunks = D / 16;                    // 16-byte chunks of codes per row
     constexpr int kRowsPerInst = 64 / kCodeChunks;
     constexpr int kInsts = kTileKeys / kRowsPerInst;
@@ -113,7 +127,7 @@ __device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uin
         if (i >= kInsts) break;
         const int r0 = i * kRowsPerInst;
         const int r = r0 + sub;
-        const int row = __shfl(tidx, r, kWave);
+        const int row = tidx[r];
         if (row >= 0) {
             const uint8_t* src = kv_seq + (int64_t)row * D + pc * 16;
             __builtin_amdgcn_global_load_lds((const void*)src, (SA_LDS void*)(raw + r0 * D), 16, 0, 0);
@@ -121,11 +135,9 @@ __device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uin
             *(SA_LDS u32x4*)(raw + r * D + pc * 16) = u32x4{0, 0, 0, 0};
         }
     }
-    // scale bytes: D/32 per row, wave 0 one lane per row (zeros for a skipped row make
-    // every value of the row decode to zero)
     constexpr int kSc = D / 32;
-    const int row = __shfl(tidx, lane & 63, kWave);
     if (wid == 0 && lane < kTileKeys) {
+        const int row = tidx[lane];
         for (int j = 0; j < kSc; ++j)
             raw_sc[lane * kSc + j] = row >= 0 ? sc_seq[(int64_t)row * kSc + j] : (uint8_t)0;
     }
@@ -166,17 +178,18 @@ __device__ __forceinline__ void convert_tile_fp8(SA_LDS const uint8_t* raw, SA_L
 // to bf16; with `rot`, the inverse rotation of the pairs that fall in the last rope_dim
 // elements (apply_rotary_emb with inverse=True: multiply by the conjugate in f32, back to
 // bf16). A pair outside the rope tail is rotated by (1, 0), which returns it unchanged.
-// `cs` points at the position's row of the (cos, sin) table. Returns two packed bf16 pairs.
+// `cs` is the position's row of the (cos, sin) table. Returns two packed bf16 pairs.
+template <typename CsPtr>
 __device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a3, float inv_l,
-                                           bool rot, int d0, int r0, const float* cs) {
+                                           bool rot, int d0, int r0, CsPtr cs) {
     uint32_t w[2] = {pack_bf16x2(a0 * inv_l, a1 * inv_l), pack_bf16x2(a2 * inv_l, a3 * inv_l)};
     if (rot) {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int dk = d0 + 2 * k;
             const bool in = dk >= r0;
-            const float2 t = *(const float2*)(cs + (in ? (dk - r0) : 0));
-            const float c = in ? t.x : 1.0f, sn = in ? t.y : 0.0f;
+            const int o = in ? (dk - r0) : 0;
+            const float c = in ? cs[o] : 1.0f, sn = in ? cs[o + 1] : 0.0f;
             const float x = bf16_lo(w[k]), y = bf16_hi(w[k]);
             w[k] = pack_bf16x2(x * c + y * sn, y * c - x * sn);
         }
@@ -208,16 +221,42 @@ __device__ __forceinline__ float max4groups(float v) {
     return v;
 }
 
+// Pipeline shape of the bf16 path: kBuffers LDS tile buffers, tiles gathered kAhead ahead
+// of the one being multiplied. The only vector-memory operations inside the key loop are
+// the tile loads (kLoadsPerWave per wave per tile), so when tile t is needed the loads
+// issued after it are exactly those of tiles t+1 .. t+kAhead-1: the wait is vmcnt(kWait),
+// which must fit the 6-bit counter.
+template <int D, int NW>
+struct Pipe {
+    static constexpr int kLoadsPerWave = kTileKeys / Geo<D>::kRowsPerInst / NW;
+    static constexpr int kBuffers = 4;
+    static constexpr int kAheadMax = 1 + 63 / kLoadsPerWave;
+    static constexpr int kAhead = kBuffers - 1 < kAheadMax ? kBuffers - 1 : kAheadMax;
+    static constexpr int kWait = (kAhead - 1) * kLoadsPerWave;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int D, bool FP8, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     using G = Geo<D>;
+    using PP = Pipe<D, NW>;
+    constexpr int NB = FP8 ? 1 : PP::kBuffers;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
-    // bf16: two tiles. fp8: one bf16 tile, then two raw staging tiles of codes, then two
-    // of scale bytes.
-    auto tile = [&](int i) { return smem + i * G::kTileBytes; };
-    auto raw = [&](int i) { return smem + G::kTileBytes + i * (kTileKeys * D); };
-    auto raw_sc = [&](int i) { return smem + G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
+    // LDS: the index stage (kMaxColsPerSplit int32), then NB bf16 tiles; fp8 adds two raw
+    // staging tiles of codes and two of scale bytes.
+    SA_LDS int32_t* istage = (SA_LDS int32_t*)smem;
+    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4;
+    auto tile = [&](int i) { return tiles + i * G::kTileBytes; };
+    auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
+    auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
 
     const int tid = threadIdx.x;
     const int wid = tid / kWave;
@@ -225,8 +264,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int l16 = lane & 15;                  // this lane's head within the wave
     const int q4 = lane >> 4;                   // lane group 0..3
 
-    // work item: ((query * head_blocks) + head block) * splits + split
+    // work item: ((query * head_blocks) + head block) * splits + split. Workgroups are
+    // dealt to the 8 XCDs round-robin (block b runs on XCD b % 8); remapping consecutive
+    // items onto one XCD keeps the workgroups of a query, which gather the same rows, in
+    // that XCD's L2.
     int item = blockIdx.x;
+    {
+        const int n8 = gridDim.x / 8;
+        if (item < 8 * n8) item = (item % 8) * n8 + item / 8;
+    }
     const int split = item % p.splits;
     item /= p.splits;
     const int hblk = item % p.head_blocks;
@@ -239,11 +285,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 
     const int32_t* idx_row = p.idx + (int64_t)seq * p.idx_seq_stride + (int64_t)t * p.topk;
     const int col_begin = split * p.cols_per_split;
-    const int col_end = min(p.topk, col_begin + p.cols_per_split);
-    const int ntiles = col_end > col_begin ? (col_end - col_begin + kTileKeys - 1) / kTileKeys : 0;
+    const int ncols = max(0, min(p.topk, col_begin + p.cols_per_split) - col_begin);
 
     const uint8_t* kv_seq = p.kv + (int64_t)seq * p.kv_seq_stride_bytes;
     const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
+    const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
 
     // Q as the B operand of the 16x16x32 product: lane holds head l16, d = 32*kk + 8*q4 + 0..7
     u32x4 qreg[G::kKSteps];
@@ -253,8 +299,35 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int kk = 0; kk < G::kKSteps; ++kk)
             qreg[kk] = head_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
     }
-
     const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+
+    // Stage this split's index columns in LDS, skips and out-of-range rows as -1, padded
+    // to whole tiles; find the last column that names a row (trailing tiles of padding are
+    // never gathered).
+    int err = 0;
+    int last = -1;
+    const int ncols_pad = (ncols + kTileKeys - 1) / kTileKeys * kTileKeys;
+    for (int c = tid; c < ncols_pad; c += NW * kWave) {
+        int row = c < ncols ? idx_row[col_begin + c] : -1;
+        if (row >= p.kv_rows) { err = 1; row = -1; }
+        row = row < 0 ? -1 : row;
+        istage[c] = row;
+        if (row >= 0) last = c;
+    }
+    {
+        // workgroup-wide max of `last` through the stage's spare... one LDS word per wave
+        for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    }
+    __syncthreads();
+    {
+        SA_LDS int32_t* lastw = (SA_LDS int32_t*)(tiles);          // scratch before any gather
+        if (lane == 0) lastw[wid] = last;
+        __syncthreads();
+        for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
+        __syncthreads();
+    }
+    const int ntiles = (last + kTileKeys) / kTileKeys;        // 0 when nothing is named
+
     float m_run = sink2;                                       // log2 domain
     float l_run = (q4 == 0 && split == 0) ? 1.0f : 0.0f;       // the sink's exp(0)
     f32x4 o_acc[G::kDBlocks];
@@ -290,37 +363,42 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
     }
 
-    // first gather; the index vector of the following tile is fetched one tile ahead
-    int tidx = ntiles > 0 ? load_tile_idx(p, idx_row, col_begin, col_end, lane) : -1;
-    if (ntiles > 0) {
-        if constexpr (FP8)
-            gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx, raw(0), raw_sc(0), wid, lane);
-        else
-            gather_tile_bf16<D, NW>(kv_seq, tidx, tile(0), wid, lane);
+    // prologue: the first kAhead tiles (bf16) or the first tile (fp8)
+    constexpr int kAhead = FP8 ? 1 : PP::kAhead;
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+        if (j < ntiles) {
+            if constexpr (FP8)
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, istage + j * kTileKeys, raw(0), raw_sc(0), wid, lane);
+            else
+                gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
+        }
     }
-    int nidx = ntiles > 1 ? load_tile_idx(p, idx_row, col_begin + kTileKeys, col_end, lane) : -1;
 
     for (int it = 0; it < ntiles; ++it) {
-        // which columns of this tile are real rows (one bit per key)
-        const uint32_t valid = (uint32_t)__ballot(tidx >= 0);
-        tidx = nidx;
-
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        SA_LDS const int32_t* tidx = istage + it * kTileKeys;
+        // which columns of this tile name a row (one bit per key)
+        const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
         SA_LDS uint8_t* cur;
         if constexpr (FP8) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
             if (it + 1 < ntiles)
-                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx + kTileKeys, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
             convert_tile_fp8<D, NW>(raw(it & 1), raw_sc(it & 1), tile(0), tid);
             __syncthreads();
             cur = tile(0);
         } else {
-            if (it + 1 < ntiles)
-                gather_tile_bf16<D, NW>(kv_seq, tidx, tile((it + 1) & 1), wid, lane);
-            cur = tile(it & 1);
+            // tile `it` has landed once only the loads of the kAhead-1 younger tiles remain
+            if (it + kAhead <= ntiles) wait_vmcnt<PP::kWait>();
+            else wait_vmcnt<0>();
+            cur = tile(it % NB);
+            if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
+            __syncthreads();               // tile visible to all; buffer of tile it-1 free
+            if (it + kAhead < ntiles)
+                gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAhead * kTileKeys, tile((it + kAhead) % NB), wid, lane);
         }
-        if (it + 2 < ntiles)
-            nidx = load_tile_idx(p, idx_row, col_begin + (it + 2) * kTileKeys, col_end, lane);
+        if (valid == 0) continue;                              // a tile of skips only
 
         // Opaque to the optimiser: addresses derived from the offsets are then formed next
         // to their reads inside the loop instead of being hoisted (and spilled) in bulk.
@@ -333,24 +411,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[ab][k]));
 
-        // ---- S^T = K . Q^T over the tile's two 16-key blocks; the K operand of step kk+1
-        //      is read while step kk multiplies, and scheduling fences keep the compiler
-        //      from hoisting every read of the unrolled loop.
+        // ---- S^T = K . Q^T over the tile's two 16-key blocks. K operands are read
+        //      kPre steps ahead of their multiply; scheduling fences keep the compiler from
+        //      hoisting every read of the unrolled loop.
         f32x4 s_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         {
-            u32x4 an0 = *(SA_LDS const u32x4*)(cur + qk_off[0][0]);
-            u32x4 an1 = *(SA_LDS const u32x4*)(cur + qk_off[1][0]);
+            constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
+            u32x4 a0[kPre], a1[kPre];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) {
+                a0[k] = *(SA_LDS const u32x4*)(cur + qk_off[0][k & 3] + 256 * (k >> 2));
+                a1[k] = *(SA_LDS const u32x4*)(cur + qk_off[1][k & 3] + 256 * (k >> 2));
+            }
 #pragma unroll
             for (int kk = 0; kk < G::kKSteps; ++kk) {
-                const u32x4 a0 = an0, a1 = an1;
-                if (kk + 1 < G::kKSteps) {
-                    const int nk = kk + 1;
-                    an0 = *(SA_LDS const u32x4*)(cur + qk_off[0][nk & 3] + 256 * (nk >> 2));
-                    an1 = *(SA_LDS const u32x4*)(cur + qk_off[1][nk & 3] + 256 * (nk >> 2));
+                const u32x4 c0 = a0[kk % kPre], c1 = a1[kk % kPre];
+                if (kk + kPre < G::kKSteps) {
+                    const int nk = kk + kPre;
+                    a0[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[0][nk & 3] + 256 * (nk >> 2));
+                    a1[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[1][nk & 3] + 256 * (nk >> 2));
                 }
                 const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[kk]);
-                s_acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb, s_acc[0], 0, 0, 0);
-                s_acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb, s_acc[1], 0, 0, 0);
+                s_acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0], 0, 0, 0);
+                s_acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -396,18 +479,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         l_run += psum;
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time
+        // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time;
+        //      V operands read kPre slices ahead
         {
             const bf16x8 pk = __builtin_bit_cast(bf16x8, pb);
-            bf16x4v va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][0]));
-            bf16x4v vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][0]));
+            constexpr int kPre = 2;
+            bf16x4v va[kPre], vb[kPre];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) {
+                va[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][k & 7] + 256 * (k >> 3)));
+                vb[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][k & 7] + 256 * (k >> 3)));
+            }
 #pragma unroll
             for (int db = 0; db < G::kDBlocks; ++db) {
-                const bf16x8 a = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                if (db + 1 < G::kDBlocks) {
-                    const int nb = db + 1;
-                    va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][nb & 7] + 256 * (nb >> 3)));
-                    vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][nb & 7] + 256 * (nb >> 3)));
+                const bf16x8 a = __builtin_shufflevector(va[db % kPre], vb[db % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
+                if (db + kPre < G::kDBlocks) {
+                    const int nb = db + kPre;
+                    va[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][nb & 7] + 256 * (nb >> 3)));
+                    vb[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][nb & 7] + 256 * (nb >> 3)));
                 }
                 o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk, o_acc[db], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -415,23 +504,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
     }
 
+    // a skipped index >= kv_rows is reported once per wave
+    if ((p.flags & 1u) && __ballot(err) != 0 && lane == 0) atomicOr(p.err_word, 1);
+
     // ---- finish: the four lane groups share m_run; their partial sums add up
     const float l_tot = sum4groups(l_run);
-    if (!head_ok) return;
     // O^T accumulator layout: lane holds head l16, d = 16*db + 4*q4 + (0..3)
     if (p.splits == 1) {
+        // the position's (cos, sin) row, staged once in LDS for all heads of the query (the
+        // index stage is free now), so the stores below never wait on table loads
+        const float* cs_g = rope_row(p, seq, t, tid == 0);
+        SA_LDS float* cs = (SA_LDS float*)smem;
+        __syncthreads();
+        if (cs_g != nullptr)
+            for (int i = tid; i < p.rope_dim; i += NW * kWave) cs[i] = cs_g[i];
+        __syncthreads();
+        if (!head_ok) return;
         const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        const float* cs = rope_row(p, seq, t, lane == 0);
         const int r0 = D - p.rope_dim;
         uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head) * D;
 #pragma unroll
         for (int db = 0; db < G::kDBlocks; ++db) {
             const int d0 = 16 * db + 4 * q4;
-            const bool rot = cs != nullptr && 16 * db + 16 > r0;    // slice meets the rope tail
+            const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
             *(u32x2*)(orow + d0) = epilogue4(o_acc[db][0], o_acc[db][1], o_acc[db][2], o_acc[db][3],
-                                             inv_l, rot, d0, r0, cs);
+                                             inv_l, rot, d0, r0, (SA_LDS const float*)cs);
         }
     } else {
+        if (!head_ok) return;
         const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head;
         float* wo = p.ws_o + slot * D;
 #pragma unroll
@@ -495,8 +595,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
 template <int D, bool FP8, int NW>
 static hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
-    const size_t lds = FP8 ? G::kTileBytes + 2 * kTileKeys * D + 2 * kTileKeys * (D / 32)
-                           : 2 * (size_t)G::kTileBytes;
+    constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
+    const size_t lds = (size_t)kMaxColsPerSplit * 4 + (size_t)NB * G::kTileBytes +
+                       (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
     auto k = attn_fwd_kernel<D, FP8, NW>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

@@ -1,5 +1,7 @@
 // The two helpers around sparse_attn: the ring-cache window index lists and the block-32
 // ue8m0 fp8 quantisation of KV rows.
+#include <climits>
+
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -12,13 +14,12 @@ namespace sa {
 __global__ void window_idxs_kernel(int32_t window, int32_t seqlen, int32_t nseq,
                                    const int32_t* __restrict__ start_pos, int32_t* __restrict__ idx,
                                    int64_t seq_stride, int64_t row_stride, int32_t cols) {
-    const int64_t total = (int64_t)nseq * seqlen * cols;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t j = (int32_t)(e % cols);
-        const int64_t rt = e / cols;
-        const int32_t t = (int32_t)(rt % seqlen);
-        const int32_t n = (int32_t)(rt / seqlen);
+    // one thread per list entry: blockIdx.y walks the (sequence, query) rows, x the columns
+    const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= cols) return;
+    for (int32_t rt = blockIdx.y; rt < nseq * seqlen; rt += gridDim.y) {
+        const int32_t t = rt % seqlen;
+        const int32_t n = rt / seqlen;
         int32_t v;
         if (start_pos == nullptr) {
             // prefill from position 0: chunk rows lo..t, lo = max(0, t - window + 1)
@@ -27,8 +28,13 @@ __global__ void window_idxs_kernel(int32_t window, int32_t seqlen, int32_t nseq,
         } else {
             const int32_t P = start_pos[n];
             if (P < 0) v = -1;
-            else if (P >= window - 1) v = (int32_t)(((int64_t)P + 1 + j) % window);  // full ring
-            else v = j <= P ? j : -1;                                              // slots 0..P
+            else if (P >= window - 1) {
+                // full ring: the oldest token P - window + 1 sits in slot (P + 1) mod window
+                const int32_t s = P % window + 1 + j;
+                v = s >= window ? s - window : s;
+            } else {
+                v = j <= P ? j : -1;                              // ring holds slots 0..P
+            }
         }
         idx[(int64_t)n * seq_stride + (int64_t)t * row_stride + j] = v;
     }
@@ -37,11 +43,12 @@ __global__ void window_idxs_kernel(int32_t window, int32_t seqlen, int32_t nseq,
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
                               hipStream_t st) {
-    const int64_t total = (int64_t)nseq * seqlen * cols;
-    const int threads = 256;
-    const int64_t want = (total + threads - 1) / threads;
-    const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(window_idxs_kernel, dim3(blocks), dim3(threads), 0, st, window, seqlen, nseq,
+    if ((int64_t)nseq * seqlen > INT32_MAX) return hipErrorInvalidValue;
+    const int threads = cols >= 256 ? 256 : ((cols + 63) / 64) * 64;
+    const int gx = (cols + threads - 1) / threads;
+    const int64_t rows = (int64_t)nseq * seqlen;
+    const int gy = (int)(rows < 65535 ? rows : 65535);
+    hipLaunchKernelGGL(window_idxs_kernel, dim3(gx, gy), dim3(threads), 0, st, window, seqlen, nseq,
                        start_pos, idx, seq_stride, row_stride, cols);
     return hipGetLastError();
 }

@@ -3,6 +3,7 @@
 // the caller's stream. Nothing is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
@@ -56,6 +57,9 @@ int check_shape(const sa_attn_args* a) {
     if (a->q_seq_stride % 8 || a->out_seq_stride % 8) return SA_ERR_INVALID;
     if (a->kv_format == SA_KV_BF16 ? (a->kv_seq_stride % 8) : (a->kv_seq_stride % 16)) return SA_ERR_INVALID;
     if (!std::isfinite(a->scale)) return SA_ERR_INVALID;
+    // one sequence's kv rows are addressed with 32-bit byte offsets
+    const int64_t row_bytes = a->kv_format == SA_KV_BF16 ? 2 * (int64_t)a->d : a->d;
+    if ((int64_t)a->kv_rows * row_bytes > INT32_MAX) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
 
@@ -72,18 +76,39 @@ int check_pointers(const sa_attn_args* a) {
     return SA_OK;
 }
 
+// Work decomposition. A workgroup takes 16*nw heads of one query and a contiguous range
+// of its index columns; its waves share every gathered key tile. Prefer the widest head
+// block that still gives at least one workgroup per compute unit (fewest re-reads of a
+// query's rows); split the columns across workgroups only when even one-wave blocks leave
+// compute units idle and each split keeps at least kMinTilesPerSplit tiles, because every
+// split writes an f32 partial of 16*nw heads x d (as large as 16*nw/8 key tiles).
+constexpr int kMinTilesPerSplit = 8;
+
 sa::Plan make_plan(const sa_attn_args* a, int cus) {
-    sa::Plan pl{};
     using sa::kHeadsPerWave;
     using sa::kTileKeys;
-    const int waves_needed = (a->h + kHeadsPerWave - 1) / kHeadsPerWave;
-    pl.nw = waves_needed >= sa::kMaxWaves ? sa::kMaxWaves : waves_needed <= 1 ? 1 : 2;
-    pl.head_blocks = (a->h + pl.nw * kHeadsPerWave - 1) / (pl.nw * kHeadsPerWave);
+    sa::Plan pl{};
+    const int64_t nq = (int64_t)a->b * a->s;
+    auto blocks_for = [&](int nw) { return (a->h + nw * kHeadsPerWave - 1) / (nw * kHeadsPerWave); };
+    const int max_nw = std::min<int>(sa::kMaxWaves, (a->h + kHeadsPerWave - 1) / kHeadsPerWave);
+    pl.nw = 1;
+    for (int nw = max_nw; nw >= 1; nw /= 2) {
+        if (nw == 3) continue;
+        if (nq * blocks_for(nw) >= cus || nw == 1) { pl.nw = nw; break; }
+    }
+    if (max_nw == 3) pl.nw = nq * blocks_for(2) >= cus ? 2 : 1;
+    pl.head_blocks = blocks_for(pl.nw);
     pl.h_pad = pl.head_blocks * pl.nw * kHeadsPerWave;
     const int ntiles = (a->topk + kTileKeys - 1) / kTileKeys;
-    const int64_t wgs = (int64_t)a->b * a->s * pl.head_blocks;
+    const int64_t wgs = nq * pl.head_blocks;
     int splits = 1;
-    if (wgs < cus) splits = (int)std::min<int64_t>(ntiles, (cus + wgs - 1) / wgs);
+    if (wgs < cus) {
+        const int64_t want = (cus + wgs - 1) / wgs;
+        splits = (int)std::max<int64_t>(1, std::min<int64_t>(want, ntiles / kMinTilesPerSplit));
+    }
+    // a workgroup stages at most kMaxColsPerSplit index columns
+    const int max_tiles = sa::kMaxColsPerSplit / kTileKeys;
+    splits = std::max(splits, (ntiles + max_tiles - 1) / max_tiles);
     const int tiles_per_split = (ntiles + splits - 1) / splits;
     pl.cols_per_split = tiles_per_split * kTileKeys;
     pl.splits = (a->topk + pl.cols_per_split - 1) / pl.cols_per_split;

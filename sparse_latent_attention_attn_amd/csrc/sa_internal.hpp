@@ -11,6 +11,7 @@ namespace sa {
 constexpr int kTileKeys = 32;       // index columns per key tile
 constexpr int kHeadsPerWave = 16;   // heads one wave owns
 constexpr int kMaxWaves = 4;        // waves per workgroup
+constexpr int kMaxColsPerSplit = 4096;  // index columns one workgroup stages in LDS
 
 // Everything one sparse_attn launch needs, passed by value as the kernel argument.
 struct KParams {
