@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // LDS: the index stage (kMaxColsPerSplit int32), then NB bf16 tiles; fp8 adds two raw
     // staging tiles of codes and two of scale bytes.
     SA_LDS int32_t* istage = (SA_LDS int32_t*)smem;
-    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4;
+    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4 + 64;
     auto tile = [&](int i) { return tiles + i * G::kTileBytes; };
     auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
     auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
@@ -291,6 +291,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
     const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
 
+    // ---- start-up, arranged so that its memory latencies overlap: the index loads go out
+    // first, then Q and the sink; the index stage is written as soon as the index loads
+    // land (Q may still be in flight), the first key tiles are issued, and only then does
+    // anything wait for Q.
+    //
+    // Stage this split's index columns in LDS, skips and out-of-range rows as -1, padded
+    // to whole tiles, and find the last column that names a row (trailing tiles of padding
+    // are never gathered). Each thread issues kStageUnroll index loads at a time.
+    constexpr int kStageUnroll = 8;
+    const int ncols_pad = (ncols + kTileKeys - 1) / kTileKeys * kTileKeys;
+    int err = 0;
+    int last = -1;
+    int stage_v[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+        const int c = tid + u * NW * kWave;
+        stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
+    }
     // Q as the B operand of the 16x16x32 product: lane holds head l16, d = 32*kk + 8*q4 + 0..7
     u32x4 qreg[G::kKSteps];
     {
@@ -299,34 +317,33 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int kk = 0; kk < G::kKSteps; ++kk)
             qreg[kk] = head_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
     }
-    const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
-
-    // Stage this split's index columns in LDS, skips and out-of-range rows as -1, padded
-    // to whole tiles; find the last column that names a row (trailing tiles of padding are
-    // never gathered).
-    int err = 0;
-    int last = -1;
-    const int ncols_pad = (ncols + kTileKeys - 1) / kTileKeys * kTileKeys;
-    for (int c = tid; c < ncols_pad; c += NW * kWave) {
-        int row = c < ncols ? idx_row[col_begin + c] : -1;
-        if (row >= p.kv_rows) { err = 1; row = -1; }
-        row = row < 0 ? -1 : row;
-        istage[c] = row;
-        if (row >= 0) last = c;
+    const float sink_raw = head_ok ? p.sink[head] : 0.0f;
+    for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
+        if (c0 > 0) {
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; ++u) {
+                const int c = c0 + tid + u * NW * kWave;
+                stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int c = c0 + tid + u * NW * kWave;
+            int row = stage_v[u];
+            if (row >= p.kv_rows) { err = 1; row = -1; }
+            row = row < 0 ? -1 : row;
+            if (c < ncols_pad) istage[c] = row;
+            if (row >= 0) last = c;
+        }
     }
-    {
-        // workgroup-wide max of `last` through the stage's spare... one LDS word per wave
-        for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
-    }
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
+    if (lane == 0) lastw[wid] = last;
     __syncthreads();
-    {
-        SA_LDS int32_t* lastw = (SA_LDS int32_t*)(tiles);          // scratch before any gather
-        if (lane == 0) lastw[wid] = last;
-        __syncthreads();
-        for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
-        __syncthreads();
-    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
     const int ntiles = (last + kTileKeys) / kTileKeys;        // 0 when nothing is named
+    const float sink2 = sink_raw * kLog2e;
 
     float m_run = sink2;                                       // log2 domain
     float l_run = (q4 == 0 && split == 0) ? 1.0f : 0.0f;       // the sink's exp(0)
@@ -596,7 +613,7 @@ template <int D, bool FP8, int NW>
 static hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
     constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
-    const size_t lds = (size_t)kMaxColsPerSplit * 4 + (size_t)NB * G::kTileBytes +
+    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)NB * G::kTileBytes +
                        (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
     auto k = attn_fwd_kernel<D, FP8, NW>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
