@@ -17,8 +17,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function",
-    # packed f32 vector ops stay off (see the kernels' notes on numerics)
+    # no packed f32 vector instructions (v_pk_*_f32) anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: with AGPR accumulators the compiler copies all of O to
+    # VGPRs on every key tile for the (rarely taken) softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -59,9 +59,27 @@ struct Geo {
 // vmcnt: a skipped row loads row 0 of the sequence instead, and zero_skipped_rows clears it
 // once it has landed (a zero row can never turn a zero probability into a NaN).
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-// raw buffer load of 16 bytes per lane straight into LDS (M0 = lds base, lane i -> +16 i)
-__device__ void raw_buffer_load_lds(i32x4 rsrc, SA_LDS void* lds, int size, int voffset, int soffset,
-                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at lds + 16 i
+// (M0 holds the LDS address). Written as inline assembly on purpose: the compiler's memory
+// model, seeing an LDS write whose completion it cannot order, would otherwise wait for
+// every such load in flight before each LDS read and each barrier, which serialises the
+// tile pipeline. Completion is tracked here with explicit vmcnt waits instead (wait_vmcnt),
+// and the "memory" clobber keeps the compiler from moving LDS accesses across the issue.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// vector-memory loads (__syncthreads would also drain every tile gather in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(SA_LDS const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
 
 // Buffer resource of one sequence's kv rows: base, no stride, `bytes` records (reads past
 // them return zeros), gfx9 default format word.
@@ -75,21 +93,27 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
+// Wave wid issues loads wid*kPer .. wid*kPer+kPer-1 of the tile; load j covers rows
+// j*kRowsPerInst .. +kRowsPerInst-1. All row indices are read before the first load issues.
 template <int D, int NW>
 __device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_t* tidx,
                                                  SA_LDS uint8_t* buf, int wid, int lane) {
     using G = Geo<D>;
     constexpr int kInsts = kTileKeys / G::kRowsPerInst;
     static_assert(kTileKeys % G::kRowsPerInst == 0 && kInsts % NW == 0, "tile split");
+    constexpr int kPer = kInsts / NW;
     const int sub = lane / G::kChunks;          // row within one load
     const int pc = lane % G::kChunks;           // physical chunk this lane fills
+    int rows[kPer];
 #pragma unroll
-    for (int j = 0; j < kInsts / NW; ++j) {
-        const int r0 = (wid + j * NW) * G::kRowsPerInst;   // loads dealt round-robin to waves
+    for (int j = 0; j < kPer; ++j) rows[j] = tidx[(wid * kPer + j) * G::kRowsPerInst + sub];
+    const uint32_t base = lds_addr(buf);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int r0 = (wid * kPer + j) * G::kRowsPerInst;
         const int r = r0 + sub;
-        const int row = max(tidx[r], 0);
-        const int voff = row * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
-        raw_buffer_load_lds(rsrc, (SA_LDS void*)(buf + r0 * G::kRowBytes), 16, voff, 0, 0, 0);
+        const int voff = max(rows[j], 0) * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
     }
 }
 
@@ -98,12 +122,12 @@ template <int D, int NW>
 __device__ __forceinline__ void zero_skipped_rows(SA_LDS const int32_t* tidx, SA_LDS uint8_t* buf,
                                                   int wid, int lane) {
     using G = Geo<D>;
-    constexpr int kInsts = kTileKeys / G::kRowsPerInst;
+    constexpr int kPer = kTileKeys / G::kRowsPerInst / NW;
     const int sub = lane / G::kChunks;
     const int pc = lane % G::kChunks;
 #pragma unroll
-    for (int j = 0; j < kInsts / NW; ++j) {
-        const int r = (wid + j * NW) * G::kRowsPerInst + sub;
+    for (int j = 0; j < kPer; ++j) {
+        const int r = (wid * kPer + j) * G::kRowsPerInst + sub;
         if (tidx[r] < 0) *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
     }
 }
@@ -210,16 +234,8 @@ __device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int 
     return p.rope_cs + (int64_t)pos * p.rope_dim;
 }
 
-__device__ __forceinline__ float sum4groups(float v) {
-    v += __shfl_xor(v, 16, kWave);
-    v += __shfl_xor(v, 32, kWave);
-    return v;
-}
-__device__ __forceinline__ float max4groups(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, kWave));
-    v = fmaxf(v, __shfl_xor(v, 32, kWave));
-    return v;
-}
+__device__ __forceinline__ float sum4groups(float v) { return sum_xor32(sum_xor16(v)); }
+__device__ __forceinline__ float max4groups(float v) { return max_xor32(max_xor16(v)); }
 
 // Pipeline shape of the bf16 path: kBuffers LDS tile buffers, tiles gathered kAhead ahead
 // of the one being multiplied. The only vector-memory operations inside the key loop are
@@ -235,12 +251,12 @@ struct Pipe {
     static constexpr int kWait = (kAhead - 1) * kLoadsPerWave;
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt bits
-// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+// s_waitcnt on the vector-memory counter only; a compiler barrier for memory accesses too,
+// so LDS reads and writes of a landed tile stay behind it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 template <int D, bool FP8, int NW>
@@ -342,8 +358,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
-    const int ntiles = (last + kTileKeys) / kTileKeys;        // 0 when nothing is named
+    // 0 when nothing is named; the same in every lane, kept in a scalar register
+    const int ntiles = __builtin_amdgcn_readfirstlane((last + kTileKeys) / kTileKeys);
     const float sink2 = sink_raw * kLog2e;
+    // Q and the sink have landed before the first tile load issues: the compiler does not
+    // count the tile loads (inline assembly), so its own waits for Q must not meet them.
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
 
     float m_run = sink2;                                       // log2 domain
     float l_run = (q4 == 0 && split == 0) ? 1.0f : 0.0f;       // the sink's exp(0)
@@ -406,12 +427,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             __syncthreads();
             cur = tile(0);
         } else {
-            // tile `it` has landed once only the loads of the kAhead-1 younger tiles remain
-            if (it + kAhead <= ntiles) wait_vmcnt<PP::kWait>();
+            // tile `it` has landed once only the loads of the younger tiles in flight remain
+            // (kAhead-1 of them, fewer at the end)
+            const int younger = ntiles - 1 - it;
+            if (younger >= kAhead - 1) wait_vmcnt<PP::kWait>();
+            else if (kAhead > 2 && younger == 1) wait_vmcnt<PP::kLoadsPerWave>();
             else wait_vmcnt<0>();
             cur = tile(it % NB);
             if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
-            __syncthreads();               // tile visible to all; buffer of tile it-1 free
+            lds_barrier();                 // tile visible to all; buffer of tile it-1 free
             if (it + kAhead < ntiles)
                 gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAhead * kTileKeys, tile((it + kAhead) % NB), wid, lane);
         }

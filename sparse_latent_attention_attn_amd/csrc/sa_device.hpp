@@ -24,21 +24,35 @@ __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cas
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return bits_f32(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return bits_f32(pair & 0xffff0000u); }
 
-// f32 -> bf16, round to nearest, ties to even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = f32_bits(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two f32 -> two bf16 in one word (lo in bits 0..15), round to nearest even: gfx950 has a
+// packed conversion instruction (v_cvt_pk_bf16_f32) for this.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Swap a value with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float xor32(float v) {
-    return __shfl_xor(v, 32, kWave);
+// Cross-lane exchanges without the LDS pipe (gfx950 permlane swaps). With both operands
+// equal, v_permlane32_swap leaves each lane holding its own value and that of lane l ^ 32
+// (one in each result), and v_permlane16_swap does the same for lane l ^ 16.
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(v), f32_bits(v), false, false);
+    return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f32_bits(v), f32_bits(v), false, false);
+    return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(v), f32_bits(v), false, false);
+    return bits_f32(r[0]) + bits_f32(r[1]);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f32_bits(v), f32_bits(v), false, false);
+    return bits_f32(r[0]) + bits_f32(r[1]);
 }
 
 }  // namespace sa
