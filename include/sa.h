@@ -51,8 +51,11 @@ enum {
 
 /* flags */
 enum {
-    SA_FLAG_CHECK_IDX = 1u    /* bounds-check every index on the device: an index >= kv_rows
-                                 is then treated as a skip and sets *err_word to 1 */
+    SA_FLAG_CHECK_IDX = 1u    /* report errors found on the device in *err_word (bits are
+                                 OR-ed in): bit 0 (value 1) an index >= kv_rows, bit 1
+                                 (value 2) a position outside [0, max_pos) with the RoPE
+                                 epilogue on. Without the flag nothing is reported; the
+                                 handling below is the same either way */
 };
 
 typedef struct sa_attn_args {
@@ -76,7 +79,8 @@ typedef struct sa_attn_args {
                                                             of the query's own sequence; any
                                                             negative value skips the column;
                                                             values >= kv_rows are a caller
-                                                            error (see SA_FLAG_CHECK_IDX) */
+                                                            error, skipped like a negative
+                                                            value (see SA_FLAG_CHECK_IDX) */
     float scale;                                         /* softmax_scale, e.g. d^-0.5 */
     void *out;              int64_t out_seq_stride;      /* bf16 [b][s][h][d]; must not alias
                                                             q, kv or idx */
@@ -89,7 +93,9 @@ typedef struct sa_attn_args {
     int32_t rope_dim;
     const float *rope_cos_sin; int32_t max_pos;          /* f32 [max_pos][rope_dim/2][2] */
     const int32_t *pos;     int64_t pos_seq_stride;      /* int32 [b][s] absolute positions,
-                                                            each in [0, max_pos) */
+                                                            each in [0, max_pos); a row at a
+                                                            position outside is left
+                                                            unrotated (a caller error) */
 
     /* split-K workspace (f32 partial results), sized by sa_sparse_attn_workspace; may be
        NULL when that function reports 0 bytes */
