@@ -234,6 +234,21 @@ __device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int 
     return p.rope_cs + (int64_t)pos * p.rope_dim;
 }
 
+// Work item of block b (items are query-major: item = query * per_q + j). Workgroups are
+// dealt to the 8 XCDs round-robin: block b runs on XCD b % 8, as the (b / 8)-th workgroup
+// there. The per_q items of one query (its head blocks and splits, which gather the same
+// rows) go to one XCD back to back, so they share its L2; queries go round-robin over the
+// XCDs, so each XCD gets an equal share of the work even when the work per query grows with
+// the query index (causal prefill); each XCD takes its queries in descending order, so the
+// longest start first. The last nq % 8 queries keep the identity order.
+__device__ __forceinline__ int work_item(int b, int nq, int per_q) {
+    const int q8 = nq / 8;
+    if (b >= q8 * 8 * per_q) return b;
+    const int x = b % 8, k = b / 8;
+    const int r = k / per_q, j = k % per_q;
+    return (8 * (q8 - 1 - r) + x) * per_q + j;
+}
+
 __device__ __forceinline__ float sum4groups(float v) { return sum_xor32(sum_xor16(v)); }
 __device__ __forceinline__ float max4groups(float v) { return max_xor32(max_xor16(v)); }
 
@@ -280,15 +295,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int l16 = lane & 15;                  // this lane's head within the wave
     const int q4 = lane >> 4;                   // lane group 0..3
 
-    // work item: ((query * head_blocks) + head block) * splits + split. Workgroups are
-    // dealt to the 8 XCDs round-robin (block b runs on XCD b % 8); remapping consecutive
-    // items onto one XCD keeps the workgroups of a query, which gather the same rows, in
-    // that XCD's L2.
-    int item = blockIdx.x;
-    {
-        const int n8 = gridDim.x / 8;
-        if (item < 8 * n8) item = (item % 8) * n8 + item / 8;
-    }
+    // work item: ((query * head_blocks) + head block) * splits + split, in the XCD-aware
+    // order of work_item
+    int item = work_item(blockIdx.x, p.b * p.s, p.head_blocks * p.splits);
     const int split = item % p.splits;
     item /= p.splits;
     const int hblk = item % p.head_blocks;
