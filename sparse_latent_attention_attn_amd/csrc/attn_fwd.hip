@@ -363,7 +363,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     }
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
     SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
+    SA_LDS int32_t* redo = lastw + 8;                           // second-pass flag
     if (lane == 0) lastw[wid] = last;
+    if (tid == 0) *redo = 0;
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
@@ -375,8 +377,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
 
-    float m_run = sink2;                                       // log2 domain
-    float l_run = (q4 == 0 && split == 0) ? 1.0f : 0.0f;       // the sink's exp(0)
+    // Softmax reference. Every probability of a pass is exp2(score - m_ref) with one fixed
+    // reference per head, so O is never rescaled inside the key loop: m_ref is taken at the
+    // first tile that names a row (max of the sink and that tile's scores; O is still zero
+    // then), and later scores may exceed it by up to kSlack (probabilities up to 2^kSlack,
+    // well inside f32 and bf16 range). A score beyond that flags the workgroup; the whole key
+    // loop then runs once more with m_ref = the maximum of every score seen (which no score
+    // can exceed), a rare second pass instead of a rescale on every tile.
+    constexpr float kSlack = 32.0f;
+    const bool sink_lane = q4 == 0 && split == 0;             // the sink counts once per head
+    float m_ref = sink2;                                       // log2 domain
+    float m_seen = sink2;                                      // max of the sink and all scores
+    bool have_ref = false;                                     // same in all lanes of a wave
+    float l_run = sink_lane ? 1.0f : 0.0f;                     // exp2(sink2 - m_ref)
     f32x4 o_acc[G::kDBlocks];
 #pragma unroll
     for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -410,8 +423,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
     }
 
-    // prologue: the first kAhead tiles (bf16) or the first tile (fp8)
     constexpr int kAhead = FP8 ? 1 : PP::kAhead;
+    for (int pass = 0;; ++pass) {
+    // prologue: the first kAhead tiles (bf16) or the first tile (fp8)
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
         if (j < ntiles) {
@@ -504,18 +518,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 tmax = fmaxf(tmax, sv);
             }
         tmax = max4groups(tmax);
-        const bool grow = tmax > m_run + 8.0f;
-        if (__ballot(grow) != 0) {
-            const float m_new = grow ? tmax : m_run;
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] *= alpha;
+        m_seen = fmaxf(m_seen, tmax);
+        if (!have_ref) {
+            // first tile with a row (valid != 0, so tmax is finite): O is still zero
+            m_ref = fmaxf(sink2, tmax);
+            l_run = sink_lane ? fast_exp2(sink2 - m_ref) : 0.0f;
+            have_ref = true;
         }
-        // a running max still at -inf (sink -inf, nothing seen yet) means every score of
-        // the tile is -inf as well: exponentiate against 0 so that they give exact zeros
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        if (__ballot(tmax > m_ref + kSlack) != 0 && lane == 0) *redo = 1;
+        const float m_use = m_ref;
         u32x4 pb;                                              // P as the PV B operand
         float psum = 0.0f;
 #pragma unroll
@@ -553,6 +564,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             }
         }
     }
+    // A score ran more than kSlack above its head's reference (rare): run the key loop again
+    // against the maximum of all scores, which every wave has tracked for its heads.
+    __syncthreads();
+    const int again = *redo;
+    if (pass > 0 || again == 0) break;
+    __syncthreads();                                           // every wave has read the flag
+    m_ref = m_seen;
+    have_ref = true;
+    l_run = sink_lane ? fast_exp2(sink2 - m_ref) : 0.0f;
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // a skipped index >= kv_rows is reported once per wave
     if ((p.flags & 1u) && __ballot(err) != 0 && lane == 0) atomicOr(p.err_word, 1);
@@ -587,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 #pragma unroll
         for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db];
         if (q4 == 0) {
-            p.ws_ml[slot * 2 + 0] = m_run;
+            p.ws_ml[slot * 2 + 0] = m_ref;
             p.ws_ml[slot * 2 + 1] = l_tot;
         }
     }

@@ -194,6 +194,50 @@ def test_strided_sequences(sa):
     assert torch.all(outb[:, 2:] == 0)
 
 
+@pytest.mark.parametrize("boost,where,fmt", [
+    (0.0, 70, "bf16"),      # nothing special: scores within a few units of each other
+    (4.0, 70, "bf16"),      # a late key ~45 log2 units above the first tile: second pass
+    (13.0, 70, "bf16"),     # ~150 log2 units above: 2^150 would overflow without it
+    (13.0, 3, "bf16"),      # the large key in the first tile: no second pass
+    (-13.0, 70, "bf16"),    # a very negative late score
+    (4.0, 70, "fp8"),
+])
+def test_late_large_scores(sa, boost, where, fmt):
+    """Scores far above the first tile's maximum (kv row = boost * q of head 0): the
+    softmax stays exact, including the second pass over the keys."""
+    _say("late large", boost, where, fmt)
+    q, kv, sink, idx = W.rand_problem(51, 1, 2, 16, 64, 120, 96, 0.0, False)
+    for t in range(2):
+        row = int(idx[0, t, where])
+        kv[0, row] = (q[0, t, 0].float() * boost).to(torch.bfloat16)
+    scale = 0.125
+    kvd = kv.cuda()
+    kv_scale = None
+    if fmt == "fp8":
+        kvd, kv_scale = sa.quant_kv_fp8(kvd, want=("codes", "scales"))
+        kv_ref = oracle.act_quant(u16(kv).reshape(-1, 64))[0].reshape(kv.shape)
+    else:
+        kv_ref = u16(kv)
+    out = sa.sparse_attn(q.cuda(), kvd, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale)
+    assert torch.isfinite(out.float()).all()
+    ref = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, 16, 64), ref, f"late large {boost} {where} {fmt}")
+
+
+def test_late_large_scores_across_splits(sa):
+    """A decode-shaped problem that the planner splits: the large score sits in a later split."""
+    q, kv, sink, idx = W.rand_problem(52, 2, 1, 64, 512, 1200, 1024, 0.0, False)
+    for b in range(2):
+        row = int(idx[b, 0, 900])
+        kv[b, row] = (q[b, 0, 5].float() * 2.0).to(torch.bfloat16)
+    scale = float(np.float32(512 ** -0.5))
+    args = sa.make_args(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
+    assert sa.sparse_attn_workspace_bytes(args) > 0, "expected a split plan"
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, 64, 512), ref, "late large split")
+
+
 def test_empty_lists_and_no_sink(sa):
     q, kv, sink, idx = W.rand_problem(31, 1, 3, 16, 64, 20, 40, 0.0, False)
     idx[0, 1] = -1
