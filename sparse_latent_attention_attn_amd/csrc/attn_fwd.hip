@@ -274,7 +274,7 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int HPW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     using G = Geo<D>;
     using PP = Pipe<D, NW>;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int tid = threadIdx.x;
     const int wid = tid / kWave;
     const int lane = tid % kWave;
-    const int l16 = lane & 15;                  // this lane's head within the wave
+    const int l16 = lane & 15;                  // this lane's head within a 16-head block
     const int q4 = lane >> 4;                   // lane group 0..3
 
     // work item: ((query * head_blocks) + head block) * splits + split, in the XCD-aware
@@ -305,8 +305,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int seq = qi / p.s;
     const int t = qi % p.s;
 
-    const int head = hblk * NW * kHeadsPerWave + wid * kHeadsPerWave + l16;
-    const bool head_ok = head < p.h;
+    // the wave's HPW blocks of 16 heads: head(hb) = head0 + 16*hb + l16
+    const int head0 = (hblk * NW + wid) * HPW * kHeadsPerWave + l16;
+    auto head_of = [&](int hb) { return head0 + hb * kHeadsPerWave; };
 
     const int32_t* idx_row = p.idx + (int64_t)seq * p.idx_seq_stride + (int64_t)t * p.topk;
     const int col_begin = split * p.cols_per_split;
@@ -334,15 +335,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         const int c = tid + u * NW * kWave;
         stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
     }
-    // Q as the B operand of the 16x16x32 product: lane holds head l16, d = 32*kk + 8*q4 + 0..7
-    u32x4 qreg[G::kKSteps];
-    {
-        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + head) * D;
+    // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
+    // d = 32*kk + 8*q4 + 0..7
+    u32x4 qreg[HPW][G::kKSteps];
+    float sink_raw[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+        const bool ok = head_of(hb) < p.h;
+        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
 #pragma unroll
         for (int kk = 0; kk < G::kKSteps; ++kk)
-            qreg[kk] = head_ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
+            qreg[hb][kk] = ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
+        sink_raw[hb] = ok ? p.sink[head_of(hb)] : 0.0f;
     }
-    const float sink_raw = head_ok ? p.sink[head] : 0.0f;
     for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
         if (c0 > 0) {
 #pragma unroll
@@ -371,7 +376,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
     // 0 when nothing is named; the same in every lane, kept in a scalar register
     const int ntiles = __builtin_amdgcn_readfirstlane((last + kTileKeys) / kTileKeys);
-    const float sink2 = sink_raw * kLog2e;
+    float sink2[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) sink2[hb] = sink_raw[hb] * kLog2e;
     // Q and the sink have landed before the first tile load issues: the compiler does not
     // count the tile loads (inline assembly), so its own waits for Q must not meet them.
     __builtin_amdgcn_s_waitcnt(0);
@@ -386,13 +393,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // can exceed), a rare second pass instead of a rescale on every tile.
     constexpr float kSlack = 32.0f;
     const bool sink_lane = q4 == 0 && split == 0;             // the sink counts once per head
-    float m_ref = sink2;                                       // log2 domain
-    float m_seen = sink2;                                      // max of the sink and all scores
-    bool have_ref = false;                                     // same in all lanes of a wave
-    float l_run = sink_lane ? 1.0f : 0.0f;                     // exp2(sink2 - m_ref)
-    f32x4 o_acc[G::kDBlocks];
+    float m_ref[HPW], m_seen[HPW], l_run[HPW];                 // log2 domain, per head
 #pragma unroll
-    for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < HPW; ++hb) {
+        m_ref[hb] = sink2[hb];
+        m_seen[hb] = sink2[hb];                                // max of the sink and all scores
+        l_run[hb] = sink_lane ? 1.0f : 0.0f;                   // exp2(sink2 - m_ref)
+    }
+    bool have_ref = false;                                     // same in all lanes of a wave
+    f32x4 o_acc[G::kDBlocks][HPW];
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) o_acc[b][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Per-lane LDS byte offsets of the two operand reads (the swizzle only touches the low
     // four bits of a chunk index, so each read is one of these plus a multiple of 256 B):
@@ -478,7 +491,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         // ---- S^T = K . Q^T over the tile's two 16-key blocks. K operands are read
         //      kPre steps ahead of their multiply; scheduling fences keep the compiler from
         //      hoisting every read of the unrolled loop.
-        f32x4 s_acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        f32x4 s_acc[2][HPW];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
             u32x4 a0[kPre], a1[kPre];
@@ -495,55 +512,66 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     a0[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[0][nk & 3] + 256 * (nk >> 2));
                     a1[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[1][nk & 3] + 256 * (nk >> 2));
                 }
-                const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[kk]);
-                s_acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0], 0, 0, 0);
-                s_acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1], 0, 0, 0);
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb) {
+                    const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
+                    s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0][hb], 0, 0, 0);
+                    s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1][hb], 0, 0, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        // ---- online softmax (log2 domain); this lane: head l16, keys 16*mb + 4*q4 + r.
-        //      The running max is only moved when the tile max exceeds it by more than 8
-        //      (a factor 256): until then the stale max keeps every exp2 below 256 and the
-        //      result is the same softmax (the common factor cancels in O / l), so the O
-        //      rescale is rare.
+        // ---- softmax (log2 domain) against the fixed reference; this lane: head l16 of
+        //      each block, keys 16*mb + 4*q4 + r
         const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
-        float tmax = -INFINITY;
+        float tmax[HPW];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int hb = 0; hb < HPW; ++hb) {
+            float tm = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sv = ((lm >> (16 * mb + r)) & 1u) ? s_acc[mb][r] * p.scale_log2 : -INFINITY;
-                s_acc[mb][r] = sv;
-                tmax = fmaxf(tmax, sv);
-            }
-        tmax = max4groups(tmax);
-        m_seen = fmaxf(m_seen, tmax);
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = ((lm >> (16 * mb + r)) & 1u) ? s_acc[mb][hb][r] * p.scale_log2 : -INFINITY;
+                    s_acc[mb][hb][r] = sv;
+                    tm = fmaxf(tm, sv);
+                }
+            tmax[hb] = max4groups(tm);
+            m_seen[hb] = fmaxf(m_seen[hb], tmax[hb]);
+        }
         if (!have_ref) {
             // first tile with a row (valid != 0, so tmax is finite): O is still zero
-            m_ref = fmaxf(sink2, tmax);
-            l_run = sink_lane ? fast_exp2(sink2 - m_ref) : 0.0f;
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) {
+                m_ref[hb] = fmaxf(sink2[hb], tmax[hb]);
+                l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
+            }
             have_ref = true;
         }
-        if (__ballot(tmax > m_ref + kSlack) != 0 && lane == 0) *redo = 1;
-        const float m_use = m_ref;
-        u32x4 pb;                                              // P as the PV B operand
-        float psum = 0.0f;
+        bool over = false;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const float p0 = fast_exp2(s_acc[mb][0] - m_use), p1 = fast_exp2(s_acc[mb][1] - m_use);
-            const float p2 = fast_exp2(s_acc[mb][2] - m_use), p3 = fast_exp2(s_acc[mb][3] - m_use);
-            psum += (p0 + p1) + (p2 + p3);
-            pb[2 * mb] = pack_bf16x2(p0, p1);
-            pb[2 * mb + 1] = pack_bf16x2(p2, p3);
+        for (int hb = 0; hb < HPW; ++hb) over |= tmax[hb] > m_ref[hb] + kSlack;
+        if (__ballot(over) != 0 && lane == 0) *redo = 1;
+        u32x4 pb[HPW];                                         // P as the PV B operands
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            float psum = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const float p0 = fast_exp2(s_acc[mb][hb][0] - m_ref[hb]), p1 = fast_exp2(s_acc[mb][hb][1] - m_ref[hb]);
+                const float p2 = fast_exp2(s_acc[mb][hb][2] - m_ref[hb]), p3 = fast_exp2(s_acc[mb][hb][3] - m_ref[hb]);
+                psum += (p0 + p1) + (p2 + p3);
+                pb[hb][2 * mb] = pack_bf16x2(p0, p1);
+                pb[hb][2 * mb + 1] = pack_bf16x2(p2, p3);
+            }
+            l_run[hb] += psum;
         }
-        l_run += psum;
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time;
         //      V operands read kPre slices ahead
         {
-            const bf16x8 pk = __builtin_bit_cast(bf16x8, pb);
             constexpr int kPre = 2;
             bf16x4v va[kPre], vb[kPre];
 #pragma unroll
@@ -559,7 +587,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     va[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[0][nb & 7] + 256 * (nb >> 3)));
                     vb[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[1][nb & 7] + 256 * (nb >> 3)));
                 }
-                o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pk, o_acc[db], 0, 0, 0);
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb)
+                    o_acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[hb]), o_acc[db][hb], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -570,19 +600,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int again = *redo;
     if (pass > 0 || again == 0) break;
     __syncthreads();                                           // every wave has read the flag
-    m_ref = m_seen;
-    have_ref = true;
-    l_run = sink_lane ? fast_exp2(sink2 - m_ref) : 0.0f;
 #pragma unroll
-    for (int b = 0; b < G::kDBlocks; ++b) o_acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < HPW; ++hb) {
+        m_ref[hb] = m_seen[hb];
+        l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
+    }
+    have_ref = true;
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) o_acc[b][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // a skipped index >= kv_rows is reported once per wave
     if ((p.flags & 1u) && __ballot(err) != 0 && lane == 0) atomicOr(p.err_word, 1);
 
-    // ---- finish: the four lane groups share m_run; their partial sums add up
-    const float l_tot = sum4groups(l_run);
-    // O^T accumulator layout: lane holds head l16, d = 16*db + 4*q4 + (0..3)
+    // ---- finish: the four lane groups share m_ref; their partial sums add up
+    float l_tot[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
+    // O^T accumulator layout: lane holds head head_of(hb), d = 16*db + 4*q4 + (0..3)
     if (p.splits == 1) {
         // the position's (cos, sin) row, staged once in LDS for all heads of the query (the
         // index stage is free now), so the stores below never wait on table loads
@@ -592,26 +629,32 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         if (cs_g != nullptr)
             for (int i = tid; i < p.rope_dim; i += NW * kWave) cs[i] = cs_g[i];
         __syncthreads();
-        if (!head_ok) return;
-        const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         const int r0 = D - p.rope_dim;
-        uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head) * D;
 #pragma unroll
-        for (int db = 0; db < G::kDBlocks; ++db) {
-            const int d0 = 16 * db + 4 * q4;
-            const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
-            *(u32x2*)(orow + d0) = epilogue4(o_acc[db][0], o_acc[db][1], o_acc[db][2], o_acc[db][3],
-                                             inv_l, rot, d0, r0, (SA_LDS const float*)cs);
+        for (int hb = 0; hb < HPW; ++hb) {
+            if (head_of(hb) >= p.h) continue;
+            const float inv_l = l_tot[hb] > 0.0f ? 1.0f / l_tot[hb] : 0.0f;
+            uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                const int d0 = 16 * db + 4 * q4;
+                const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
+                *(u32x2*)(orow + d0) = epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2],
+                                                 o_acc[db][hb][3], inv_l, rot, d0, r0, (SA_LDS const float*)cs);
+            }
         }
     } else {
-        if (!head_ok) return;
-        const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head;
-        float* wo = p.ws_o + slot * D;
 #pragma unroll
-        for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db];
-        if (q4 == 0) {
-            p.ws_ml[slot * 2 + 0] = m_ref;
-            p.ws_ml[slot * 2 + 1] = l_tot;
+        for (int hb = 0; hb < HPW; ++hb) {
+            if (head_of(hb) >= p.h) continue;
+            const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head_of(hb);
+            float* wo = p.ws_o + slot * D;
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db][hb];
+            if (q4 == 0) {
+                p.ws_ml[slot * 2 + 0] = m_ref[hb];
+                p.ws_ml[slot * 2 + 1] = l_tot[hb];
+            }
         }
     }
 }
@@ -665,13 +708,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int HPW = 1>
 static hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
     constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
     const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)NB * G::kTileBytes +
                        (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
-    auto k = attn_fwd_kernel<D, FP8, NW>;
+    auto k = attn_fwd_kernel<D, FP8, NW, HPW>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(NW * kWave), lds, st, p);
@@ -679,28 +722,32 @@ static hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
 }
 
 template <int D, bool FP8>
-static hipError_t launch_fwd_nw(const KParams& p, int nw, int blocks, hipStream_t st) {
+static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int blocks, hipStream_t st) {
+    if constexpr (D == 512 && !FP8) {
+        if (hpw == 2) return nw == 4 ? launch_fwd<D, FP8, 4, 2>(p, blocks, st) : hipErrorInvalidValue;
+    }
+    if (hpw != 1) return hipErrorInvalidValue;
     if (nw == 1) return launch_fwd<D, FP8, 1>(p, blocks, st);
     if (nw == 2) return launch_fwd<D, FP8, 2>(p, blocks, st);
     return launch_fwd<D, FP8, 4>(p, blocks, st);
 }
 
 template <int D>
-static hipError_t launch_all(const KParams& p, bool fp8, int nw, int blocks, hipStream_t st) {
-    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, blocks, st) : launch_fwd_nw<D, false>(p, nw, blocks, st);
+static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int blocks, hipStream_t st) {
+    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, blocks, st) : launch_fwd_nw<D, false>(p, nw, hpw, blocks, st);
     if (e != hipSuccess || p.splits == 1) return e;
     const int waves = p.b * p.s * p.h;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((waves + 3) / 4), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, hipStream_t st) {
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, hipStream_t st) {
     const int blocks = p.b * p.s * p.head_blocks * p.splits;
     switch (p.d) {
-        case 64: return launch_all<64>(p, fp8, nw, blocks, st);
-        case 128: return launch_all<128>(p, fp8, nw, blocks, st);
-        case 256: return launch_all<256>(p, fp8, nw, blocks, st);
-        case 512: return launch_all<512>(p, fp8, nw, blocks, st);
+        case 64: return launch_all<64>(p, fp8, nw, hpw, blocks, st);
+        case 128: return launch_all<128>(p, fp8, nw, hpw, blocks, st);
+        case 256: return launch_all<256>(p, fp8, nw, hpw, blocks, st);
+        case 512: return launch_all<512>(p, fp8, nw, hpw, blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

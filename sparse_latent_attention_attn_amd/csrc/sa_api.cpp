@@ -95,8 +95,14 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // and a workgroup of several waves keeps more loads in flight than a lone wave (which
     // measured 2-3x slower per byte). Occupancy for short batches comes from splits.
     pl.nw = max_nw == 3 ? 2 : max_nw;
-    pl.head_blocks = blocks_for(pl.nw);
-    pl.h_pad = pl.head_blocks * pl.nw * kHeadsPerWave;
+    // Two head blocks per wave (one gathered operand feeds two MFMAs) when there are enough
+    // workgroups without splitting: bf16 rows of 512, 128 heads or more.
+    pl.hpw = 1;
+    if (a->kv_format == SA_KV_BF16 && a->d == 512 && pl.nw == 4 && a->h >= 8 * kHeadsPerWave &&
+        nq * blocks_for(8) >= cus)
+        pl.hpw = 2;
+    pl.head_blocks = blocks_for(pl.nw * pl.hpw);
+    pl.h_pad = pl.head_blocks * pl.nw * pl.hpw * kHeadsPerWave;
     const int ntiles = (a->topk + kTileKeys - 1) / kTileKeys;
     const int64_t wgs = nq * pl.head_blocks;
     int splits = 1;
@@ -172,7 +178,7 @@ SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
         p.ws_ml = p.ws_o + slots * a->d;
     }
     p.flags = a->flags; p.err_word = a->err_word;
-    const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, (hipStream_t)stream);
+    const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, pl.hpw, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -9,7 +9,7 @@ namespace sa {
 
 // Tiling shared by the planner (sa_api.cpp) and the kernels (attn_fwd.hip).
 constexpr int kTileKeys = 32;       // index columns per key tile
-constexpr int kHeadsPerWave = 16;   // heads one wave owns
+constexpr int kHeadsPerWave = 16;   // heads in one block (the N of a 16x16 MFMA tile)
 constexpr int kMaxWaves = 4;        // waves per workgroup
 constexpr int kMaxColsPerSplit = 4096;  // index columns one workgroup stages in LDS
 
@@ -35,7 +35,8 @@ struct KParams {
 
 // Split plan shared by sa_sparse_attn and sa_sparse_attn_workspace.
 struct Plan {
-    int nw;             // waves per workgroup (32 heads each)
+    int nw;             // waves per workgroup
+    int hpw;            // blocks of 16 heads per wave (1, or 2 for wide bf16 d = 512 work)
     int head_blocks;
     int h_pad;
     int splits;
@@ -43,7 +44,7 @@ struct Plan {
     size_t ws_bytes;
 };
 
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, hipStream_t st);
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, hipStream_t st);
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
                               hipStream_t st);

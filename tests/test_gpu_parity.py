@@ -177,6 +177,24 @@ def test_random_problems(sa, seed, b, s, h, d, rows, topk, hole, dup):
     assert_close(u16(out).reshape(-1, h, d), ref, f"random {seed}")
 
 
+@pytest.mark.parametrize("seed,b,s,h,rows,topk,hole", [
+    (61, 1, 300, 128, 200, 70, 0.1),     # 300 workgroups of 128 heads: two head blocks per wave
+    (62, 2, 140, 160, 100, 40, 0.3),     # 160 heads: the second workgroup's last 96 heads are padding
+])
+def test_wide_waves(sa, seed, b, s, h, rows, topk, hole):
+    """Enough queries at d = 512 and >= 128 heads for the plan with two blocks of 16 heads
+    per wave (one gathered K or V operand feeds two MFMAs)."""
+    _say("wide", seed, b, s, h, rows, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, 512, rows, topk, hole, False)
+    scale = float(np.float32(512 ** -0.5))
+    # a late key far above the rest for a few queries: the second key pass on this plan too
+    for t in range(0, s, 37):
+        kv[0, int(idx[0, t, topk - 1]) if idx[0, t, topk - 1] >= 0 else 0] = (q[0, t, 3].float() * 2).to(torch.bfloat16)
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, 512), ref, f"wide {seed}")
+
+
 def test_strided_sequences(sa):
     """Per-sequence blocks inside larger buffers (non-packed sequence strides)."""
     q, kv, sink, idx = W.rand_problem(21, 3, 2, 32, 128, 50, 40, 0.1, False)
