@@ -207,7 +207,7 @@ def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0):
 
 # ------------------------------------------------------------------ HBM traffic counters
 CAL_BYTES = 1 << 30              # calibration copy: 1 GiB read, 1 GiB written
-KERNEL_SOURCES = ["attn_fwd.hip", "sa_api.cpp", "sa_internal.hpp", "sa_device.hpp"]
+KERNEL_SOURCES = ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "sa_api.cpp", "sa_internal.hpp", "sa_device.hpp"]
 
 
 def kernel_source_hash() -> str:

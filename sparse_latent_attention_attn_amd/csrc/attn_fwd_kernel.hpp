@@ -1,0 +1,666 @@
+// sparse_attn for gfx950: one workgroup per (query, block of heads, split of the index
+// columns). The operation follows the attention API docs ("sparse_attn", precision
+// paragraph) and the call in Attention.forward: per query and head, a softmax in f32 over
+// the gathered latent rows plus the sink (denominator only), bf16 output.
+//
+// Work inside a workgroup of NW waves (NW = 1, 2 or 4), 16 heads per wave:
+//   * key tiles of 32 index columns are gathered row by row from HBM straight into LDS
+//     (global_load_lds_dwordx4, 16 B per lane), double-buffered, so the gather of tile t+1
+//     overlaps the matrix work on tile t. All waves of the workgroup read the same tile:
+//     one gather serves 16*NW heads of the query. Rows carry a 16-byte-chunk XOR swizzle so
+//     that both LDS read patterns below avoid bank conflicts.
+//   * scores are computed transposed, S^T[key][head] = K . Q^T, on v_mfma_f32_16x16x32_bf16:
+//     K comes from LDS as the A operand, Q stays in registers as the B operand. In the
+//     accumulator layout each lane holds one head and 4 keys per 16-key block, so the
+//     online softmax needs in-lane work plus two exchanges across the 4 lane groups.
+//   * the probabilities are rounded to bf16 in registers and are already the B operand of
+//     O^T[d][head] += V^T . P^T (a 32-key step); V^T is read from the same LDS tile with the
+//     transposing ds_read_b64_tr_b16, so the tile is stored once and is both K and V.
+//   * O^T stays in accumulator registers (4 f32 per lane per 16-wide slice of d); each lane
+//     holds a single head, so the softmax rescale is a per-lane scalar multiply.
+//   * the running max starts at the sink logit and the running sum at exp(0) = 1 (counted
+//     in one lane group only and in split 0 only), which puts the sink in the denominator.
+//   * with more than one split, unnormalised partials (O, m, l) go to the workspace and a
+//     small combine kernel merges them; otherwise the epilogue (divide, bf16, optional
+//     inverse RoPE) runs here.
+// At d = 512 a wave keeps Q (64 VGPRs) and O (128 accumulators) resident for the whole key
+// loop; 16 heads per wave is what fits beside them without spilling.
+#pragma once
+
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte chunk swizzle of LDS row r. Both operand reads must hit distinct banks:
+//   K operand: 16 consecutive rows at one chunk -> swz must be a bijection on r mod 16;
+//   V operand: a transposing read covers 8 consecutive rows x 2 adjacent chunks (c, c^1)
+//   -> swz(r) >> 1 must differ across every 8 aligned consecutive rows.
+// ((r & 7) << 1) | ((r >> 3) & 1) does both; it only changes the low four bits of a chunk
+// index (for rows narrower than 16 chunks it is cut down to the row).
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+    return (((r & 7) << 1) | ((r >> 3) & 1)) & (CH - 1);
+}
+
+template <int D>
+struct Geo {
+    static constexpr int kRowBytes = D * 2;                 // one bf16 row in LDS
+    static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+    static constexpr int kRowsPerInst = 64 / kChunks;       // rows one wave load covers
+    static constexpr int kKSteps = D / 32;                  // QK k-steps (32 d each)
+    static constexpr int kDBlocks = D / 16;                 // 16-wide slices of d for PV
+    static constexpr int kTileBytes = kTileKeys * kRowBytes;
+};
+
+// Direct-to-LDS gather of one key tile (bf16 storage). The tile's row indices are read
+// from the index stage in LDS (-1 = skip). Every wave issues exactly kInsts/NW loads per
+// tile, whatever the indices, so that waiting for the oldest tile in flight is an exact
+// vmcnt: a skipped row loads row 0 of the sequence instead, and zero_skipped_rows clears it
+// once it has landed (a zero row can never turn a zero probability into a NaN).
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at lds + 16 i
+// (M0 holds the LDS address). Written as inline assembly on purpose: the compiler's memory
+// model, seeing an LDS write whose completion it cannot order, would otherwise wait for
+// every such load in flight before each LDS read and each barrier, which serialises the
+// tile pipeline. Completion is tracked here with explicit vmcnt waits instead (wait_vmcnt),
+// and the "memory" clobber keeps the compiler from moving LDS accesses across the issue.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// vector-memory loads (__syncthreads would also drain every tile gather in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(SA_LDS const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// Buffer resource of one sequence's kv rows: base, no stride, `bytes` records (reads past
+// them return zeros), gfx9 default format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)(a >> 32) & 0xffff;
+    r[2] = (int32_t)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Wave wid issues loads wid*kPer .. wid*kPer+kPer-1 of the tile; load j covers rows
+// j*kRowsPerInst .. +kRowsPerInst-1. All row indices are read before the first load issues.
+template <int D, int NW>
+__device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_t* tidx,
+                                                 SA_LDS uint8_t* buf, int wid, int lane) {
+    using G = Geo<D>;
+    constexpr int kInsts = kTileKeys / G::kRowsPerInst;
+    static_assert(kTileKeys % G::kRowsPerInst == 0 && kInsts % NW == 0, "tile split");
+    constexpr int kPer = kInsts / NW;
+    const int sub = lane / G::kChunks;          // row within one load
+    const int pc = lane % G::kChunks;           // physical chunk this lane fills
+    int rows[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) rows[j] = tidx[(wid * kPer + j) * G::kRowsPerInst + sub];
+    const uint32_t base = lds_addr(buf);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int r0 = (wid * kPer + j) * G::kRowsPerInst;
+        const int r = r0 + sub;
+        const int voff = max(rows[j], 0) * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
+    }
+}
+
+// Zero the rows of a landed tile whose column is a skip (only the rows this wave loaded).
+template <int D, int NW>
+__device__ __forceinline__ void zero_skipped_rows(SA_LDS const int32_t* tidx, SA_LDS uint8_t* buf,
+                                                  int wid, int lane) {
+    using G = Geo<D>;
+    constexpr int kPer = kTileKeys / G::kRowsPerInst / NW;
+    const int sub = lane / G::kChunks;
+    const int pc = lane % G::kChunks;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int r = (wid * kPer + j) * G::kRowsPerInst + sub;
+        if (tidx[r] < 0) *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
+    }
+}
+
+// fp8 storage: the gather of e4m3 codes (D bytes per row) and the row's D/32 scale bytes
+// into a raw staging tile (zeros for skipped rows), converted to the bf16 tile by
+// convert_tile_fp8.
+template <int D, int NW>
+__device__ __forceinline__ void gather_tile_fp8(const uint8_t* kv_seq, const uint8_t* sc_seq,
+                                                SA_LDS const int32_t* tidx, SA_LDS uint8_t* raw,
+                                                SA_LDS uint8_t* raw_sc, int wid, int lane) {
+    constexpr int kCodeChunks = D / 16;                    // 16-byte chunks of codes per row
+    constexpr int kRowsPerInst = 64 / kCodeChunks;
+    constexpr int kInsts = kTileKeys / kRowsPerInst;
+    static_assert(kTileKeys % kRowsPerInst == 0, "tile split");
+    const int sub = lane / kCodeChunks;
+    const int pc = lane % kCodeChunks;
+#pragma unroll
+    for (int j = 0; j < (kInsts + NW - 1) / NW; ++j) {
+        const int i = wid + j * NW;
+        if (i >= kInsts) break;
+        const int r0 = i * kRowsPerInst;
+        const int r = r0 + sub;
+        const int row = tidx[r];
+        if (row >= 0) {
+            const uint8_t* src = kv_seq + (int64_t)row * D + pc * 16;
+            __builtin_amdgcn_global_load_lds((const void*)src, (SA_LDS void*)(raw + r0 * D), 16, 0, 0);
+        } else {
+            *(SA_LDS u32x4*)(raw + r * D + pc * 16) = u32x4{0, 0, 0, 0};
+        }
+    }
+    constexpr int kSc = D / 32;
+    if (wid == 0 && lane < kTileKeys) {
+        const int row = tidx[lane];
+        for (int j = 0; j < kSc; ++j)
+            raw_sc[lane * kSc + j] = row >= 0 ? sc_seq[(int64_t)row * kSc + j] : (uint8_t)0;
+    }
+}
+
+// e4m3fn code -> f32 (exact): placing the 7 magnitude bits at f32 bits 20..26 gives the
+// code's value times 2^-120 for normal and subnormal codes alike.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    return bits_f32(((c & 0x80u) << 24) | ((c & 0x7fu) << 20)) * 0x1p120f;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void convert_tile_fp8(SA_LDS const uint8_t* raw, SA_LDS const uint8_t* raw_sc,
+                                                 SA_LDS uint8_t* buf, int tid) {
+    using G = Geo<D>;
+    constexpr int kUnits = kTileKeys * D / 8;              // 8 codes -> one 16-byte bf16 chunk
+    for (int u = tid; u < kUnits; u += NW * kWave) {
+        const int r = u / (D / 8);
+        const int c8 = u % (D / 8);                         // logical 16-byte chunk of the row
+        const u32x2 codes = *(SA_LDS const u32x2*)(raw + r * D + c8 * 8);
+        const float s = bits_f32((uint32_t)raw_sc[r * (D / 32) + (c8 * 8) / 32] << 23);
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w = codes[k >> 1] >> ((k & 1) * 16);
+            // the product of an e4m3 value and a power of two has at most 4 significant
+            // bits, so dropping the low half of the f32 is the exact bf16 value
+            const uint32_t lo = f32_bits(e4m3_to_f32(w & 0xffu) * s) >> 16;
+            const uint32_t hi = f32_bits(e4m3_to_f32((w >> 8) & 0xffu) * s) >> 16;
+            o[k] = lo | (hi << 16);
+        }
+        const int pcn = c8 ^ swz<G::kChunks>(r);
+        *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pcn * 16) = o;
+    }
+}
+
+// Epilogue for 4 consecutive output elements d0..d0+3 of one head: o = acc * inv_l rounded
+// to bf16; with `rot`, the inverse rotation of the pairs that fall in the last rope_dim
+// elements (apply_rotary_emb with inverse=True: multiply by the conjugate in f32, back to
+// bf16). A pair outside the rope tail is rotated by (1, 0), which returns it unchanged.
+// `cs` is the position's row of the (cos, sin) table. Returns two packed bf16 pairs.
+template <typename CsPtr>
+__device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a3, float inv_l,
+                                           bool rot, int d0, int r0, CsPtr cs) {
+    uint32_t w[2] = {pack_bf16x2(a0 * inv_l, a1 * inv_l), pack_bf16x2(a2 * inv_l, a3 * inv_l)};
+    if (rot) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int dk = d0 + 2 * k;
+            const bool in = dk >= r0;
+            const int o = in ? (dk - r0) : 0;
+            const float c = in ? cs[o] : 1.0f, sn = in ? cs[o + 1] : 0.0f;
+            const float x = bf16_lo(w[k]), y = bf16_hi(w[k]);
+            w[k] = pack_bf16x2(x * c + y * sn, y * c - x * sn);
+        }
+    }
+    return u32x2{w[0], w[1]};
+}
+
+// Position of query t of sequence seq and its (cos, sin) row, or nullptr when the epilogue
+// is off or the position has no row in the table (then no rotation is applied; bit 2 of
+// the error word records it when checking is on).
+__device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int t, bool report) {
+    if (p.rope_dim == 0) return nullptr;
+    const int pos = p.pos[(int64_t)seq * p.pos_seq_stride + t];
+    if (pos < 0 || pos >= p.max_pos) {
+        if (report && (p.flags & 1u)) atomicOr(p.err_word, 2);
+        return nullptr;
+    }
+    return p.rope_cs + (int64_t)pos * p.rope_dim;
+}
+
+// Work item of block b (items are query-major: item = query * per_q + j). Workgroups are
+// dealt to the 8 XCDs round-robin: block b runs on XCD b % 8, as the (b / 8)-th workgroup
+// there. The per_q items of one query (its head blocks and splits, which gather the same
+// rows) go to one XCD back to back, so they share its L2; queries go round-robin over the
+// XCDs, so each XCD gets an equal share of the work even when the work per query grows with
+// the query index (causal prefill); each XCD takes its queries in descending order, so the
+// longest start first. The last nq % 8 queries keep the identity order.
+__device__ __forceinline__ int work_item(int b, int nq, int per_q) {
+    const int q8 = nq / 8;
+    if (b >= q8 * 8 * per_q) return b;
+    const int x = b % 8, k = b / 8;
+    const int r = k / per_q, j = k % per_q;
+    return (8 * (q8 - 1 - r) + x) * per_q + j;
+}
+
+__device__ __forceinline__ float sum4groups(float v) { return sum_xor32(sum_xor16(v)); }
+__device__ __forceinline__ float max4groups(float v) { return max_xor32(max_xor16(v)); }
+
+// Pipeline shape of the bf16 path: kBuffers LDS tile buffers, tiles gathered kAhead ahead
+// of the one being multiplied. The only vector-memory operations inside the key loop are
+// the tile loads (kLoadsPerWave per wave per tile), so when tile t is needed the loads
+// issued after it are exactly those of tiles t+1 .. t+kAhead-1: the wait is vmcnt(kWait),
+// which must fit the 6-bit counter.
+template <int D, int NW>
+struct Pipe {
+    static constexpr int kLoadsPerWave = kTileKeys / Geo<D>::kRowsPerInst / NW;
+    static constexpr int kBuffers = 4;
+    static constexpr int kAheadMax = 1 + 63 / kLoadsPerWave;
+    static constexpr int kAhead = kBuffers - 1 < kAheadMax ? kBuffers - 1 : kAheadMax;
+    static constexpr int kWait = (kAhead - 1) * kLoadsPerWave;
+};
+
+// s_waitcnt on the vector-memory counter only; a compiler barrier for memory accesses too,
+// so LDS reads and writes of a landed tile stay behind it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int D, bool FP8, int NW, int HPW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
+    using G = Geo<D>;
+    using PP = Pipe<D, NW>;
+    constexpr int NB = FP8 ? 1 : PP::kBuffers;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
+    // LDS: the index stage (kMaxColsPerSplit int32), then NB bf16 tiles; fp8 adds two raw
+    // staging tiles of codes and two of scale bytes.
+    SA_LDS int32_t* istage = (SA_LDS int32_t*)smem;
+    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4 + 64;
+    auto tile = [&](int i) { return tiles + i * G::kTileBytes; };
+    auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
+    auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
+
+    const int tid = threadIdx.x;
+    const int wid = tid / kWave;
+    const int lane = tid % kWave;
+    const int l16 = lane & 15;                  // this lane's head within a 16-head block
+    const int q4 = lane >> 4;                   // lane group 0..3
+
+    // work item: ((query * head_blocks) + head block) * splits + split, in the XCD-aware
+    // order of work_item
+    int item = work_item(blockIdx.x, p.b * p.s, p.head_blocks * p.splits);
+    const int split = item % p.splits;
+    item /= p.splits;
+    const int hblk = item % p.head_blocks;
+    const int qi = item / p.head_blocks;
+    const int seq = qi / p.s;
+    const int t = qi % p.s;
+
+    // the wave's HPW blocks of 16 heads: head(hb) = head0 + 16*hb + l16
+    const int head0 = (hblk * NW + wid) * HPW * kHeadsPerWave + l16;
+    auto head_of = [&](int hb) { return head0 + hb * kHeadsPerWave; };
+
+    const int32_t* idx_row = p.idx + (int64_t)seq * p.idx_seq_stride + (int64_t)t * p.topk;
+    const int col_begin = split * p.cols_per_split;
+    const int ncols = max(0, min(p.topk, col_begin + p.cols_per_split) - col_begin);
+
+    const uint8_t* kv_seq = p.kv + (int64_t)seq * p.kv_seq_stride_bytes;
+    const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
+    const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
+
+    // ---- start-up, arranged so that its memory latencies overlap: the index loads go out
+    // first, then Q and the sink; the index stage is written as soon as the index loads
+    // land (Q may still be in flight), the first key tiles are issued, and only then does
+    // anything wait for Q.
+    //
+    // Stage this split's index columns in LDS, skips and out-of-range rows as -1, padded
+    // to whole tiles, and find the last column that names a row (trailing tiles of padding
+    // are never gathered). Each thread issues kStageUnroll index loads at a time.
+    constexpr int kStageUnroll = 16;
+    const int ncols_pad = (ncols + kTileKeys - 1) / kTileKeys * kTileKeys;
+    int err = 0;
+    int last = -1;
+    int stage_v[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+        const int c = tid + u * NW * kWave;
+        stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
+    }
+    // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
+    // d = 32*kk + 8*q4 + 0..7
+    u32x4 qreg[HPW][G::kKSteps];
+    float sink_raw[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+        const bool ok = head_of(hb) < p.h;
+        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
+#pragma unroll
+        for (int kk = 0; kk < G::kKSteps; ++kk)
+            qreg[hb][kk] = ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
+        sink_raw[hb] = ok ? p.sink[head_of(hb)] : 0.0f;
+    }
+    for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
+        if (c0 > 0) {
+#pragma unroll
+            for (int u = 0; u < kStageUnroll; ++u) {
+                const int c = c0 + tid + u * NW * kWave;
+                stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStageUnroll; ++u) {
+            const int c = c0 + tid + u * NW * kWave;
+            int row = stage_v[u];
+            if (row >= p.kv_rows) { err = 1; row = -1; }
+            row = row < 0 ? -1 : row;
+            if (c < ncols_pad) istage[c] = row;
+            if (row >= 0) last = c;
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
+    SA_LDS int32_t* redo = lastw + 8;                           // second-pass flag
+    if (lane == 0) lastw[wid] = last;
+    if (tid == 0) *redo = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) last = max(last, lastw[w]);
+    // 0 when nothing is named; the same in every lane, kept in a scalar register
+    const int ntiles = __builtin_amdgcn_readfirstlane((last + kTileKeys) / kTileKeys);
+    float sink2[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) sink2[hb] = sink_raw[hb] * kLog2e;
+    // Q and the sink have landed before the first tile load issues: the compiler does not
+    // count the tile loads (inline assembly), so its own waits for Q must not meet them.
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+
+    // Softmax reference. Every probability of a pass is exp2(score - m_ref) with one fixed
+    // reference per head, so O is never rescaled inside the key loop: m_ref is taken at the
+    // first tile that names a row (max of the sink and that tile's scores; O is still zero
+    // then), and later scores may exceed it by up to kSlack (probabilities up to 2^kSlack,
+    // well inside f32 and bf16 range). A score beyond that flags the workgroup; the whole key
+    // loop then runs once more with m_ref = the maximum of every score seen (which no score
+    // can exceed), a rare second pass instead of a rescale on every tile.
+    constexpr float kSlack = 32.0f;
+    const bool sink_lane = q4 == 0 && split == 0;             // the sink counts once per head
+    float m_ref[HPW], m_seen[HPW], l_run[HPW];                 // log2 domain, per head
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+        m_ref[hb] = sink2[hb];
+        m_seen[hb] = sink2[hb];                                // max of the sink and all scores
+        l_run[hb] = sink_lane ? 1.0f : 0.0f;                   // exp2(sink2 - m_ref)
+    }
+    bool have_ref = false;                                     // same in all lanes of a wave
+    f32x4 o_acc[G::kDBlocks][HPW];
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) o_acc[b][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Per-lane LDS byte offsets of the two operand reads (the swizzle only touches the low
+    // four bits of a chunk index, so each read is one of these plus a multiple of 256 B; rows
+    // 16 apart share a swizzle, so the second 16-key block is the same plus kHalf):
+    //   K operand, block mb, step kk: qk_off[kk % 4] + 256 * (kk / 4) + kHalf * mb
+    //   V operand, read ab, d slice db: pv_off[db % 8] + 256 * (db / 8) + kHalf * ab
+    constexpr int kHalf = 16 * G::kRowBytes;
+    int qk_off[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qk_off[k] = l16 * G::kRowBytes + 16 * ((4 * k + q4) ^ swz<G::kChunks>(l16));
+    int pv_off[8];
+    {
+        // 16-lane group q4 reads keys 4*q4 + (0..3) (then 16 + ...) of d columns
+        // 16*db + (0..15); lane i of the group names row i/4 and columns 4*(i%4)..+3 of that
+        // 4 x 16 block and receives column i.
+        const int rr = 4 * q4 + (l16 >> 2);
+#pragma unroll
+        for (int b8 = 0; b8 < 8; ++b8) {
+            const int col = 16 * b8 + 4 * (l16 & 3);           // bf16 column within 128
+            pv_off[b8] = rr * G::kRowBytes + (col & 7) * 2 + 16 * ((col >> 3) ^ swz<G::kChunks>(rr));
+        }
+    }
+
+    constexpr int kAhead = FP8 ? 1 : PP::kAhead;
+    for (int pass = 0;; ++pass) {
+    // prologue: the first kAhead tiles (bf16) or the first tile (fp8)
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+        if (j < ntiles) {
+            if constexpr (FP8)
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, istage + j * kTileKeys, raw(0), raw_sc(0), wid, lane);
+            else
+                gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
+        }
+    }
+
+    for (int it = 0; it < ntiles; ++it) {
+        SA_LDS const int32_t* tidx = istage + it * kTileKeys;
+        // which columns of this tile name a row (one bit per key)
+        const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
+        SA_LDS uint8_t* cur;
+        if constexpr (FP8) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (it + 1 < ntiles)
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx + kTileKeys, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
+            convert_tile_fp8<D, NW>(raw(it & 1), raw_sc(it & 1), tile(0), tid);
+            __syncthreads();
+            cur = tile(0);
+        } else {
+            // tile `it` has landed once only the loads of the younger tiles in flight remain
+            // (kAhead-1 of them, fewer at the end)
+            const int younger = ntiles - 1 - it;
+            if (younger >= kAhead - 1) wait_vmcnt<PP::kWait>();
+            else if (kAhead > 2 && younger == 1) wait_vmcnt<PP::kLoadsPerWave>();
+            else wait_vmcnt<0>();
+            cur = tile(it % NB);
+            if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
+            lds_barrier();                 // tile visible to all; buffer of tile it-1 free
+            if (it + kAhead < ntiles)
+                gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAhead * kTileKeys, tile((it + kAhead) % NB), wid, lane);
+        }
+        if (valid == 0) continue;                              // a tile of skips only
+
+        // Opaque to the optimiser: addresses derived from the offsets are then formed next
+        // to their reads inside the loop instead of being hoisted (and spilled) in bulk.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(qk_off[k]));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[k]));
+
+        // ---- S^T = K . Q^T over the tile's two 16-key blocks. K operands are read
+        //      kPre steps ahead of their multiply; scheduling fences keep the compiler from
+        //      hoisting every read of the unrolled loop.
+        f32x4 s_acc[2][HPW];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
+            u32x4 a0[kPre], a1[kPre];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) {
+                a0[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2));
+                a1[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2) + kHalf);
+            }
+#pragma unroll
+            for (int kk = 0; kk < G::kKSteps; ++kk) {
+                const u32x4 c0 = a0[kk % kPre], c1 = a1[kk % kPre];
+                if (kk + kPre < G::kKSteps) {
+                    const int nk = kk + kPre;
+                    a0[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2));
+                    a1[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2) + kHalf);
+                }
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb) {
+                    const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
+                    s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0][hb], 0, 0, 0);
+                    s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1][hb], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        // ---- softmax (log2 domain) against the fixed reference; this lane: head l16 of
+        //      each block, keys 16*mb + 4*q4 + r
+        const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
+        float tmax[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            float tm = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = ((lm >> (16 * mb + r)) & 1u) ? s_acc[mb][hb][r] * p.scale_log2 : -INFINITY;
+                    s_acc[mb][hb][r] = sv;
+                    tm = fmaxf(tm, sv);
+                }
+            tmax[hb] = max4groups(tm);
+            m_seen[hb] = fmaxf(m_seen[hb], tmax[hb]);
+        }
+        if (!have_ref) {
+            // first tile with a row (valid != 0, so tmax is finite): O is still zero
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) {
+                m_ref[hb] = fmaxf(sink2[hb], tmax[hb]);
+                l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
+            }
+            have_ref = true;
+        }
+        bool over = false;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) over |= tmax[hb] > m_ref[hb] + kSlack;
+        if (__ballot(over) != 0 && lane == 0) *redo = 1;
+        u32x4 pb[HPW];                                         // P as the PV B operands
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            float psum = 0.0f;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const float p0 = fast_exp2(s_acc[mb][hb][0] - m_ref[hb]), p1 = fast_exp2(s_acc[mb][hb][1] - m_ref[hb]);
+                const float p2 = fast_exp2(s_acc[mb][hb][2] - m_ref[hb]), p3 = fast_exp2(s_acc[mb][hb][3] - m_ref[hb]);
+                psum += (p0 + p1) + (p2 + p3);
+                pb[hb][2 * mb] = pack_bf16x2(p0, p1);
+                pb[hb][2 * mb + 1] = pack_bf16x2(p2, p3);
+            }
+            l_run[hb] += psum;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time;
+        //      V operands read kPre slices ahead
+        {
+            constexpr int kPre = 2;
+            bf16x4v va[kPre], vb[kPre];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) {
+                va[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3)));
+                vb[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3) + kHalf));
+            }
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                const bf16x8 a = __builtin_shufflevector(va[db % kPre], vb[db % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
+                if (db + kPre < G::kDBlocks) {
+                    const int nb = db + kPre;
+                    va[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3)));
+                    vb[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3) + kHalf));
+                }
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb)
+                    o_acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[hb]), o_acc[db][hb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // A score ran more than kSlack above its head's reference (rare): run the key loop again
+    // against the maximum of all scores, which every wave has tracked for its heads.
+    __syncthreads();
+    const int again = *redo;
+    if (pass > 0 || again == 0) break;
+    __syncthreads();                                           // every wave has read the flag
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+        m_ref[hb] = m_seen[hb];
+        l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
+    }
+    have_ref = true;
+#pragma unroll
+    for (int b = 0; b < G::kDBlocks; ++b)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) o_acc[b][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // a skipped index >= kv_rows is reported once per wave
+    if ((p.flags & 1u) && __ballot(err) != 0 && lane == 0) atomicOr(p.err_word, 1);
+
+    // ---- finish: the four lane groups share m_ref; their partial sums add up
+    float l_tot[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
+    // O^T accumulator layout: lane holds head head_of(hb), d = 16*db + 4*q4 + (0..3)
+    if (p.splits == 1) {
+        // the position's (cos, sin) row, staged once in LDS for all heads of the query (the
+        // index stage is free now), so the stores below never wait on table loads
+        const float* cs_g = rope_row(p, seq, t, tid == 0);
+        SA_LDS float* cs = (SA_LDS float*)smem;
+        __syncthreads();
+        if (cs_g != nullptr)
+            for (int i = tid; i < p.rope_dim; i += NW * kWave) cs[i] = cs_g[i];
+        __syncthreads();
+        const int r0 = D - p.rope_dim;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            if (head_of(hb) >= p.h) continue;
+            const float inv_l = l_tot[hb] > 0.0f ? 1.0f / l_tot[hb] : 0.0f;
+            uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                const int d0 = 16 * db + 4 * q4;
+                const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
+                *(u32x2*)(orow + d0) = epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2],
+                                                 o_acc[db][hb][3], inv_l, rot, d0, r0, (SA_LDS const float*)cs);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            if (head_of(hb) >= p.h) continue;
+            const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head_of(hb);
+            float* wo = p.ws_o + slot * D;
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db][hb];
+            if (q4 == 0) {
+                p.ws_ml[slot * 2 + 0] = m_ref[hb];
+                p.ws_ml[slot * 2 + 1] = l_tot[hb];
+            }
+        }
+    }
+}
+
+template <int D, bool FP8, int NW, int HPW = 1>
+inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
+    using G = Geo<D>;
+    constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
+    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)NB * G::kTileBytes +
+                       (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
+    auto k = attn_fwd_kernel<D, FP8, NW, HPW>;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(NW * kWave), lds, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -296,6 +296,57 @@ def test_deterministic_and_order_free(sa):
     assert_close(u16(c), u16(a), "column order")
 
 
+@pytest.mark.parametrize("name", ["decode_compress", "prefill_window"])
+def test_graph_replays_match_eager(sa, name):
+    """The step (window lists, then sparse_attn with the RoPE epilogue and, for the decode
+    shape, a split plan and its combine) captured in a HIP graph and replayed several times,
+    with new inputs copied in eagerly between replays: every replay equals an eager run on
+    the same inputs, bit for bit."""
+    w = W.small_variant(name)
+    q, kv, _, sink, idx = gpu_inputs(w)
+    table = sa.rope_table(w.rd, w.max_pos, w.rope_base, "cuda")
+    pos = w.pos.cuda()
+    sp = None if w.win_start_pos is None else w.win_start_pos.cuda()
+    view = idx.view(w.win_nseq, w.win_seqlen, w.topk)
+    args = sa.make_args(q, kv, sink, idx, w.scale, torch.empty_like(q), rope=(table, pos))
+    nws = sa.sparse_attn_workspace_bytes(args)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda") if nws else None
+    out = torch.empty_like(q)
+
+    def step():
+        sa.window_topk_idxs(w.window, w.win_seqlen, w.win_nseq, start_pos=sp, out=view)
+        sa.sparse_attn(q, kv, sink, idx, w.scale, out=out, rope=(table, pos), workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(7)
+    for r in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen).to(torch.bfloat16))
+        if sp is not None:
+            sp.copy_(torch.randint(w.window - 1, 4 * w.window, sp.shape, generator=gen, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref_idx = torch.empty_like(idx)
+        if w.comp_idx is not None:
+            ref_idx.copy_(idx)
+        sa.window_topk_idxs(w.window, w.win_seqlen, w.win_nseq, start_pos=sp,
+                            out=ref_idx.view(w.win_nseq, w.win_seqlen, w.topk))
+        assert torch.equal(ref_idx, idx), f"replay {r}: index lists"
+        ref = sa.sparse_attn(q, kv, sink, ref_idx, w.scale, rope=(table, pos))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {r}: output differs from the eager call"
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 FULL = {
     "decode_window": [0, 7, 19, 31],
