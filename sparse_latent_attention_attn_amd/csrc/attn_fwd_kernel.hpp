@@ -3,28 +3,29 @@
 // paragraph) and the call in Attention.forward: per query and head, a softmax in f32 over
 // the gathered latent rows plus the sink (denominator only), bf16 output.
 //
-// Work inside a workgroup of NW waves (NW = 1, 2 or 4), 16 heads per wave:
+// Work inside a workgroup of NW waves (NW = 1, 2 or 4), HPW blocks of 16 heads per wave:
 //   * key tiles of 32 index columns are gathered row by row from HBM straight into LDS
-//     (global_load_lds_dwordx4, 16 B per lane), double-buffered, so the gather of tile t+1
-//     overlaps the matrix work on tile t. All waves of the workgroup read the same tile:
-//     one gather serves 16*NW heads of the query. Rows carry a 16-byte-chunk XOR swizzle so
-//     that both LDS read patterns below avoid bank conflicts.
+//     (buffer_load_dwordx4 ... lds, 16 B per lane) through a ring of 4 buffers, 3 tiles in
+//     flight, so the gathers overlap the matrix work. All waves of the workgroup read the
+//     same tile: one gather serves every head of the query in the workgroup. Rows carry a
+//     16-byte-chunk XOR swizzle so that both LDS read patterns below avoid bank conflicts.
 //   * scores are computed transposed, S^T[key][head] = K . Q^T, on v_mfma_f32_16x16x32_bf16:
-//     K comes from LDS as the A operand, Q stays in registers as the B operand. In the
-//     accumulator layout each lane holds one head and 4 keys per 16-key block, so the
-//     online softmax needs in-lane work plus two exchanges across the 4 lane groups.
+//     K comes from LDS as the A operand (each read feeds the HPW head blocks), Q stays in
+//     registers as the B operand. In the accumulator layout each lane holds one head and 4
+//     keys per 16-key block, so the softmax needs in-lane work plus two exchanges across
+//     the 4 lane groups.
 //   * the probabilities are rounded to bf16 in registers and are already the B operand of
 //     O^T[d][head] += V^T . P^T (a 32-key step); V^T is read from the same LDS tile with the
 //     transposing ds_read_b64_tr_b16, so the tile is stored once and is both K and V.
-//   * O^T stays in accumulator registers (4 f32 per lane per 16-wide slice of d); each lane
-//     holds a single head, so the softmax rescale is a per-lane scalar multiply.
-//   * the running max starts at the sink logit and the running sum at exp(0) = 1 (counted
-//     in one lane group only and in split 0 only), which puts the sink in the denominator.
-//   * with more than one split, unnormalised partials (O, m, l) go to the workspace and a
-//     small combine kernel merges them; otherwise the epilogue (divide, bf16, optional
-//     inverse RoPE) runs here.
-// At d = 512 a wave keeps Q (64 VGPRs) and O (128 accumulators) resident for the whole key
-// loop; 16 heads per wave is what fits beside them without spilling.
+//   * softmax against a fixed reference per head (taken at the first tile that names a row,
+//     from the sink and that tile's scores), with a rare second pass over the keys when a
+//     later score exceeds it by too much: O is never rescaled inside the key loop and stays
+//     in accumulator registers (4 f32 per lane per 16-wide slice of d and head block).
+//   * the sink enters the running sum as exp(sink - reference), in one lane group and in
+//     split 0 only, which puts it in the denominator.
+//   * with more than one split, unnormalised partials (O, reference, sum) go to the
+//     workspace and a small combine kernel merges them; otherwise the epilogue (divide,
+//     bf16, optional inverse RoPE) runs here.
 #pragma once
 
 #include "sa_device.hpp"
@@ -226,14 +227,19 @@ __device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a
 // Position of query t of sequence seq and its (cos, sin) row, or nullptr when the epilogue
 // is off or the position has no row in the table (then no rotation is applied; bit 2 of
 // the error word records it when checking is on).
-__device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int t, bool report) {
+__device__ __forceinline__ int rope_pos(const KParams& p, int seq, int t) {
+    return p.rope_dim == 0 ? 0 : p.pos[(int64_t)seq * p.pos_seq_stride + t];
+}
+__device__ __forceinline__ const float* rope_ptr(const KParams& p, int pos, bool report) {
     if (p.rope_dim == 0) return nullptr;
-    const int pos = p.pos[(int64_t)seq * p.pos_seq_stride + t];
     if (pos < 0 || pos >= p.max_pos) {
         if (report && (p.flags & 1u)) atomicOr(p.err_word, 2);
         return nullptr;
     }
     return p.rope_cs + (int64_t)pos * p.rope_dim;
+}
+__device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int t, bool report) {
+    return rope_ptr(p, rope_pos(p, seq, t), report);
 }
 
 // Work item of block b (items are query-major: item = query * per_q + j). Workgroups are
@@ -283,10 +289,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     constexpr int NB = FP8 ? 1 : PP::kBuffers;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
-    // LDS: the index stage (kMaxColsPerSplit int32), then NB bf16 tiles; fp8 adds two raw
-    // staging tiles of codes and two of scale bytes.
+    // LDS: the index stage (kMaxColsPerSplit int32), 64 B of flags, the position's (cos, sin)
+    // row (D f32), then NB bf16 tiles; fp8 adds two raw staging tiles of codes and two of
+    // scale bytes.
     SA_LDS int32_t* istage = (SA_LDS int32_t*)smem;
-    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4 + 64;
+    SA_LDS float* cs_lds = (SA_LDS float*)(smem + kMaxColsPerSplit * 4 + 64);
+    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4 + 64 + D * 4;
     auto tile = [&](int i) { return tiles + i * G::kTileBytes; };
     auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
     auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
@@ -319,54 +327,67 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
     const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
 
-    // ---- start-up, arranged so that its memory latencies overlap: the index loads go out
-    // first, then Q and the sink; the index stage is written as soon as the index loads
-    // land (Q may still be in flight), the first key tiles are issued, and only then does
-    // anything wait for Q.
-    //
+    // ---- start-up, arranged so that its memory latencies overlap: the position and the
+    // index loads go out first, then the position's (cos, sin) row, Q and the sink; the
+    // index stage is written as soon as the index loads land (Q may still be in flight).
+    // Every load here is issued by every lane (addresses clamped instead of per-lane
+    // branches), so the compiler's waits for one group never cover the next.
+    const int pos = rope_pos(p, seq, t);
+
     // Stage this split's index columns in LDS, skips and out-of-range rows as -1, padded
     // to whole tiles, and find the last column that names a row (trailing tiles of padding
-    // are never gathered). Each thread issues kStageUnroll index loads at a time.
+    // are never gathered). Each thread issues kStageUnroll index loads at a time; columns
+    // past the end re-read the last column and are masked afterwards.
     constexpr int kStageUnroll = 16;
     const int ncols_pad = (ncols + kTileKeys - 1) / kTileKeys * kTileKeys;
+    const int32_t* cols = idx_row + col_begin;
     int err = 0;
     int last = -1;
     int stage_v[kStageUnroll];
+    if (ncols > 0) {
 #pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-        const int c = tid + u * NW * kWave;
-        stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
+        for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[min(tid + u * NW * kWave, ncols - 1)];
+    }
+    // nullptr: no rotation here (none asked for, or the combine kernel finishes the rows)
+    const float* cs_g = p.splits == 1 ? rope_ptr(p, pos, tid == 0) : nullptr;
+    constexpr int kCsPer = (D + NW * kWave - 1) / (NW * kWave);
+    float cs_v[kCsPer];
+    if (cs_g != nullptr) {
+#pragma unroll
+        for (int u = 0; u < kCsPer; ++u) cs_v[u] = cs_g[min(tid + u * NW * kWave, p.rope_dim - 1)];
     }
     // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
-    // d = 32*kk + 8*q4 + 0..7
+    // d = 32*kk + 8*q4 + 0..7. Padding heads (past h) repeat the last head: they are never
+    // stored, and their softmax, identical to that head's, flags nothing new.
     u32x4 qreg[HPW][G::kKSteps];
     float sink_raw[HPW];
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
-        const bool ok = head_of(hb) < p.h;
-        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
+        const int hq = min(head_of(hb), p.h - 1);
+        const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + hq) * D;
 #pragma unroll
-        for (int kk = 0; kk < G::kKSteps; ++kk)
-            qreg[hb][kk] = ok ? *(const u32x4*)(qrow + 32 * kk + 8 * q4) : u32x4{0, 0, 0, 0};
-        sink_raw[hb] = ok ? p.sink[head_of(hb)] : 0.0f;
+        for (int kk = 0; kk < G::kKSteps; ++kk) qreg[hb][kk] = *(const u32x4*)(qrow + 32 * kk + 8 * q4);
+        sink_raw[hb] = p.sink[hq];
     }
     for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
         if (c0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kStageUnroll; ++u) {
-                const int c = c0 + tid + u * NW * kWave;
-                stage_v[u] = c < ncols ? idx_row[col_begin + c] : -1;
-            }
+            for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[min(c0 + tid + u * NW * kWave, ncols - 1)];
         }
 #pragma unroll
         for (int u = 0; u < kStageUnroll; ++u) {
             const int c = c0 + tid + u * NW * kWave;
-            int row = stage_v[u];
+            int row = c < ncols ? stage_v[u] : -1;
             if (row >= p.kv_rows) { err = 1; row = -1; }
             row = row < 0 ? -1 : row;
             if (c < ncols_pad) istage[c] = row;
             if (row >= 0) last = c;
         }
+    }
+    if (cs_g != nullptr) {
+#pragma unroll
+        for (int u = 0; u < kCsPer; ++u)
+            if (tid + u * NW * kWave < p.rope_dim) cs_lds[tid + u * NW * kWave] = cs_v[u];
     }
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
     SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
@@ -612,14 +633,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
     // O^T accumulator layout: lane holds head head_of(hb), d = 16*db + 4*q4 + (0..3)
     if (p.splits == 1) {
-        // the position's (cos, sin) row, staged once in LDS for all heads of the query (the
-        // index stage is free now), so the stores below never wait on table loads
-        const float* cs_g = rope_row(p, seq, t, tid == 0);
-        SA_LDS float* cs = (SA_LDS float*)smem;
-        __syncthreads();
-        if (cs_g != nullptr)
-            for (int i = tid; i < p.rope_dim; i += NW * kWave) cs[i] = cs_g[i];
-        __syncthreads();
+        // the position's (cos, sin) row was staged in LDS at start-up (visible since the
+        // barrier after the key loop), so the stores below never wait on table loads
         const int r0 = D - p.rope_dim;
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
@@ -631,7 +646,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 const int d0 = 16 * db + 4 * q4;
                 const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
                 *(u32x2*)(orow + d0) = epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2],
-                                                 o_acc[db][hb][3], inv_l, rot, d0, r0, (SA_LDS const float*)cs);
+                                                 o_acc[db][hb][3], inv_l, rot, d0, r0, (SA_LDS const float*)cs_lds);
             }
         }
     } else {
@@ -654,7 +669,7 @@ template <int D, bool FP8, int NW, int HPW = 1>
 inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
     constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
-    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)NB * G::kTileBytes +
+    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)D * 4 + (size_t)NB * G::kTileBytes +
                        (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
     auto k = attn_fwd_kernel<D, FP8, NW, HPW>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
