@@ -35,12 +35,16 @@ namespace sa {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte chunk swizzle of LDS row r. Both operand reads must hit distinct banks:
-//   K operand: 16 consecutive rows at one chunk -> swz must be a bijection on r mod 16;
-//   V operand: a transposing read covers 8 consecutive rows x 2 adjacent chunks (c, c^1)
-//   -> swz(r) >> 1 must differ across every 8 aligned consecutive rows.
-// ((r & 7) << 1) | ((r >> 3) & 1) does both; it only changes the low four bits of a chunk
-// index (for rows narrower than 16 chunks it is cut down to the row).
+// 16-byte chunk swizzle of LDS row r. Both operand reads must hit distinct banks (64 banks
+// of 4 bytes; a bank group is a 16-byte chunk index mod 16):
+//   V operand: a transposing read serves 32 lanes at a time, covering 8 consecutive rows x
+//   2 adjacent chunks (c, c^1) -> swz(r) >> 1 must differ across every 8 aligned rows;
+//   K operand: each ds_read_b128 lane group (two octets) reads rows 0-7 at chunk c and rows
+//   8-15 at chunk c ^ 2 -> swz must map rows 0-7 and rows 8-15 to complementary sets that
+//   the XOR by 2 keeps apart.
+// ((r & 7) << 1) | ((r >> 3) & 1) does both (rows 0-7 -> even, rows 8-15 -> odd chunks); it
+// only changes the low four bits of a chunk index (for rows narrower than 16 chunks it is
+// cut down to the row).
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
     return (((r & 7) << 1) | ((r >> 3) & 1)) & (CH - 1);
@@ -304,6 +308,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int lane = tid % kWave;
     const int l16 = lane & 15;                  // this lane's head within a 16-head block
     const int q4 = lane >> 4;                   // lane group 0..3
+    // d chunk (8 elements) that lane group q4 takes in each 32-wide step of the QK product:
+    // 0, 2, 1, 3. Any order is correct as long as K and Q use the same one; this one keeps the
+    // K operand reads free of bank conflicts (ds_read_b128 serves the lanes in four groups of
+    // two octets, {0-7, 24-31}, {8-15, 16-23}, {32-39, 56-63}, {40-47, 48-55}, and with the
+    // row swizzle below these groups then read sixteen distinct 16-byte bank groups).
+    const int qc = ((q4 & 1) << 1) | (q4 >> 1);
 
     // work item: ((query * head_blocks) + head block) * splits + split, in the XCD-aware
     // order of work_item
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int u = 0; u < kCsPer; ++u) cs_v[u] = cs_g[min(tid + u * NW * kWave, p.rope_dim - 1)];
     }
     // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
-    // d = 32*kk + 8*q4 + 0..7. Padding heads (past h) repeat the last head: they are never
+    // d = 32*kk + 8*qc + 0..7. Padding heads (past h) repeat the last head: they are never
     // stored, and their softmax, identical to that head's, flags nothing new.
     u32x4 qreg[HPW][G::kKSteps];
     float sink_raw[HPW];
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         const int hq = min(head_of(hb), p.h - 1);
         const uint16_t* qrow = p.q + (int64_t)seq * p.q_seq_stride + ((int64_t)t * p.h + hq) * D;
 #pragma unroll
-        for (int kk = 0; kk < G::kKSteps; ++kk) qreg[hb][kk] = *(const u32x4*)(qrow + 32 * kk + 8 * q4);
+        for (int kk = 0; kk < G::kKSteps; ++kk) qreg[hb][kk] = *(const u32x4*)(qrow + 32 * kk + 8 * qc);
         sink_raw[hb] = p.sink[hq];
     }
     for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
         m_ref[hb] = sink2[hb];
-        m_seen[hb] = sink2[hb];                                // max of the sink and all scores
+        m_seen[hb] = -INFINITY;                                // this lane's maximum score
         l_run[hb] = sink_lane ? 1.0f : 0.0f;                   // exp2(sink2 - m_ref)
     }
     bool have_ref = false;                                     // same in all lanes of a wave
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     constexpr int kHalf = 16 * G::kRowBytes;
     int qk_off[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qk_off[k] = l16 * G::kRowBytes + 16 * ((4 * k + q4) ^ swz<G::kChunks>(l16));
+    for (int k = 0; k < 4; ++k) qk_off[k] = l16 * G::kRowBytes + 16 * ((4 * k + qc) ^ swz<G::kChunks>(l16));
     int pv_off[8];
     {
         // 16-lane group q4 reads keys 4*q4 + (0..3) (then 16 + ...) of d columns
@@ -535,44 +545,69 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
 
         // ---- softmax (log2 domain) against the fixed reference; this lane: head l16 of
-        //      each block, keys 16*mb + 4*q4 + r
-        const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
-        float tmax[HPW];
-#pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) {
-            float tm = -INFINITY;
+        //      each block, keys 16*mb + 4*q4 + r. A score in log2 units is raw * scale_log2.
+        //      Skipped keys (rows zeroed in LDS) get a raw score of -inf; a tile whose keys
+        //      all name a row, the common case, needs no masking.
+        if (valid != 0xffffffffu) {
+            const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float sv = ((lm >> (16 * mb + r)) & 1u) ? s_acc[mb][hb][r] * p.scale_log2 : -INFINITY;
-                    s_acc[mb][hb][r] = sv;
-                    tm = fmaxf(tm, sv);
+                    const bool keep = (lm >> (16 * mb + r)) & 1u;
+#pragma unroll
+                    for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb][r] = keep ? s_acc[mb][hb][r] : -INFINITY;
                 }
-            tmax[hb] = max4groups(tm);
-            m_seen[hb] = fmaxf(m_seen[hb], tmax[hb]);
+        }
+        // With a positive scale a maximum of scores is the scaled maximum of the raw scores
+        // and each probability is exp2(fma(raw, scale, -m_ref)). Otherwise the scores are
+        // scaled first (unit scale afterwards), skipped keys set to -inf again after scaling.
+        float sc = p.scale_log2;
+        if (!(sc > 0.0f)) {
+            const uint32_t lm = valid >> (4 * q4);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = (lm >> (16 * mb + r)) & 1u;
+#pragma unroll
+                    for (int hb = 0; hb < HPW; ++hb)
+                        s_acc[mb][hb][r] = keep ? s_acc[mb][hb][r] * sc : -INFINITY;
+                }
+            sc = 1.0f;
+        }
+        // this lane's maximum of its 8 scores per head block; the lane groups are only
+        // combined where a head's maximum is needed (the first tile, the second pass)
+        float lmax[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            const float t0 = fmaxf(fmaxf(s_acc[0][hb][0], s_acc[0][hb][1]), fmaxf(s_acc[0][hb][2], s_acc[0][hb][3]));
+            const float t1 = fmaxf(fmaxf(s_acc[1][hb][0], s_acc[1][hb][1]), fmaxf(s_acc[1][hb][2], s_acc[1][hb][3]));
+            lmax[hb] = fmaxf(t0, t1) * sc;
+            m_seen[hb] = fmaxf(m_seen[hb], lmax[hb]);
         }
         if (!have_ref) {
-            // first tile with a row (valid != 0, so tmax is finite): O is still zero
+            // first tile with a row (valid != 0, so its maximum is finite): O is still zero
 #pragma unroll
             for (int hb = 0; hb < HPW; ++hb) {
-                m_ref[hb] = fmaxf(sink2[hb], tmax[hb]);
+                m_ref[hb] = fmaxf(sink2[hb], max4groups(lmax[hb]));
                 l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
             }
             have_ref = true;
         }
         bool over = false;
 #pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) over |= tmax[hb] > m_ref[hb] + kSlack;
+        for (int hb = 0; hb < HPW; ++hb) over |= lmax[hb] > m_ref[hb] + kSlack;
         if (__ballot(over) != 0 && lane == 0) *redo = 1;
         u32x4 pb[HPW];                                         // P as the PV B operands
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
             float psum = 0.0f;
+            const float nm = -m_ref[hb];
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const float p0 = fast_exp2(s_acc[mb][hb][0] - m_ref[hb]), p1 = fast_exp2(s_acc[mb][hb][1] - m_ref[hb]);
-                const float p2 = fast_exp2(s_acc[mb][hb][2] - m_ref[hb]), p3 = fast_exp2(s_acc[mb][hb][3] - m_ref[hb]);
+                const float p0 = fast_exp2(fmaf(s_acc[mb][hb][0], sc, nm)), p1 = fast_exp2(fmaf(s_acc[mb][hb][1], sc, nm));
+                const float p2 = fast_exp2(fmaf(s_acc[mb][hb][2], sc, nm)), p3 = fast_exp2(fmaf(s_acc[mb][hb][3], sc, nm));
                 psum += (p0 + p1) + (p2 + p3);
                 pb[hb][2 * mb] = pack_bf16x2(p0, p1);
                 pb[hb][2 * mb + 1] = pack_bf16x2(p2, p3);
@@ -614,7 +649,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     __syncthreads();                                           // every wave has read the flag
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
-        m_ref[hb] = m_seen[hb];
+        m_ref[hb] = fmaxf(sink2[hb], max4groups(m_seen[hb]));
         l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
     }
     have_ref = true;
