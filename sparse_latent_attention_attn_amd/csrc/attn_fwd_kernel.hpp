@@ -231,8 +231,16 @@ __device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a
 // Position of query t of sequence seq and its (cos, sin) row, or nullptr when the epilogue
 // is off or the position has no row in the table (then no rotation is applied; bit 2 of
 // the error word records it when checking is on).
+// The position is read with a vector load (through a zero offset held in a vector register,
+// which the compiler cannot see through): a scalar load would be waited for together with the
+// kernel-argument loads (scalar loads complete out of order, so the compiler can only wait
+// for all of them), which would hold back every load issued after that wait by one memory
+// round trip.
 __device__ __forceinline__ int rope_pos(const KParams& p, int seq, int t) {
-    return p.rope_dim == 0 ? 0 : p.pos[(int64_t)seq * p.pos_seq_stride + t];
+    if (p.rope_dim == 0) return 0;
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    return p.pos[(int64_t)seq * p.pos_seq_stride + t + zero];
 }
 __device__ __forceinline__ const float* rope_ptr(const KParams& p, int pos, bool report) {
     if (p.rope_dim == 0) return nullptr;
@@ -338,8 +346,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
 
     // ---- start-up, arranged so that its memory latencies overlap: the position and the
-    // index loads go out first, then the position's (cos, sin) row, Q and the sink; the
-    // index stage is written as soon as the index loads land (Q may still be in flight).
+    // index loads go out first, then Q and the sink; the index stage is written as soon as
+    // the index loads land (Q may still be in flight).
     // Every load here is issued by every lane (addresses clamped instead of per-lane
     // branches), so the compiler's waits for one group never cover the next.
     const int pos = rope_pos(p, seq, t);
@@ -357,14 +365,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     if (ncols > 0) {
 #pragma unroll
         for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[min(tid + u * NW * kWave, ncols - 1)];
-    }
-    // nullptr: no rotation here (none asked for, or the combine kernel finishes the rows)
-    const float* cs_g = p.splits == 1 ? rope_ptr(p, pos, tid == 0) : nullptr;
-    constexpr int kCsPer = (D + NW * kWave - 1) / (NW * kWave);
-    float cs_v[kCsPer];
-    if (cs_g != nullptr) {
-#pragma unroll
-        for (int u = 0; u < kCsPer; ++u) cs_v[u] = cs_g[min(tid + u * NW * kWave, p.rope_dim - 1)];
     }
     // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
     // d = 32*kk + 8*qc + 0..7. Padding heads (past h) repeat the last head: they are never
@@ -394,11 +394,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             if (row >= 0) last = c;
         }
     }
-    if (cs_g != nullptr) {
-#pragma unroll
-        for (int u = 0; u < kCsPer; ++u)
-            if (tid + u * NW * kWave < p.rope_dim) cs_lds[tid + u * NW * kWave] = cs_v[u];
-    }
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
     SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
     SA_LDS int32_t* redo = lastw + 8;                           // second-pass flag
@@ -416,6 +411,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // count the tile loads (inline assembly), so its own waits for Q must not meet them.
     __builtin_amdgcn_s_waitcnt(0);
     asm volatile("" ::: "memory");
+    // The position's (cos, sin) row is only needed by the epilogue: its loads go out here,
+    // before every tile load, so they never disturb the tile waits (which count only tile
+    // loads issued after them), and they land with the first tile at the latest.
+    // nullptr: no rotation here (none asked for, or the combine kernel finishes the rows)
+    const float* cs_g = p.splits == 1 ? rope_ptr(p, pos, tid == 0) : nullptr;
+    constexpr int kCsPer = (D + NW * kWave - 1) / (NW * kWave);
+    float cs_v[kCsPer];
+    if (cs_g != nullptr) {
+#pragma unroll
+        for (int u = 0; u < kCsPer; ++u) cs_v[u] = cs_g[min(tid + u * NW * kWave, p.rope_dim - 1)];
+    }
 
     // Softmax reference. Every probability of a pass is exp2(score - m_ref) with one fixed
     // reference per head, so O is never rescaled inside the key loop: m_ref is taken at the
@@ -434,6 +440,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         l_run[hb] = sink_lane ? 1.0f : 0.0f;                   // exp2(sink2 - m_ref)
     }
     bool have_ref = false;                                     // same in all lanes of a wave
+    bool over = false;                                         // a score passed m_ref + kSlack
     f32x4 o_acc[G::kDBlocks][HPW];
 #pragma unroll
     for (int b = 0; b < G::kDBlocks; ++b)
@@ -462,92 +469,53 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
     }
 
-    constexpr int kAhead = FP8 ? 1 : PP::kAhead;
-    for (int pass = 0;; ++pass) {
-    // prologue: the first kAhead tiles (bf16) or the first tile (fp8)
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) {
-        if (j < ntiles) {
-            if constexpr (FP8)
-                gather_tile_fp8<D, NW>(kv_seq, sc_seq, istage + j * kTileKeys, raw(0), raw_sc(0), wid, lane);
-            else
-                gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
-        }
-    }
-
-    for (int it = 0; it < ntiles; ++it) {
-        SA_LDS const int32_t* tidx = istage + it * kTileKeys;
-        // which columns of this tile name a row (one bit per key)
-        const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
-        SA_LDS uint8_t* cur;
-        if constexpr (FP8) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (it + 1 < ntiles)
-                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx + kTileKeys, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
-            convert_tile_fp8<D, NW>(raw(it & 1), raw_sc(it & 1), tile(0), tid);
-            __syncthreads();
-            cur = tile(0);
-        } else {
-            // tile `it` has landed once only the loads of the younger tiles in flight remain
-            // (kAhead-1 of them, fewer at the end)
-            const int younger = ntiles - 1 - it;
-            if (younger >= kAhead - 1) wait_vmcnt<PP::kWait>();
-            else if (kAhead > 2 && younger == 1) wait_vmcnt<PP::kLoadsPerWave>();
-            else wait_vmcnt<0>();
-            cur = tile(it % NB);
-            if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
-            lds_barrier();                 // tile visible to all; buffer of tile it-1 free
-            if (it + kAhead < ntiles)
-                gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAhead * kTileKeys, tile((it + kAhead) % NB), wid, lane);
-        }
-        if (valid == 0) continue;                              // a tile of skips only
-
-        // Opaque to the optimiser: addresses derived from the offsets are then formed next
-        // to their reads inside the loop instead of being hoisted (and spilled) in bulk.
-#pragma unroll
-        for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(qk_off[k]));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[k]));
-
-        // ---- S^T = K . Q^T over the tile's two 16-key blocks. K operands are read
-        //      kPre steps ahead of their multiply; scheduling fences keep the compiler from
-        //      hoisting every read of the unrolled loop.
-        f32x4 s_acc[2][HPW];
+    // ---- the stages of one key tile, shared by the two loop shapes below ----------------
+    // QK: S^T = K . Q^T over the tile's two 16-key blocks. K operands are read kPre steps
+    // ahead of their multiply; scheduling fences keep the compiler from hoisting every read of
+    // the unrolled loop.
+    auto qk = [&](SA_LDS const uint8_t* cur, f32x4 (&s_acc)[2][HPW]) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-            constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
-            u32x4 a0[kPre], a1[kPre];
+        constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
+        u32x4 a0[kPre], a1[kPre];
 #pragma unroll
-            for (int k = 0; k < kPre; ++k) {
-                a0[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2));
-                a1[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2) + kHalf);
-            }
-#pragma unroll
-            for (int kk = 0; kk < G::kKSteps; ++kk) {
-                const u32x4 c0 = a0[kk % kPre], c1 = a1[kk % kPre];
-                if (kk + kPre < G::kKSteps) {
-                    const int nk = kk + kPre;
-                    a0[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2));
-                    a1[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2) + kHalf);
-                }
-#pragma unroll
-                for (int hb = 0; hb < HPW; ++hb) {
-                    const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
-                    s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0][hb], 0, 0, 0);
-                    s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1][hb], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int k = 0; k < kPre; ++k) {
+            a0[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2));
+            a1[k] = *(SA_LDS const u32x4*)(cur + qk_off[k & 3] + 256 * (k >> 2) + kHalf);
         }
+#pragma unroll
+        for (int kk = 0; kk < G::kKSteps; ++kk) {
+            const u32x4 c0 = a0[kk % kPre], c1 = a1[kk % kPre];
+            if (kk + kPre < G::kKSteps) {
+                const int nk = kk + kPre;
+                a0[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2));
+                a1[kk % kPre] = *(SA_LDS const u32x4*)(cur + qk_off[nk & 3] + 256 * (nk >> 2) + kHalf);
+            }
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) {
+                const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
+                s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0][hb], 0, 0, 0);
+                s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1][hb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
-        // ---- softmax (log2 domain) against the fixed reference; this lane: head l16 of
-        //      each block, keys 16*mb + 4*q4 + r. A score in log2 units is raw * scale_log2.
-        //      Skipped keys (rows zeroed in LDS) get a raw score of -inf; a tile whose keys
-        //      all name a row, the common case, needs no masking.
+    // Softmax, part 1 (log2 domain; this lane: head l16 of each block, keys 16*mb + 4*q4 + r;
+    // a score in log2 units is raw * scale_log2). Skipped keys (rows zeroed in LDS) get a raw
+    // score of -inf; a tile whose keys all name a row, the common case, needs no masking.
+    // With a positive scale a maximum of scores is the scaled maximum of the raw scores and
+    // each probability is exp2(fma(raw, scale, -m_ref)); otherwise the scores are scaled here
+    // (skipped keys set to -inf again) and the returned scale is 1. At the first tile that
+    // names a row the reference is taken (O is still zero then).
+    auto lane_max = [&](const f32x4 (&s_acc)[2][HPW], int hb) {
+        const float t0 = fmaxf(fmaxf(s_acc[0][hb][0], s_acc[0][hb][1]), fmaxf(s_acc[0][hb][2], s_acc[0][hb][3]));
+        const float t1 = fmaxf(fmaxf(s_acc[1][hb][0], s_acc[1][hb][1]), fmaxf(s_acc[1][hb][2], s_acc[1][hb][3]));
+        return fmaxf(t0, t1);
+    };
+    auto prepare = [&](f32x4 (&s_acc)[2][HPW], uint32_t valid) {
         if (valid != 0xffffffffu) {
             const uint32_t lm = valid >> (4 * q4);     // bits r and 16 + r: this lane's keys
 #pragma unroll
@@ -559,9 +527,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb][r] = keep ? s_acc[mb][hb][r] : -INFINITY;
                 }
         }
-        // With a positive scale a maximum of scores is the scaled maximum of the raw scores
-        // and each probability is exp2(fma(raw, scale, -m_ref)). Otherwise the scores are
-        // scaled first (unit scale afterwards), skipped keys set to -inf again after scaling.
         float sc = p.scale_log2;
         if (!(sc > 0.0f)) {
             const uint32_t lm = valid >> (4 * q4);
@@ -576,73 +541,173 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 }
             sc = 1.0f;
         }
-        // this lane's maximum of its 8 scores per head block; the lane groups are only
-        // combined where a head's maximum is needed (the first tile, the second pass)
-        float lmax[HPW];
-#pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) {
-            const float t0 = fmaxf(fmaxf(s_acc[0][hb][0], s_acc[0][hb][1]), fmaxf(s_acc[0][hb][2], s_acc[0][hb][3]));
-            const float t1 = fmaxf(fmaxf(s_acc[1][hb][0], s_acc[1][hb][1]), fmaxf(s_acc[1][hb][2], s_acc[1][hb][3]));
-            lmax[hb] = fmaxf(t0, t1) * sc;
-            m_seen[hb] = fmaxf(m_seen[hb], lmax[hb]);
-        }
-        if (!have_ref) {
-            // first tile with a row (valid != 0, so its maximum is finite): O is still zero
+        if (!have_ref && valid != 0) {
+            // first tile with a row (valid != 0, so its maximum is finite)
 #pragma unroll
             for (int hb = 0; hb < HPW; ++hb) {
-                m_ref[hb] = fmaxf(sink2[hb], max4groups(lmax[hb]));
+                m_ref[hb] = fmaxf(sink2[hb], max4groups(lane_max(s_acc, hb) * sc));
                 l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
             }
             have_ref = true;
         }
-        bool over = false;
-#pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) over |= lmax[hb] > m_ref[hb] + kSlack;
-        if (__ballot(over) != 0 && lane == 0) *redo = 1;
-        u32x4 pb[HPW];                                         // P as the PV B operands
-#pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) {
-            float psum = 0.0f;
+        return sc;
+    };
+    // Softmax, part 2, in kSoftSteps small steps that can be interleaved with matrix work:
+    // steps 0 .. 4*HPW-1 turn two scores into probabilities (packed to bf16 as the PV B
+    // operand, summed per lane), then one step per head block tracks the lane's maximum
+    // score and flags a score more than kSlack above the reference, and the last step adds
+    // the sums to the running denominators.
+    constexpr int kSoftSteps = 5 * HPW + 1;
+    auto soft_step = [&](int k, const f32x4 (&s_acc)[2][HPW], float sc, u32x4 (&pb)[HPW], float (&psum)[HPW]) {
+        if (k < 4 * HPW) {
+            const int hb = k >> 2, mb = (k >> 1) & 1, h = k & 1;
             const float nm = -m_ref[hb];
+            const float p0 = fast_exp2(fmaf(s_acc[mb][hb][2 * h], sc, nm));
+            const float p1 = fast_exp2(fmaf(s_acc[mb][hb][2 * h + 1], sc, nm));
+            psum[hb] += p0 + p1;
+            pb[hb][2 * mb + h] = pack_bf16x2(p0, p1);
+        } else if (k < 5 * HPW) {
+            const int hb = k - 4 * HPW;
+            const float lm = lane_max(s_acc, hb) * sc;
+            m_seen[hb] = fmaxf(m_seen[hb], lm);
+            over |= lm > m_ref[hb] + kSlack;
+        } else if (k == 5 * HPW) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const float p0 = fast_exp2(fmaf(s_acc[mb][hb][0], sc, nm)), p1 = fast_exp2(fmaf(s_acc[mb][hb][1], sc, nm));
-                const float p2 = fast_exp2(fmaf(s_acc[mb][hb][2], sc, nm)), p3 = fast_exp2(fmaf(s_acc[mb][hb][3], sc, nm));
-                psum += (p0 + p1) + (p2 + p3);
-                pb[hb][2 * mb] = pack_bf16x2(p0, p1);
-                pb[hb][2 * mb + 1] = pack_bf16x2(p2, p3);
-            }
-            l_run[hb] += psum;
+            for (int hb = 0; hb < HPW; ++hb) l_run[hb] += psum[hb];
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // PV: O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time; V
+    // operands read kPre slices ahead. hook(j) runs after every second slice (j = db / 2),
+    // and the hooks the slices did not reach run at the end.
+    auto pv = [&](SA_LDS const uint8_t* cur, const u32x4 (&pb)[HPW], auto hook) {
+        constexpr int kPre = 2;
+        bf16x4v va[kPre], vb[kPre];
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+            va[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3)));
+            vb[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3) + kHalf));
+        }
+#pragma unroll
+        for (int db = 0; db < G::kDBlocks; ++db) {
+            const bf16x8 a = __builtin_shufflevector(va[db % kPre], vb[db % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
+            if (db + kPre < G::kDBlocks) {
+                const int nb = db + kPre;
+                va[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3)));
+                vb[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3) + kHalf));
+            }
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb)
+                o_acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[hb]), o_acc[db][hb], 0, 0, 0);
+            if ((db & 1) == 0 && db / 2 < kSoftSteps) hook(db / 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = (G::kDBlocks + 1) / 2; j < kSoftSteps; ++j) hook(j);
+    };
+    // Opaque to the optimiser: addresses derived from the offsets are then formed next to
+    // their reads inside the loop instead of being hoisted (and spilled) in bulk.
+    auto pin_offsets = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(qk_off[k]));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[k]));
+    };
 
-        // ---- O^T += V^T . P^T over the whole 32-key tile, one 16-wide d slice at a time;
-        //      V operands read kPre slices ahead
-        {
-            constexpr int kPre = 2;
-            bf16x4v va[kPre], vb[kPre];
+    for (int pass = 0;; ++pass) {
+    if constexpr (FP8) {
+        // fp8 storage: one bf16 tile; the codes of the next tile are gathered into a raw
+        // staging tile while the current one is converted and multiplied
+        if (ntiles > 0) gather_tile_fp8<D, NW>(kv_seq, sc_seq, istage, raw(0), raw_sc(0), wid, lane);
+        for (int it = 0; it < ntiles; ++it) {
+            SA_LDS const int32_t* tidx = istage + it * kTileKeys;
+            // which columns of this tile name a row (one bit per key)
+            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (it + 1 < ntiles)
+                gather_tile_fp8<D, NW>(kv_seq, sc_seq, tidx + kTileKeys, raw((it + 1) & 1), raw_sc((it + 1) & 1), wid, lane);
+            convert_tile_fp8<D, NW>(raw(it & 1), raw_sc(it & 1), tile(0), tid);
+            __syncthreads();
+            if (valid == 0) continue;                          // a tile of skips only
+            pin_offsets();
+            f32x4 s_acc[2][HPW];
+            qk(tile(0), s_acc);
+            const float sc = prepare(s_acc, valid);
+            u32x4 pb[HPW];
+            float psum[HPW];
 #pragma unroll
-            for (int k = 0; k < kPre; ++k) {
-                va[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3)));
-                vb[k] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[k & 7] + 256 * (k >> 3) + kHalf));
-            }
+            for (int hb = 0; hb < HPW; ++hb) psum[hb] = 0.0f;
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db) {
-                const bf16x8 a = __builtin_shufflevector(va[db % kPre], vb[db % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
-                if (db + kPre < G::kDBlocks) {
-                    const int nb = db + kPre;
-                    va[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3)));
-                    vb[db % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SA_LDS bf16x4v*)(cur + pv_off[nb & 7] + 256 * (nb >> 3) + kHalf));
-                }
-#pragma unroll
-                for (int hb = 0; hb < HPW; ++hb)
-                    o_acc[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pb[hb]), o_acc[db][hb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int k = 0; k < kSoftSteps; ++k) soft_step(k, s_acc, sc, pb, psum);
+            __builtin_amdgcn_sched_barrier(0);
+            pv(tile(0), pb, [](int) {});
         }
+    } else {
+        // bf16 storage, software-pipelined: iteration `it` scores tile it, then multiplies the
+        // probabilities of tile it-1 with its rows while tile it's softmax runs in between
+        // the matrix instructions. Tiles it-1 and it are in use and tiles it+1 and it+2 are
+        // in flight (kBuffers = 4). The only vector-memory operations inside the loop are the
+        // tile loads, so tile it has landed once only tile it+1's loads remain.
+        constexpr int kAh = 2;
+        static_assert(NB >= kAh + 2, "tile ring too small for the pipeline");
+#pragma unroll
+        for (int j = 0; j < kAh; ++j)
+            if (j < ntiles) gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
+        // One PV instance for every iteration, so that O stays in the same registers
+        // throughout: iteration 0 has no previous tile (its softmax runs on its own), and the
+        // extra last iteration scores nothing (all its keys are masked, p = 0) while it
+        // multiplies the last tile.
+        u32x4 pb_prev[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) pb_prev[hb] = u32x4{0, 0, 0, 0};
+        SA_LDS const uint8_t* prev = tiles;
+        for (int it = 0; it <= ntiles; ++it) {
+            SA_LDS uint8_t* cur = tile(it % NB);
+            uint32_t valid = 0;
+            f32x4 s_acc[2][HPW];
+            if (it < ntiles) {
+                SA_LDS const int32_t* tidx = istage + it * kTileKeys;
+                valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
+                if (it + 1 < ntiles) wait_vmcnt<PP::kLoadsPerWave>();
+                else wait_vmcnt<0>();
+                if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
+                lds_barrier();             // tile it visible to all; buffer of tile it-2 free
+                if (it + kAh < ntiles)
+                    gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
+                pin_offsets();
+                qk(cur, s_acc);
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const float sc = prepare(s_acc, valid);
+            u32x4 pb[HPW];
+            float psum[HPW];
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) psum[hb] = 0.0f;
+            auto hook = [&](int k) { soft_step(k, s_acc, sc, pb, psum); };
+            if (it > 0) {
+                pin_offsets();
+                pv(prev, pb_prev, hook);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kSoftSteps; ++k) hook(k);
+            }
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) pb_prev[hb] = pb[hb];
+            prev = cur;
+        }
+    }
+    if (cs_g != nullptr) {
+#pragma unroll
+        for (int u = 0; u < kCsPer; ++u)
+            if (tid + u * NW * kWave < p.rope_dim) cs_lds[tid + u * NW * kWave] = cs_v[u];
     }
     // A score ran more than kSlack above its head's reference (rare): run the key loop again
     // against the maximum of all scores, which every wave has tracked for its heads.
+    if (__ballot(over) != 0 && lane == 0) *redo = 1;
     __syncthreads();
     const int again = *redo;
     if (pass > 0 || again == 0) break;
@@ -653,6 +718,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
     }
     have_ref = true;
+    over = false;
 #pragma unroll
     for (int b = 0; b < G::kDBlocks; ++b)
 #pragma unroll
@@ -668,20 +734,38 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
     // O^T accumulator layout: lane holds head head_of(hb), d = 16*db + 4*q4 + (0..3)
     if (p.splits == 1) {
-        // the position's (cos, sin) row was staged in LDS at start-up (visible since the
-        // barrier after the key loop), so the stores below never wait on table loads
+        // The rows go out through LDS: each lane's 4-element pieces (which lie 16 heads x 4
+        // lane groups apart) are written to a per-wave staging block of 16 head rows, read back
+        // a whole row per instruction and stored to HBM as full, contiguous rows. The tile
+        // buffers are free once the key loop is done (a barrier ends it). Rows carry 16 bytes
+        // of padding so that both the 8-byte writes and the 16-byte reads are free of bank
+        // conflicts. The position's (cos, sin) row was staged in LDS at start-up.
+        constexpr int kOutStride = 2 * D + 16;                      // bytes per staged row
+        constexpr int kLanesPerRow = 2 * D / 16;                    // 16-byte pieces per row
+        constexpr int kRowsPerRead = kWave / kLanesPerRow;
+        SA_LDS uint8_t* ob = tiles + wid * (kHeadsPerWave * kOutStride);
         const int r0 = D - p.rope_dim;
+        const int wave_head0 = head0 - l16;                         // first head of block 0
+        const int prow = lane / kLanesPerRow, pcol = lane % kLanesPerRow;
+        uint16_t* out_q = p.out + (int64_t)seq * p.out_seq_stride + (int64_t)t * p.h * D;
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
-            if (head_of(hb) >= p.h) continue;
             const float inv_l = l_tot[hb] > 0.0f ? 1.0f / l_tot[hb] : 0.0f;
-            uint16_t* orow = p.out + (int64_t)seq * p.out_seq_stride + ((int64_t)t * p.h + head_of(hb)) * D;
 #pragma unroll
             for (int db = 0; db < G::kDBlocks; ++db) {
                 const int d0 = 16 * db + 4 * q4;
                 const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
-                *(u32x2*)(orow + d0) = epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2],
-                                                 o_acc[db][hb][3], inv_l, rot, d0, r0, (SA_LDS const float*)cs_lds);
+                *(SA_LDS u32x2*)(ob + l16 * kOutStride + 2 * d0) =
+                    epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2], o_acc[db][hb][3], inv_l,
+                              rot, d0, r0, (SA_LDS const float*)cs_lds);
+            }
+            // the wave's own LDS writes complete in order before its reads below
+#pragma unroll
+            for (int j = 0; j < kHeadsPerWave / kRowsPerRead; ++j) {
+                const int hr = j * kRowsPerRead + prow;
+                const u32x4 v = *(SA_LDS const u32x4*)(ob + hr * kOutStride + 16 * pcol);
+                const int head = wave_head0 + hb * kHeadsPerWave + hr;
+                if (head < p.h) *(u32x4*)(out_q + (int64_t)head * D + 8 * pcol) = v;
             }
         }
     } else {
@@ -704,8 +788,11 @@ template <int D, bool FP8, int NW, int HPW = 1>
 inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
     constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
-    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)D * 4 + (size_t)NB * G::kTileBytes +
-                       (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
+    // after the tile buffers (and the fp8 staging tiles) the region must also hold the
+    // epilogue's 16 padded output rows per wave
+    constexpr size_t kTiles = (size_t)NB * G::kTileBytes + (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
+    constexpr size_t kOut = (size_t)NW * kHeadsPerWave * (2 * D + 16);
+    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)D * 4 + (kTiles > kOut ? kTiles : kOut);
     auto k = attn_fwd_kernel<D, FP8, NW, HPW>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
