@@ -56,32 +56,35 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
 
 // ------------------------------------------------------------------ launch
 template <int D, bool FP8>
-static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int blocks, hipStream_t st) {
+static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int kg, int blocks, hipStream_t st) {
     if constexpr (D == 512 && !FP8) {
-        if (hpw == 2) return nw == 4 ? launch_fwd_wide(p, blocks, st) : hipErrorInvalidValue;
+        if (hpw == 2) return nw == 4 && kg == 1 ? launch_fwd_wide(p, blocks, st) : hipErrorInvalidValue;
+        if (kg == 2) return nw == 4 && hpw == 1 ? launch_fwd<D, FP8, 4, 1, 2>(p, blocks, st) : hipErrorInvalidValue;
+        if (kg == 4) return nw == 4 && hpw == 1 ? launch_fwd<D, FP8, 4, 1, 4>(p, blocks, st) : hipErrorInvalidValue;
     }
-    if (hpw != 1) return hipErrorInvalidValue;
+    if (hpw != 1 || kg != 1) return hipErrorInvalidValue;
     if (nw == 1) return launch_fwd<D, FP8, 1>(p, blocks, st);
     if (nw == 2) return launch_fwd<D, FP8, 2>(p, blocks, st);
     return launch_fwd<D, FP8, 4>(p, blocks, st);
 }
 
 template <int D>
-static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int blocks, hipStream_t st) {
-    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, blocks, st) : launch_fwd_nw<D, false>(p, nw, hpw, blocks, st);
+static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int kg, int blocks, hipStream_t st) {
+    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, kg, blocks, st)
+                       : launch_fwd_nw<D, false>(p, nw, hpw, kg, blocks, st);
     if (e != hipSuccess || p.splits == 1) return e;
     const int waves = p.b * p.s * p.h;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((waves + 3) / 4), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, hipStream_t st) {
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st) {
     const int blocks = p.b * p.s * p.head_blocks * p.splits;
     switch (p.d) {
-        case 64: return launch_all<64>(p, fp8, nw, hpw, blocks, st);
-        case 128: return launch_all<128>(p, fp8, nw, hpw, blocks, st);
-        case 256: return launch_all<256>(p, fp8, nw, hpw, blocks, st);
-        case 512: return launch_all<512>(p, fp8, nw, hpw, blocks, st);
+        case 64: return launch_all<64>(p, fp8, nw, hpw, kg, blocks, st);
+        case 128: return launch_all<128>(p, fp8, nw, hpw, kg, blocks, st);
+        case 256: return launch_all<256>(p, fp8, nw, hpw, kg, blocks, st);
+        case 512: return launch_all<512>(p, fp8, nw, hpw, kg, blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -294,8 +294,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int D, bool FP8, int NW, int HPW>
+// KG key groups: the NW waves form NW / KG head groups times KG key groups; the waves of
+// one key group take every KG-th tile of the item's index columns, so one query's keys are
+// worked on by KG waves side by side, and their partial results are merged in LDS at the
+// end (KG = 1: every wave takes every tile, for its own heads).
+template <int D, bool FP8, int NW, int HPW, int KG = 1>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
+    static_assert(KG == 1 || (!FP8 && NW % KG == 0), "key groups need bf16 storage");
+    constexpr int HB = NW / KG;                 // head groups of the workgroup
     using G = Geo<D>;
     using PP = Pipe<D, NW>;
     constexpr int NB = FP8 ? 1 : PP::kBuffers;
@@ -314,6 +320,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int tid = threadIdx.x;
     const int wid = tid / kWave;
     const int lane = tid % kWave;
+    const int kg = wid / HB;                    // this wave's key group
+    const int hbw = wid % HB;                   // and head group
     const int l16 = lane & 15;                  // this lane's head within a 16-head block
     const int q4 = lane >> 4;                   // lane group 0..3
     // d chunk (8 elements) that lane group q4 takes in each 32-wide step of the QK product:
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     const int t = qi % p.s;
 
     // the wave's HPW blocks of 16 heads: head(hb) = head0 + 16*hb + l16
-    const int head0 = (hblk * NW + wid) * HPW * kHeadsPerWave + l16;
+    const int head0 = (hblk * HB + hbw) * HPW * kHeadsPerWave + l16;
     auto head_of = [&](int hb) { return head0 + hb * kHeadsPerWave; };
 
     const int32_t* idx_row = p.idx + (int64_t)seq * p.idx_seq_stride + (int64_t)t * p.topk;
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // loop then runs once more with m_ref = the maximum of every score seen (which no score
     // can exceed), a rare second pass instead of a rescale on every tile.
     constexpr float kSlack = 32.0f;
-    const bool sink_lane = q4 == 0 && split == 0;             // the sink counts once per head
+    const bool sink_lane = q4 == 0 && split == 0 && kg == 0;  // the sink counts once per head
     float m_ref[HPW], m_seen[HPW], l_run[HPW];                 // log2 domain, per head
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
@@ -642,6 +650,62 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             __builtin_amdgcn_sched_barrier(0);
             pv(tile(0), pb, [](int) {});
         }
+    } else if constexpr (KG > 1) {
+        // Key groups: the tile ring holds NS groups of KG tiles ("super tiles"); all waves
+        // gather every tile, the waves of key group g work on tile s*KG + g of super tile s.
+        // With two super tiles in the ring the next one is gathered while the current one is
+        // worked on; with one, after it (a barrier in between).
+        constexpr int NS = NB / KG;
+        static_assert(NS >= 1, "tile ring too small for the key groups");
+        const int nsuper = (ntiles + KG - 1) / KG;
+        auto gather_super = [&](int su) {
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                const int ti = su * KG + g;
+                if (ti < ntiles)
+                    gather_tile_bf16<D, NW>(kv_rsrc, istage + ti * kTileKeys, tile((su % NS) * KG + g), wid, lane);
+            }
+        };
+        if (nsuper > 0) gather_super(0);
+        for (int su = 0; su < nsuper; ++su) {
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                const int ti = su * KG + g;
+                if (ti < ntiles) {
+                    SA_LDS const int32_t* tix = istage + ti * kTileKeys;
+                    const uint32_t v = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
+                    if (v != 0 && v != 0xffffffffu) zero_skipped_rows<D, NW>(tix, tile((su % NS) * KG + g), wid, lane);
+                }
+            }
+            lds_barrier();                 // super tile su visible to all
+            if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
+            const int ti = su * KG + kg;
+            uint32_t valid = 0;
+            if (ti < ntiles) {
+                SA_LDS const int32_t* tix = istage + ti * kTileKeys;
+                valid = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
+            }
+            if (valid != 0) {
+                SA_LDS const uint8_t* cur = tile((su % NS) * KG + kg);
+                pin_offsets();
+                f32x4 s_acc[2][HPW];
+                qk(cur, s_acc);
+                const float sc = prepare(s_acc, valid);
+                u32x4 pb[HPW];
+                float psum[HPW];
+#pragma unroll
+                for (int hb = 0; hb < HPW; ++hb) psum[hb] = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kSoftSteps; ++k) soft_step(k, s_acc, sc, pb, psum);
+                __builtin_amdgcn_sched_barrier(0);
+                pv(cur, pb, [](int) {});
+            }
+            if (NS == 1 && su + 1 < nsuper) {
+                lds_barrier();             // every wave is done with the super tile
+                gather_super(su + 1);
+            }
+        }
     } else {
         // bf16 storage, software-pipelined: iteration `it` scores tile it, then multiplies the
         // probabilities of tile it-1 with its rows while tile it's softmax runs in between
@@ -732,6 +796,58 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     float l_tot[HPW];
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
+    if constexpr (KG > 1) {
+        // Merge the key groups into group 0: m = max m_g, O = sum O_g 2^(m_g - m),
+        // l = sum l_g 2^(m_g - m). Groups 1.. leave O (accumulator layout, 16 bytes per lane
+        // and slice) and (m, l) in LDS behind the epilogue's output staging area; the tile
+        // buffers are free (a barrier ended the key loop).
+        constexpr int kSlotO = HPW * G::kDBlocks * kWave * 16;
+        constexpr int kSlot = kSlotO + HPW * kWave * 8;
+        SA_LDS uint8_t* mrg = tiles + HB * kHeadsPerWave * (2 * D + 16);
+        if (kg > 0) {
+            SA_LDS uint8_t* slot = mrg + ((kg - 1) * HB + hbw) * kSlot;
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) {
+#pragma unroll
+                for (int db = 0; db < G::kDBlocks; ++db)
+                    *(SA_LDS f32x4*)(slot + ((hb * G::kDBlocks + db) * kWave + lane) * 16) = o_acc[db][hb];
+                *(SA_LDS f32x2*)(slot + kSlotO + (hb * kWave + lane) * 8) = f32x2{m_ref[hb], l_tot[hb]};
+            }
+        }
+        __syncthreads();
+        if (kg > 0) return;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            float mg[KG], lg[KG];
+            mg[0] = m_ref[hb];
+            lg[0] = l_tot[hb];
+#pragma unroll
+            for (int g = 1; g < KG; ++g) {
+                const f32x2 ml = *(SA_LDS const f32x2*)(mrg + ((g - 1) * HB + hbw) * kSlot + kSlotO + (hb * kWave + lane) * 8);
+                mg[g] = ml[0];
+                lg[g] = ml[1];
+            }
+            float m = mg[0];
+#pragma unroll
+            for (int g = 1; g < KG; ++g) m = fmaxf(m, mg[g]);
+            float wg[KG], l = 0.0f;
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                wg[g] = mg[g] == -INFINITY ? 0.0f : fast_exp2(mg[g] - m);   // no row and no sink
+                l += lg[g] * wg[g];
+            }
+#pragma unroll
+            for (int db = 0; db < G::kDBlocks; ++db) {
+                f32x4 o = o_acc[db][hb] * wg[0];
+#pragma unroll
+                for (int g = 1; g < KG; ++g)
+                    o += *(SA_LDS const f32x4*)(mrg + ((g - 1) * HB + hbw) * kSlot + ((hb * G::kDBlocks + db) * kWave + lane) * 16) * wg[g];
+                o_acc[db][hb] = o;
+            }
+            m_ref[hb] = m;
+            l_tot[hb] = l;
+        }
+    }
     // O^T accumulator layout: lane holds head head_of(hb), d = 16*db + 4*q4 + (0..3)
     if (p.splits == 1) {
         // The rows go out through LDS: each lane's 4-element pieces (which lie 16 heads x 4
@@ -784,7 +900,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     }
 }
 
-template <int D, bool FP8, int NW, int HPW = 1>
+template <int D, bool FP8, int NW, int HPW = 1, int KG = 1>
 inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
     constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
@@ -793,7 +909,11 @@ inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     constexpr size_t kTiles = (size_t)NB * G::kTileBytes + (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
     constexpr size_t kOut = (size_t)NW * kHeadsPerWave * (2 * D + 16);
     const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)D * 4 + (kTiles > kOut ? kTiles : kOut);
-    auto k = attn_fwd_kernel<D, FP8, NW, HPW>;
+    // the key-group merge slots sit behind the output staging area
+    static_assert(KG == 1 || (size_t)(NW / KG) * kHeadsPerWave * (2 * D + 16) +
+                                 (size_t)(KG - 1) * (NW / KG) * (HPW * G::kDBlocks * kWave * 16 + HPW * kWave * 8) <= kTiles,
+                  "key-group merge does not fit the tile region");
+    auto k = attn_fwd_kernel<D, FP8, NW, HPW, KG>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(NW * kWave), lds, st, p);

@@ -37,6 +37,7 @@ struct KParams {
 struct Plan {
     int nw;             // waves per workgroup
     int hpw;            // blocks of 16 heads per wave (1, or 2 for wide bf16 d = 512 work)
+    int kg;             // key groups: waves that share a query's heads and split its tiles
     int head_blocks;
     int h_pad;
     int splits;
@@ -44,7 +45,7 @@ struct Plan {
     size_t ws_bytes;
 };
 
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, hipStream_t st);
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st);
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
                               hipStream_t st);

@@ -242,18 +242,49 @@ def test_late_large_scores(sa, boost, where, fmt):
     assert_close(u16(out).reshape(-1, 16, 64), ref, f"late large {boost} {where} {fmt}")
 
 
-def test_late_large_scores_across_splits(sa):
-    """A decode-shaped problem that the planner splits: the large score sits in a later split."""
-    q, kv, sink, idx = W.rand_problem(52, 2, 1, 64, 512, 1200, 1024, 0.0, False)
-    for b in range(2):
-        row = int(idx[b, 0, 900])
+@pytest.mark.parametrize("d,plan", [(512, "key groups"), (256, "splits")])
+def test_late_large_scores_across_splits(sa, d, plan):
+    """A decode-shaped problem with few queries: at d = 512 the waves of a workgroup split the
+    tiles between key groups (merged in LDS), at other widths the planner splits them across
+    workgroups (f32 partials and a combine kernel). Large late scores sit in tiles of
+    different groups or splits, so the second key pass and the merge meet."""
+    _say("late large across", d, plan)
+    q, kv, sink, idx = W.rand_problem(52, 2, 1, 64, d, 1200, 1024, 0.0, False)
+    for b, col in ((0, 900), (1, 950)):
+        row = int(idx[b, 0, col])
         kv[b, row] = (q[b, 0, 5].float() * 2.0).to(torch.bfloat16)
-    scale = float(np.float32(512 ** -0.5))
+    scale = float(np.float32(d ** -0.5))
     args = sa.make_args(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
-    assert sa.sparse_attn_workspace_bytes(args) > 0, "expected a split plan"
+    ws = sa.sparse_attn_workspace_bytes(args)
+    assert (ws > 0) == (plan == "splits"), f"expected a plan with {plan}"
     out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
     ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
-    assert_close(u16(out).reshape(-1, 64, 512), ref, "late large split")
+    assert_close(u16(out).reshape(-1, 64, d), ref, f"late large {plan}")
+
+
+@pytest.mark.parametrize("seed,b,h,topk,hole", [
+    (71, 40, 128, 600, 0.1),     # 40 queries x 128 heads: two key groups of 32 heads
+    (72, 30, 96, 700, 0.05),     # four key groups of 16 heads; 22 tiles, the last super tile half full
+    (73, 6, 64, 520, 0.3),       # four key groups; 17 tiles, three groups idle in the last super tile
+])
+def test_key_groups(sa, seed, b, h, topk, hole):
+    """Decode-shaped problems (one query per sequence, d = 512) with long key lists and few
+    queries, which the planner gives to key groups (the waves of a workgroup share out each
+    query's tiles) instead of splits; ragged tile counts leave groups idle at the end, and a
+    query whose list names nothing leaves every group empty."""
+    _say("key groups", seed, b, h, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, 1, h, 512, 400, topk, hole, False)
+    idx[b // 2, 0] = -1
+    scale = float(np.float32(512 ** -0.5))
+    args = sa.make_args(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
+    assert sa.sparse_attn_workspace_bytes(args) == 0
+    for sk in (sink, torch.full_like(sink, -math.inf)):
+        out = sa.sparse_attn(q.cuda(), kv.cuda(), sk.cuda(), idx.cuda(), scale)
+        o = out.float().cpu()
+        assert torch.isfinite(o).all()
+        assert torch.all(o[b // 2] == 0) or sk[0] != -math.inf
+        ref = oracle.sparse_attn(u16(q), u16(kv), sk.numpy(), idx.numpy(), scale)
+        assert_close(u16(out).reshape(-1, h, 512), ref, f"key groups {seed}")
 
 
 def test_empty_lists_and_no_sink(sa):
