@@ -156,11 +156,20 @@ def time_kernel(sets, calls: int):
     all first (so no host gap lands inside the interval). Returns (mean ms, mean ms of the
     fastest of 5 such batches)."""
     st = torch.cuda.current_stream()
+    # the spin must outlast the host's enqueueing of the whole batch (slower under a kernel
+    # tracer): time one batch's enqueueing first and spin for twice that, at least 5 ms
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        sets[i % len(sets)].attend()
+    enqueue_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    spin_s = max(0.005, 2.0 * enqueue_s)
     per = []
     for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        torch.cuda._sleep(int(2.4e9 * 0.005))        # ~5 ms spin while the host enqueues
+        torch.cuda._sleep(int(2.4e9 * spin_s))       # GPU spin while the host enqueues
         e0.record(st)
         for i in range(calls):
             sets[i % len(sets)].attend()
