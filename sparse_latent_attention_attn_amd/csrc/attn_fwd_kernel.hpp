@@ -854,34 +854,56 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         // lane groups apart) are written to a per-wave staging block of 16 head rows, read back
         // a whole row per instruction and stored to HBM as full, contiguous rows. The tile
         // buffers are free once the key loop is done (a barrier ends it). Rows carry 16 bytes
-        // of padding so that both the 8-byte writes and the 16-byte reads are free of bank
-        // conflicts. The position's (cos, sin) row was staged in LDS at start-up.
+        // of padding so that the 8-byte writes, the 16-byte reads and the rotation's 4-byte
+        // accesses are free of bank conflicts. The position's (cos, sin) row was staged in LDS
+        // at start-up.
+        // This code runs once per workgroup, so its instructions are fetched cold: it is kept
+        // short and nearly free of branches (the rotation is a small loop over the staged rows
+        // rather than a test in every slice of d, and the stores take one uniform branch).
         constexpr int kOutStride = 2 * D + 16;                      // bytes per staged row
         constexpr int kLanesPerRow = 2 * D / 16;                    // 16-byte pieces per row
         constexpr int kRowsPerRead = kWave / kLanesPerRow;
+        constexpr int kReads = kHeadsPerWave / kRowsPerRead;
         SA_LDS uint8_t* ob = tiles + wid * (kHeadsPerWave * kOutStride);
         const int r0 = D - p.rope_dim;
         const int wave_head0 = head0 - l16;                         // first head of block 0
         const int prow = lane / kLanesPerRow, pcol = lane % kLanesPerRow;
         uint16_t* out_q = p.out + (int64_t)seq * p.out_seq_stride + (int64_t)t * p.h * D;
+        // inverse RoPE: lane takes row lane / 4 and its pairs lane % 4, +4, ... of the last
+        // rope_dim elements (apply_rotary_emb with inverse=True: the bf16 pair times the
+        // conjugate of (cos, sin) in f32, back to bf16)
+        SA_LDS uint8_t* rot_row = ob + (lane >> 2) * kOutStride + 2 * r0;
+        const int rot_pairs = cs_g != nullptr ? p.rope_dim / 2 : 0;
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
             const float inv_l = l_tot[hb] > 0.0f ? 1.0f / l_tot[hb] : 0.0f;
 #pragma unroll
             for (int db = 0; db < G::kDBlocks; ++db) {
-                const int d0 = 16 * db + 4 * q4;
-                const bool rot = cs_g != nullptr && 16 * db + 16 > r0;  // slice meets the rope tail
-                *(SA_LDS u32x2*)(ob + l16 * kOutStride + 2 * d0) =
-                    epilogue4(o_acc[db][hb][0], o_acc[db][hb][1], o_acc[db][hb][2], o_acc[db][hb][3], inv_l,
-                              rot, d0, r0, (SA_LDS const float*)cs_lds);
+                const f32x4 o = o_acc[db][hb] * inv_l;
+                *(SA_LDS u32x2*)(ob + l16 * kOutStride + 2 * (16 * db + 4 * q4)) =
+                    u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             }
-            // the wave's own LDS writes complete in order before its reads below
+            // the wave's own LDS accesses complete in order: no barrier between the phases
+            for (int i = lane & 3; i < rot_pairs; i += 4) {
+                SA_LDS uint32_t* e = (SA_LDS uint32_t*)(rot_row + 4 * i);
+                const f32x2 cs = *(SA_LDS const f32x2*)(cs_lds + 2 * i);
+                const uint32_t w = *e;
+                const float x = bf16_lo(w), y = bf16_hi(w);
+                *e = pack_bf16x2(x * cs[0] + y * cs[1], y * cs[0] - x * cs[1]);
+            }
+            u32x4 v[kReads];
 #pragma unroll
-            for (int j = 0; j < kHeadsPerWave / kRowsPerRead; ++j) {
-                const int hr = j * kRowsPerRead + prow;
-                const u32x4 v = *(SA_LDS const u32x4*)(ob + hr * kOutStride + 16 * pcol);
-                const int head = wave_head0 + hb * kHeadsPerWave + hr;
-                if (head < p.h) *(u32x4*)(out_q + (int64_t)head * D + 8 * pcol) = v;
+            for (int j = 0; j < kReads; ++j)
+                v[j] = *(SA_LDS const u32x4*)(ob + (j * kRowsPerRead + prow) * kOutStride + 16 * pcol);
+            const int hrow0 = wave_head0 + hb * kHeadsPerWave;
+            uint16_t* orow = out_q + (int64_t)(hrow0 + prow) * D + 8 * pcol;
+            if (hrow0 + kHeadsPerWave <= p.h) {
+#pragma unroll
+                for (int j = 0; j < kReads; ++j) *(u32x4*)(orow + (int64_t)j * kRowsPerRead * D) = v[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < kReads; ++j)
+                    if (hrow0 + j * kRowsPerRead + prow < p.h) *(u32x4*)(orow + (int64_t)j * kRowsPerRead * D) = v[j];
             }
         }
     } else {
