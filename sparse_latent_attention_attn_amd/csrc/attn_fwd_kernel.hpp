@@ -205,6 +205,36 @@ __device__ __forceinline__ void convert_tile_fp8(SA_LDS const uint8_t* raw, SA_L
     }
 }
 
+// Score product step with the accumulator in VGPRs: acc (+)= A . B on
+// v_mfma_f32_16x16x32_bf16. Written as inline assembly because the compiler picks one
+// register class for every MFMA accumulator of a kernel: with O in AGPRs (the kernels that
+// hold 32 heads per wave need all 256 of them for O) it would give the scores AGPRs too and
+// move part of O in and out of VGPRs around every tile. The compiler does not see these as
+// matrix instructions, so the hazards it would otherwise handle are handled here:
+//   * the A and B operands come from LDS (waits on its counter, which the compiler inserts
+//     for the asm inputs) or are Q, held in VGPRs since start-up: no vector instruction
+//     writes them just ahead (checked on the compiled code of the kernel that uses this);
+//   * back-to-back steps on the same accumulator (same opcode, same registers) need no wait
+//     states;
+//   * vector instructions read the result only after mfma_v_drain, which waits out the
+//     pipeline (an 8-pass matrix instruction needs 11 wait states before a vector read or
+//     write of its result; 24 are given) and is tied to every accumulator, so that no read
+//     can be scheduled ahead of it.
+__device__ __forceinline__ void mfma_vz(f32x4& acc, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x4& acc, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+template <int N>
+__device__ __forceinline__ void mfma_v_drain(f32x4 (&acc)[2][N]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < N; ++n) asm volatile("" : "+v"(acc[m][n]));
+}
+
 // Epilogue for 4 consecutive output elements d0..d0+3 of one head: o = acc * inv_l rounded
 // to bf16; with `rot`, the inverse rotation of the pairs that fall in the last rope_dim
 // elements (apply_rotary_emb with inverse=True: multiply by the conjugate in f32, back to
@@ -481,11 +511,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // QK: S^T = K . Q^T over the tile's two 16-key blocks. K operands are read kPre steps
     // ahead of their multiply; scheduling fences keep the compiler from hoisting every read of
     // the unrolled loop.
+    // With two head blocks per wave O takes all 256 AGPRs (that kernel's accumulators live in
+    // AGPRs): the score accumulators are then kept in VGPRs by writing the score product in
+    // assembly (mfma_v). With one head block every accumulator is a VGPR already.
+    constexpr bool kScoresInVgprs = HPW == 2;
     auto qk = [&](SA_LDS const uint8_t* cur, f32x4 (&s_acc)[2][HPW]) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int kPre = G::kKSteps < 3 ? G::kKSteps : 3;
         u32x4 a0[kPre], a1[kPre];
 #pragma unroll
@@ -503,12 +533,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             }
 #pragma unroll
             for (int hb = 0; hb < HPW; ++hb) {
-                const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
-                s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, s_acc[0][hb], 0, 0, 0);
-                s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, s_acc[1][hb], 0, 0, 0);
+                if constexpr (kScoresInVgprs) {
+                    if (kk == 0) {
+                        mfma_vz(s_acc[0][hb], c0, qreg[hb][kk]);
+                        mfma_vz(s_acc[1][hb], c1, qreg[hb][kk]);
+                    } else {
+                        mfma_v(s_acc[0][hb], c0, qreg[hb][kk]);
+                        mfma_v(s_acc[1][hb], c1, qreg[hb][kk]);
+                    }
+                } else {
+                    // the first step starts from a zero accumulator (an inline constant)
+                    const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[hb][kk]);
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    s_acc[0][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c0), qb, kk == 0 ? z : s_acc[0][hb], 0, 0, 0);
+                    s_acc[1][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, c1), qb, kk == 0 ? z : s_acc[1][hb], 0, 0, 0);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the scores are read by vector instructions next: wait out the matrix pipeline
+        if constexpr (kScoresInVgprs) mfma_v_drain(s_acc);
     };
 
     // Softmax, part 1 (log2 domain; this lane: head l16 of each block, keys 16*mb + 4*q4 + r;
