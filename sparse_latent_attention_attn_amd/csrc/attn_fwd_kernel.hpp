@@ -347,6 +347,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
     auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
 
+    // The kernel arguments that start-up needs, all at once: scalar loads complete out of
+    // order, so the compiler can only wait for all of them, and loads placed next to their
+    // uses would cost one memory round trip per group before the first vector load issues.
+    asm volatile("" ::"s"(p.q), "s"(p.q_seq_stride), "s"(p.idx), "s"(p.idx_seq_stride), "s"(p.pos),
+                 "s"(p.pos_seq_stride), "s"(p.sink), "s"(p.kv), "s"(p.kv_seq_stride_bytes), "s"(p.b),
+                 "s"(p.s), "s"(p.h), "s"(p.topk), "s"(p.kv_rows), "s"(p.rope_dim), "s"(p.splits),
+                 "s"(p.cols_per_split), "s"(p.head_blocks));
     const int tid = threadIdx.x;
     const int wid = tid / kWave;
     const int lane = tid % kWave;
