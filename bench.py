@@ -47,8 +47,12 @@ DECODE = {"decode_window", "decode_compress"}
 
 
 # ------------------------------------------------------------------ algorithmic work
-def algorithmic(w: W.Workload, idx: np.ndarray, kv_format: str):
-    """Bytes the method must move and flops it must do for one step."""
+def algorithmic(w: W.Workload, idx: np.ndarray, kv_format: str, epilogue: bool = True):
+    """Bytes the method must move and flops it must do for one step: q, out, the index
+    lists, the sink, and every distinct KV row a sequence's lists name, once, in its storage
+    format (1024 B per bf16 row at d 512, 528 B per fp8 row with its scales); with the
+    epilogue also the positions and their (cos, sin) rows. Flops: 4 h d per valid (query,
+    index) pair."""
     row_bytes = w.d * 2 if kv_format == "bf16" else w.d + w.d // 32
     distinct = 0
     valid_pairs = 0
@@ -60,7 +64,7 @@ def algorithmic(w: W.Workload, idx: np.ndarray, kv_format: str):
     nq = w.b * w.s
     qo_bytes = 2 * nq * w.h * w.d * 2
     idx_bytes = nq * w.topk * 4
-    small = w.h * 4 + nq * 4 + nq * (w.rd // 2) * 8          # sink, positions, rope rows
+    small = w.h * 4 + (nq * 4 + nq * (w.rd // 2) * 8 if epilogue else 0)   # sink, positions, rope rows
     attn_bytes = kv_bytes + qo_bytes + idx_bytes + small
     flops = 4.0 * w.h * w.d * valid_pairs
     return dict(kv_bytes=kv_bytes, attn_bytes=attn_bytes, flops=flops, valid_pairs=valid_pairs,
@@ -71,7 +75,8 @@ def algorithmic(w: W.Workload, idx: np.ndarray, kv_format: str):
 class Step:
     """One input set on the device and the library calls of one step."""
 
-    def __init__(self, w, q, kv, kv_scale, sink, idx, pos, table, start_pos, ws):
+    def __init__(self, w, q, kv, kv_scale, sink, idx, pos, table, start_pos, ws, epilogue=True):
+        self.epilogue = epilogue
         self.w, self.q, self.kv, self.kv_scale, self.sink = w, q, kv, kv_scale, sink
         self.idx, self.pos, self.table, self.start_pos, self.ws = idx, pos, table, start_pos, ws
         self.out = torch.empty_like(q)
@@ -84,14 +89,15 @@ class Step:
 
     def attend(self):
         sa.sparse_attn(self.q, self.kv, self.sink, self.idx, self.w.scale, out=self.out,
-                       kv_scale=self.kv_scale, rope=(self.table, self.pos), workspace=self.ws)
+                       kv_scale=self.kv_scale, rope=(self.table, self.pos) if self.epilogue else None,
+                       workspace=self.ws)
 
     def run(self):
         self.window()
         self.attend()
 
 
-def make_sets(w: W.Workload, kv_format: str, touched_bytes: int, dev):
+def make_sets(w: W.Workload, kv_format: str, touched_bytes: int, dev, epilogue: bool = True):
     """Set 0 from the seeded draws; the other sets are device copies of it at distinct
     addresses (same values, so every set computes the same result)."""
     q0 = w.q.to(dev)
@@ -117,7 +123,7 @@ def make_sets(w: W.Workload, kv_format: str, touched_bytes: int, dev):
     for k in range(nsets):
         c = (lambda t: t) if k == 0 else (lambda t: None if t is None else t.clone())
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
-        sets.append(Step(w, c(q0), c(kv0), c(scales0), sink, c(idx0), c(pos0), table, c(sp0), ws))
+        sets.append(Step(w, c(q0), c(kv0), c(scales0), sink, c(idx0), c(pos0), table, c(sp0), ws, epilogue))
     return sets
 
 
@@ -179,7 +185,7 @@ def time_kernel(sets, calls: int):
     return float(np.mean(per)), float(np.min(per))
 
 
-def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0):
+def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0, rope: bool = True):
     """The oracle (plain C, OpenMP over queries) on a bounded sample of queries, scaled to
     the metric's unit."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -189,7 +195,7 @@ def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0):
     threads = oracle.max_threads()
     # per-query cost estimate from one query, then a sample sized to the budget
     t0 = time.perf_counter()
-    oracle_run(w, qsel=np.array([nq - 1]), rope=True, round_trip=w.kv_roundtrip, nthreads=1)
+    oracle_run(w, qsel=np.array([nq - 1]), rope=rope, round_trip=w.kv_roundtrip, nthreads=1)
     one = time.perf_counter() - t0
     n = int(max(1, min(nq, budget_s * threads / max(one, 1e-6))))
     sel = np.linspace(0, nq - 1, n).round().astype(np.int64)
@@ -198,7 +204,7 @@ def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0):
     reps = 1
     t0 = time.perf_counter()
     while True:
-        oracle_run(w, qsel=sel, rope=True, round_trip=w.kv_roundtrip, nthreads=threads)
+        oracle_run(w, qsel=sel, rope=rope, round_trip=w.kv_roundtrip, nthreads=threads)
         dt = time.perf_counter() - t0
         if sel.size < nq or dt >= 2.0 or reps >= 100:
             break
@@ -210,7 +216,7 @@ def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0):
         value, unit = alg["flops"] / per_step / 1e12, "TFLOP/s"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
             "sample": f"{sel.size} of {nq} queries (all heads) x {reps} run(s), oracle incl. "
-                      f"fp8 round trip of their rows, window lists and inverse RoPE; {dt:.1f} s "
+                      f"fp8 round trip of their rows, window lists{' and inverse RoPE' if rope else ''}; {dt:.1f} s "
                       f"wall, scaled to one step"}
 
 
@@ -307,6 +313,8 @@ def main():
     ap.add_argument("--workload", default="decode_window", choices=sorted(W.WORKLOADS))
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-epilogue", action="store_true",
+                    help="time sparse_attn without the inverse-RoPE epilogue (plain bf16 output)")
     ap.add_argument("--profile-calls", type=int, default=0,
                     help="counter-collection mode: N eager steps over the input sets, then "
                          "the copy kernel of known size that calibrates the byte counters; "
@@ -320,7 +328,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sparse_attn shards over heads with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(sparse_attn would shard over heads with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -335,10 +343,10 @@ def main():
                         start_pos=None if w.win_start_pos is None else w.win_start_pos.to(dev), out=view)
     if w.comp_idx is not None:
         probe_idx[:, :, w.win_cols:] = w.comp_idx.to(dev)
-    alg = algorithmic(w, probe_idx.cpu().numpy(), args.kv)
+    alg = algorithmic(w, probe_idx.cpu().numpy(), args.kv, epilogue=not args.no_epilogue)
     del probe_idx
 
-    sets = make_sets(w, args.kv, alg["attn_bytes"], dev)
+    sets = make_sets(w, args.kv, alg["attn_bytes"], dev, epilogue=not args.no_epilogue)
     if args.profile_calls:
         profile_pass(sets, args.profile_calls, dev)
         return
@@ -367,7 +375,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.kv, alg)
+        cpu = cpu_baseline(w, args.kv, alg, rope=not args.no_epilogue)
 
     rec = {
         "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": timed_steps,
@@ -376,7 +384,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.b, "queries_per_sequence": w.s, "heads": w.h,
                    "head_dim": w.d, "rope_dim": w.rd, "topk": w.topk, "kv_rows_per_sequence": w.kv_rows,
-                   "kv_storage": args.kv, "epilogue": "inverse RoPE", "input_sets": len(sets),
+                   "kv_storage": args.kv, "epilogue": "none" if args.no_epilogue else "inverse RoPE", "input_sets": len(sets),
                    "kv_bytes_per_step": alg["kv_bytes"], "distinct_kv_rows": alg["distinct_rows"],
                    "valid_pairs": alg["valid_pairs"]},
         "roofline": roof,

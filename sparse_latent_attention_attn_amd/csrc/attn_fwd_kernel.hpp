@@ -205,6 +205,67 @@ __device__ __forceinline__ void convert_tile_fp8(SA_LDS const uint8_t* raw, SA_L
     }
 }
 
+// fp8 storage at d = 512, pipelined: a raw slot holds a tile's e4m3 codes ([32][D] bytes)
+// followed by its e8m0 scale bytes ([32][D/32]).
+template <int D>
+struct RawSlot {
+    static constexpr int kCodes = kTileKeys * D;
+    static constexpr int kBytes = kCodes + kTileKeys * (D / 32);
+};
+
+// Direct-to-LDS gather of one tile's codes and scale bytes into a raw slot. Codes: 16 B per
+// lane, two rows of 512 codes per load, dealt to the waves (kTileKeys * D / 1024 / NW loads
+// each); scales: one load per wave, a lane per row (rows wid * 32/NW ..), 16 bytes each.
+// Every wave issues the same number of loads, so the waits are exact vmcnt counts; a skipped
+// column loads row 0, and the conversion writes zeros for it.
+template <int D, int NW>
+struct RawGather {
+    static_assert(D == 512, "pipelined fp8 path: rows of 512 codes");
+    static constexpr int kCodeLoads = RawSlot<D>::kCodes / 1024 / NW;
+    static constexpr int kLoads = kCodeLoads + 1;            // loads per wave per tile
+    __device__ static void issue(i32x4 codes_rsrc, i32x4 sc_rsrc, SA_LDS const int32_t* tidx,
+                                 SA_LDS uint8_t* slot, int wid, int lane) {
+        const int sub = lane >> 5, pc = lane & 31;
+        int rows[kCodeLoads];
+#pragma unroll
+        for (int j = 0; j < kCodeLoads; ++j) rows[j] = tidx[2 * (wid * kCodeLoads + j) + sub];
+        constexpr int kScRows = kTileKeys / NW;
+        const int sc_row = tidx[wid * kScRows + (lane & (kScRows - 1))];
+        const uint32_t base = lds_addr(slot);
+#pragma unroll
+        for (int j = 0; j < kCodeLoads; ++j)
+            dma16(codes_rsrc, __builtin_amdgcn_readfirstlane(base + 2 * (wid * kCodeLoads + j) * D),
+                  max(rows[j], 0) * D + 16 * pc);
+        if (lane < kScRows)
+            dma16(sc_rsrc, __builtin_amdgcn_readfirstlane(base + RawSlot<D>::kCodes + wid * kScRows * (D / 32)),
+                  max(sc_row, 0) * (D / 32));
+    }
+};
+
+// Codes of a landed raw slot -> the bf16 tile (same layout and swizzle as a gathered bf16
+// tile), on v_cvt_scalef32_pk_bf16_fp8: each code times its block's scale 2^(e - 127), which
+// is exact in bf16 (the stored values are bf16 values). A lane converts 8 codes (one 16-byte
+// bf16 chunk) per step, a wave one row; skipped columns become zero rows.
+template <int D, int NW>
+__device__ __forceinline__ void convert_raw_fp8(SA_LDS const uint8_t* slot, SA_LDS const int32_t* tidx,
+                                                SA_LDS uint8_t* buf, int wid, int lane) {
+    using G = Geo<D>;
+    static_assert(G::kChunks == kWave, "one bf16 row per wave and step");
+#pragma unroll
+    for (int j = 0; j < kTileKeys / NW; ++j) {
+        const int r = j * NW + wid;
+        const u32x2 codes = *(SA_LDS const u32x2*)(slot + r * D + 8 * lane);
+        const float sc = bits_f32((uint32_t)slot[RawSlot<D>::kCodes + r * (D / 32) + (lane >> 2)] << 23);
+        u32x4 o;
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
+        if (tidx[r] < 0) o = u32x4{0, 0, 0, 0};
+        *(SA_LDS u32x4*)(buf + r * G::kRowBytes + ((lane ^ swz<G::kChunks>(r)) << 4)) = o;
+    }
+}
+
 // Score product step with the accumulator in VGPRs: acc (+)= A . B on
 // v_mfma_f32_16x16x32_bf16. Written as inline assembly because the compiler picks one
 // register class for every MFMA accumulator of a kernel: with O in AGPRs (the kernels that
@@ -316,6 +377,20 @@ struct Pipe {
     static constexpr int kWait = (kAhead - 1) * kLoadsPerWave;
 };
 
+// LDS plan of one kernel instance: the index stage, the bf16 tile buffers and, for fp8
+// storage, the raw slots of codes and scales.
+template <int D, bool FP8, int NW>
+struct KernelLds {
+    static constexpr bool kFp8Pipe = FP8 && D == 512;
+    // bf16: the ring of the pipelined loop; fp8 at d = 512: the tiles being scored, multiplied
+    // and converted; other fp8: one tile
+    static constexpr int kTileBufs = FP8 ? (kFp8Pipe ? 3 : 1) : Pipe<D, NW>::kBuffers;
+    static constexpr int kRawSlots = FP8 ? (kFp8Pipe ? 3 : 2) : 0;
+    // the pipelined fp8 path stages fewer index columns so that its slots fit in LDS
+    static constexpr int kStageCols = kFp8Pipe ? kMaxColsFp8Pipe : kMaxColsPerSplit;
+    static constexpr size_t kTiles = (size_t)kTileBufs * Geo<D>::kTileBytes + (size_t)kRawSlots * RawSlot<D>::kBytes;
+};
+
 // s_waitcnt on the vector-memory counter only; a compiler barrier for memory accesses too,
 // so LDS reads and writes of a landed tile stay behind it.
 template <int N>
@@ -334,18 +409,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     constexpr int HB = NW / KG;                 // head groups of the workgroup
     using G = Geo<D>;
     using PP = Pipe<D, NW>;
-    constexpr int NB = FP8 ? 1 : PP::kBuffers;
+    using KL = KernelLds<D, FP8, NW>;
+    constexpr int NB = KL::kTileBufs;
+    constexpr bool kFp8Pipe = KL::kFp8Pipe;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
-    // LDS: the index stage (kMaxColsPerSplit int32), 64 B of flags, the position's (cos, sin)
-    // row (D f32), then NB bf16 tiles; fp8 adds two raw staging tiles of codes and two of
-    // scale bytes.
+    // LDS: the index stage (KL::kStageCols int32), 64 B of flags, the position's (cos, sin)
+    // row (D f32), then NB bf16 tiles; fp8 adds raw slots of codes and scale bytes.
     SA_LDS int32_t* istage = (SA_LDS int32_t*)smem;
-    SA_LDS float* cs_lds = (SA_LDS float*)(smem + kMaxColsPerSplit * 4 + 64);
-    SA_LDS uint8_t* tiles = smem + kMaxColsPerSplit * 4 + 64 + D * 4;
+    SA_LDS float* cs_lds = (SA_LDS float*)(smem + KL::kStageCols * 4 + 64);
+    SA_LDS uint8_t* tiles = smem + KL::kStageCols * 4 + 64 + D * 4;
     auto tile = [&](int i) { return tiles + i * G::kTileBytes; };
-    auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * (kTileKeys * D); };
-    auto raw_sc = [&](int i) { return tiles + NB * G::kTileBytes + 2 * kTileKeys * D + i * (kTileKeys * (D / 32)); };
+    auto raw = [&](int i) { return tiles + NB * G::kTileBytes + i * RawSlot<D>::kBytes; };
+    auto raw_sc = [&](int i) { return raw(i) + RawSlot<D>::kCodes; };
 
     // The kernel arguments that start-up needs, all at once: scalar loads complete out of
     // order, so the compiler can only wait for all of them, and loads placed next to their
@@ -440,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
     }
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
-    SA_LDS int32_t* lastw = istage + kMaxColsPerSplit;           // one word per wave
+    SA_LDS int32_t* lastw = istage + KL::kStageCols;             // one word per wave
     SA_LDS int32_t* redo = lastw + 8;                           // second-pass flag
     if (lane == 0) lastw[wid] = last;
     if (tid == 0) *redo = 0;
@@ -673,9 +749,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     };
 
     for (int pass = 0;; ++pass) {
-    if constexpr (FP8) {
-        // fp8 storage: one bf16 tile; the codes of the next tile are gathered into a raw
-        // staging tile while the current one is converted and multiplied
+    if constexpr (FP8 && !kFp8Pipe) {
+        // fp8 storage (d other than 512): one bf16 tile; the codes of the next tile are
+        // gathered into a raw staging tile while the current one is converted and multiplied
         if (ntiles > 0) gather_tile_fp8<D, NW>(kv_seq, sc_seq, istage, raw(0), raw_sc(0), wid, lane);
         for (int it = 0; it < ntiles; ++it) {
             SA_LDS const int32_t* tidx = istage + it * kTileKeys;
@@ -758,16 +834,34 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             }
         }
     } else {
-        // bf16 storage, software-pipelined: iteration `it` scores tile it, then multiplies the
-        // probabilities of tile it-1 with its rows while tile it's softmax runs in between
-        // the matrix instructions. Tiles it-1 and it are in use and tiles it+1 and it+2 are
-        // in flight (kBuffers = 4). The only vector-memory operations inside the loop are the
-        // tile loads, so tile it has landed once only tile it+1's loads remain.
+        // Software-pipelined: iteration `it` scores tile it, then multiplies the probabilities
+        // of tile it-1 with its rows while tile it's softmax runs in between the matrix
+        // instructions. The only vector-memory operations inside the loop are the tile loads.
+        //   bf16 storage: tiles it-1 and it are in use and tiles it+1 and it+2 are in flight
+        //   (kBuffers = 4), so tile it has landed once only tile it+1's loads remain.
+        //   fp8 storage (d = 512): the codes and scales of tiles it+1 and it+2 sit in raw
+        //   slots (it+1 landed, it+2 in flight) and tile it+1 is converted into its bf16
+        //   buffer between the two products; tile it+3's loads go out at the top.
         constexpr int kAh = 2;
-        static_assert(NB >= kAh + 2, "tile ring too small for the pipeline");
+        static_assert(kFp8Pipe || NB >= kAh + 2, "tile ring too small for the pipeline");
+        const i32x4 sc_rsrc = FP8 ? make_rsrc(sc_seq, (uint32_t)p.kv_rows * (uint32_t)(D / 32)) : kv_rsrc;
+        if constexpr (kFp8Pipe) {
+            using RG = RawGather<D, NW>;
 #pragma unroll
-        for (int j = 0; j < kAh; ++j)
-            if (j < ntiles) gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
+            for (int j = 0; j < 3; ++j)
+                if (j < ntiles) RG::issue(kv_rsrc, sc_rsrc, istage + j * kTileKeys, raw(j), wid, lane);
+            if (ntiles > 0) {
+                if (ntiles >= 3) wait_vmcnt<2 * RG::kLoads>();
+                else if (ntiles == 2) wait_vmcnt<RG::kLoads>();
+                else wait_vmcnt<0>();
+                lds_barrier();                 // tile 0's codes from every wave
+                convert_raw_fp8<D, NW>(raw(0), istage, tile(0), wid, lane);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kAh; ++j)
+                if (j < ntiles) gather_tile_bf16<D, NW>(kv_rsrc, istage + j * kTileKeys, tile(j), wid, lane);
+        }
         // One PV instance for every iteration, so that O stays in the same registers
         // throughout: iteration 0 has no previous tile (its softmax runs on its own), and the
         // extra last iteration scores nothing (all its keys are masked, p = 0) while it
@@ -783,12 +877,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             if (it < ntiles) {
                 SA_LDS const int32_t* tidx = istage + it * kTileKeys;
                 valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
-                if (it + 1 < ntiles) wait_vmcnt<PP::kLoadsPerWave>();
-                else wait_vmcnt<0>();
-                if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
-                lds_barrier();             // tile it visible to all; buffer of tile it-2 free
-                if (it + kAh < ntiles)
-                    gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
+                if constexpr (kFp8Pipe) {
+                    using RG = RawGather<D, NW>;
+                    if (it + 2 < ntiles) wait_vmcnt<RG::kLoads>();
+                    else wait_vmcnt<0>();
+                    // tile it converted by every wave, tile it+1's codes visible; the slot of
+                    // tile it and the buffer of tile it-2 are free
+                    lds_barrier();
+                    if (it + 3 < ntiles)
+                        RG::issue(kv_rsrc, sc_rsrc, tidx + 3 * kTileKeys, raw((it + 3) % 3), wid, lane);
+                } else {
+                    if (it + 1 < ntiles) wait_vmcnt<PP::kLoadsPerWave>();
+                    else wait_vmcnt<0>();
+                    if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
+                    lds_barrier();         // tile it visible to all; buffer of tile it-2 free
+                    if (it + kAh < ntiles)
+                        gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
+                }
                 pin_offsets();
                 qk(cur, s_acc);
             } else {
@@ -798,6 +903,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     for (int hb = 0; hb < HPW; ++hb) s_acc[mb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             const float sc = prepare(s_acc, valid);
+            if constexpr (kFp8Pipe) {
+                if (it + 1 < ntiles)
+                    convert_raw_fp8<D, NW>(raw((it + 1) % 3), istage + (it + 1) * kTileKeys, tile((it + 1) % NB), wid, lane);
+            }
             u32x4 pb[HPW];
             float psum[HPW];
 #pragma unroll
@@ -992,12 +1101,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 template <int D, bool FP8, int NW, int HPW = 1, int KG = 1>
 inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
-    constexpr int NB = FP8 ? 1 : Pipe<D, NW>::kBuffers;
-    // after the tile buffers (and the fp8 staging tiles) the region must also hold the
+    using KL = KernelLds<D, FP8, NW>;
+    // after the tile buffers (and the fp8 raw slots) the region must also hold the
     // epilogue's 16 padded output rows per wave
-    constexpr size_t kTiles = (size_t)NB * G::kTileBytes + (FP8 ? 2 * kTileKeys * D + 2 * kTileKeys * (D / 32) : 0);
+    constexpr size_t kTiles = KL::kTiles;
     constexpr size_t kOut = (size_t)NW * kHeadsPerWave * (2 * D + 16);
-    const size_t lds = (size_t)kMaxColsPerSplit * 4 + 64 + (size_t)D * 4 + (kTiles > kOut ? kTiles : kOut);
+    constexpr size_t lds = (size_t)KL::kStageCols * 4 + 64 + (size_t)D * 4 + (kTiles > kOut ? kTiles : kOut);
+    static_assert(lds <= 160 * 1024, "LDS plan exceeds 160 KB");
     // the key-group merge slots sit behind the output staging area
     static_assert(KG == 1 || (size_t)(NW / KG) * kHeadsPerWave * (2 * D + 16) +
                                  (size_t)(KG - 1) * (NW / KG) * (HPW * G::kDBlocks * kWave * 16 + HPW * kWave * 8) <= kTiles,

@@ -135,8 +135,10 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
         }
     }
     pl.h_pad = pl.head_blocks * pl.nw / pl.kg * pl.hpw * kHeadsPerWave;
-    // a workgroup stages at most kMaxColsPerSplit index columns
-    const int max_tiles = sa::kMaxColsPerSplit / kTileKeys;
+    // a workgroup stages at most kMaxColsPerSplit index columns (kMaxColsFp8Pipe for fp8
+    // storage at d = 512)
+    const int max_cols = a->kv_format != SA_KV_BF16 && a->d == 512 ? sa::kMaxColsFp8Pipe : sa::kMaxColsPerSplit;
+    const int max_tiles = max_cols / kTileKeys;
     splits = std::max(splits, (ntiles + max_tiles - 1) / max_tiles);
     const int tiles_per_split = (ntiles + splits - 1) / splits;
     pl.cols_per_split = tiles_per_split * kTileKeys;

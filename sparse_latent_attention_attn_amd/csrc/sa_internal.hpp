@@ -12,6 +12,7 @@ constexpr int kTileKeys = 32;       // index columns per key tile
 constexpr int kHeadsPerWave = 16;   // heads in one block (the N of a 16x16 MFMA tile)
 constexpr int kMaxWaves = 4;        // waves per workgroup
 constexpr int kMaxColsPerSplit = 4096;  // index columns one workgroup stages in LDS
+constexpr int kMaxColsFp8Pipe = 3072;   // the same for fp8 storage at d = 512 (its raw slots take the rest)
 
 // Everything one sparse_attn launch needs, passed by value as the kernel argument.
 struct KParams {

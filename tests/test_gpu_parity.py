@@ -242,6 +242,34 @@ def test_late_large_scores(sa, boost, where, fmt):
     assert_close(u16(out).reshape(-1, 16, 64), ref, f"late large {boost} {where} {fmt}")
 
 
+@pytest.mark.parametrize("seed,b,s,h,rows,topk,hole,boost", [
+    (81, 1, 3, 16, 40, 20, 0.0, 0.0),       # one wave per workgroup, a single tile
+    (82, 2, 2, 32, 100, 64, 0.3, 0.0),      # two waves, two tiles (the shortest pipeline)
+    (83, 1, 4, 64, 200, 96, 0.1, 0.0),      # four waves, three tiles
+    (84, 2, 3, 128, 500, 300, 0.5, 0.0),    # ten tiles, half the columns skipped
+    (85, 1, 2, 64, 4000, 3200, 0.02, 0.0),  # more columns than one workgroup stages: splits
+    (86, 1, 2, 48, 60, 50, 1.0, 0.0),       # every column skipped
+    (87, 1, 3, 64, 300, 200, 0.0, 4.0),     # a late large score: the second key pass
+])
+def test_fp8_pipeline(sa, seed, b, s, h, rows, topk, hole, boost):
+    """fp8 storage at d = 512 (codes and scales gathered into raw slots two tiles ahead,
+    converted to bf16 tiles between the two products) against the oracle on the
+    round-tripped rows."""
+    _say("fp8 pipeline", seed, b, s, h, rows, topk, hole, boost)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, 512, rows, topk, hole, False)
+    if boost:
+        for t in range(s):
+            col = topk - 5
+            if idx[0, t, col] >= 0:
+                kv[0, int(idx[0, t, col])] = (q[0, t, 2].float() * boost).to(torch.bfloat16)
+    scale = float(np.float32(512 ** -0.5))
+    codes, kv_scale = sa.quant_kv_fp8(kv.cuda(), want=("codes", "scales"))
+    kv_ref = oracle.act_quant(u16(kv).reshape(-1, 512))[0].reshape(kv.shape)
+    out = sa.sparse_attn(q.cuda(), codes, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale)
+    ref = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, 512), ref, f"fp8 pipeline {seed}")
+
+
 @pytest.mark.parametrize("d,plan", [(512, "key groups"), (256, "splits")])
 def test_late_large_scores_across_splits(sa, d, plan):
     """A decode-shaped problem with few queries: at d = 512 the waves of a workgroup split the
