@@ -57,10 +57,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
 // ------------------------------------------------------------------ launch
 template <int D, bool FP8>
 static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int kg, int blocks, hipStream_t st) {
-    if constexpr (D == 512 && !FP8) {
-        if (hpw == 2) return nw == 4 && kg == 1 ? launch_fwd_wide(p, blocks, st) : hipErrorInvalidValue;
+    if constexpr (D == 512) {
+        if constexpr (!FP8)
+            if (hpw == 2) return nw == 4 && kg == 1 ? launch_fwd_wide(p, blocks, st) : hipErrorInvalidValue;
         if (kg == 2) return nw == 4 && hpw == 1 ? launch_fwd<D, FP8, 4, 1, 2>(p, blocks, st) : hipErrorInvalidValue;
-        if (kg == 4) return nw == 4 && hpw == 1 ? launch_fwd<D, FP8, 4, 1, 4>(p, blocks, st) : hipErrorInvalidValue;
+        if constexpr (!FP8)   // fp8: at most two key groups (its raw slots hold two tiles of a super tile)
+            if (kg == 4) return nw == 4 && hpw == 1 ? launch_fwd<D, FP8, 4, 1, 4>(p, blocks, st) : hipErrorInvalidValue;
     }
     if (hpw != 1 || kg != 1) return hipErrorInvalidValue;
     if (nw == 1) return launch_fwd<D, FP8, 1>(p, blocks, st);

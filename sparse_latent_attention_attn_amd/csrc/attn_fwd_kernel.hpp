@@ -405,7 +405,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // end (KG = 1: every wave takes every tile, for its own heads).
 template <int D, bool FP8, int NW, int HPW, int KG = 1>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
-    static_assert(KG == 1 || (!FP8 && NW % KG == 0), "key groups need bf16 storage");
+    static_assert(KG == 1 || ((!FP8 || D == 512) && NW % KG == 0), "key groups: bf16, or fp8 at d = 512");
     constexpr int HB = NW / KG;                 // head groups of the workgroup
     using G = Geo<D>;
     using PP = Pipe<D, NW>;
@@ -748,6 +748,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(pv_off[k]));
     };
 
+    // fp8 storage: the rows' scale bytes
+    const i32x4 sc_rsrc = FP8 ? make_rsrc(sc_seq, (uint32_t)p.kv_rows * (uint32_t)(D / 32)) : kv_rsrc;
     for (int pass = 0;; ++pass) {
     if constexpr (FP8 && !kFp8Pipe) {
         // fp8 storage (d other than 512): one bf16 tile; the codes of the next tile are
@@ -778,35 +780,53 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             pv(tile(0), pb, [](int) {});
         }
     } else if constexpr (KG > 1) {
-        // Key groups: the tile ring holds NS groups of KG tiles ("super tiles"); all waves
-        // gather every tile, the waves of key group g work on tile s*KG + g of super tile s.
-        // With two super tiles in the ring the next one is gathered while the current one is
-        // worked on; with one, after it (a barrier in between).
-        constexpr int NS = NB / KG;
-        static_assert(NS >= 1, "tile ring too small for the key groups");
+        // Key groups: the waves of key group g work on tile s*KG + g of super tile s.
+        //   bf16 storage: the tile ring holds NS super tiles of KG tiles and all waves gather
+        //   every tile. With two super tiles in the ring the next one is gathered while the
+        //   current one is worked on; with one, after it (a barrier in between).
+        //   fp8 storage: the codes and scales of the next super tile are gathered into raw
+        //   slots while the current one is worked on; all waves convert a landed super tile
+        //   into the bf16 tiles between two barriers.
+        constexpr int NS = kFp8Pipe ? 1 : NB / KG;
+        static_assert(NS >= 1 && (!kFp8Pipe || KL::kRawSlots >= KG), "tile ring too small for the key groups");
         const int nsuper = (ntiles + KG - 1) / KG;
         auto gather_super = [&](int su) {
 #pragma unroll
             for (int g = 0; g < KG; ++g) {
                 const int ti = su * KG + g;
-                if (ti < ntiles)
-                    gather_tile_bf16<D, NW>(kv_rsrc, istage + ti * kTileKeys, tile((su % NS) * KG + g), wid, lane);
+                if (ti < ntiles) {
+                    if constexpr (kFp8Pipe)
+                        RawGather<D, NW>::issue(kv_rsrc, sc_rsrc, istage + ti * kTileKeys, raw(g), wid, lane);
+                    else
+                        gather_tile_bf16<D, NW>(kv_rsrc, istage + ti * kTileKeys, tile((su % NS) * KG + g), wid, lane);
+                }
             }
         };
         if (nsuper > 0) gather_super(0);
         for (int su = 0; su < nsuper; ++su) {
             wait_vmcnt<0>();
+            if constexpr (kFp8Pipe) {
+                lds_barrier();             // super tile su's codes; every wave done with su-1
 #pragma unroll
-            for (int g = 0; g < KG; ++g) {
-                const int ti = su * KG + g;
-                if (ti < ntiles) {
-                    SA_LDS const int32_t* tix = istage + ti * kTileKeys;
-                    const uint32_t v = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
-                    if (v != 0 && v != 0xffffffffu) zero_skipped_rows<D, NW>(tix, tile((su % NS) * KG + g), wid, lane);
+                for (int g = 0; g < KG; ++g) {
+                    const int ti = su * KG + g;
+                    if (ti < ntiles) convert_raw_fp8<D, NW>(raw(g), istage + ti * kTileKeys, tile(g), wid, lane);
                 }
+                lds_barrier();             // super tile su converted; its raw slots free
+                if (su + 1 < nsuper) gather_super(su + 1);
+            } else {
+#pragma unroll
+                for (int g = 0; g < KG; ++g) {
+                    const int ti = su * KG + g;
+                    if (ti < ntiles) {
+                        SA_LDS const int32_t* tix = istage + ti * kTileKeys;
+                        const uint32_t v = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
+                        if (v != 0 && v != 0xffffffffu) zero_skipped_rows<D, NW>(tix, tile((su % NS) * KG + g), wid, lane);
+                    }
+                }
+                lds_barrier();             // super tile su visible to all
+                if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             }
-            lds_barrier();                 // super tile su visible to all
-            if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             const int ti = su * KG + kg;
             uint32_t valid = 0;
             if (ti < ntiles) {
@@ -828,7 +848,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 __builtin_amdgcn_sched_barrier(0);
                 pv(cur, pb, [](int) {});
             }
-            if (NS == 1 && su + 1 < nsuper) {
+            if (!kFp8Pipe && NS == 1 && su + 1 < nsuper) {
                 lds_barrier();             // every wave is done with the super tile
                 gather_super(su + 1);
             }
@@ -844,7 +864,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         //   buffer between the two products; tile it+3's loads go out at the top.
         constexpr int kAh = 2;
         static_assert(kFp8Pipe || NB >= kAh + 2, "tile ring too small for the pipeline");
-        const i32x4 sc_rsrc = FP8 ? make_rsrc(sc_seq, (uint32_t)p.kv_rows * (uint32_t)(D / 32)) : kv_rsrc;
         if constexpr (kFp8Pipe) {
             using RG = RawGather<D, NW>;
 #pragma unroll

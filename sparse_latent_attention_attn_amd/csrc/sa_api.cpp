@@ -114,17 +114,17 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
         const int64_t want = (cus + wgs - 1) / wgs;
         splits = (int)std::max<int64_t>(1, std::min<int64_t>(want, ntiles / kMinTilesPerSplit));
     }
-    // Key groups instead of splits (bf16 rows of 512): the four waves of a workgroup take the
-    // same 16 or 32 heads and share out the query's tiles, merging their partial results in
-    // LDS, which saves the f32 partials (one per head and split, as large as 2 KB per head)
-    // and the combine kernel. Measured on 64 queries x 128 heads x 640 columns: 41.5 us with
+    // Key groups instead of splits (rows of 512; fp8 storage: at most two groups): the four
+    // waves of a workgroup take the same 16 or 32 heads and share out the query's tiles,
+    // merging their partial results in LDS, which saves the f32 partials (one per head and
+    // split, as large as 2 KB per head) and the combine kernel. Measured on 64 queries x 128 heads x 640 columns: 41.5 us with
     // two splits, 36.7 us with two key groups. The most key groups that keep one round of
     // workgroups on the GPU and leave no group without tiles. (Without splits, a short key
     // list does better on one wave per head block: 32 queries x 64 heads x 128 columns took
     // 12.9 us that way and 13.6 us with four key groups, the merge costing what the shorter
     // loop saved.)
-    if (splits > 1 && a->kv_format == SA_KV_BF16 && a->d == 512 && pl.hpw == 1) {
-        for (int kg = 4; kg >= 2; kg /= 2) {
+    if (splits > 1 && a->d == 512 && pl.hpw == 1) {
+        for (int kg = a->kv_format == SA_KV_BF16 ? 4 : 2; kg >= 2; kg /= 2) {
             if (nq * blocks_for(4 / kg) <= cus && ntiles >= kg) {
                 pl.kg = kg;
                 pl.nw = 4;

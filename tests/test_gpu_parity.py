@@ -250,6 +250,7 @@ def test_late_large_scores(sa, boost, where, fmt):
     (85, 1, 2, 64, 4000, 3200, 0.02, 0.0),  # more columns than one workgroup stages: splits
     (86, 1, 2, 48, 60, 50, 1.0, 0.0),       # every column skipped
     (87, 1, 3, 64, 300, 200, 0.0, 4.0),     # a late large score: the second key pass
+    (88, 2, 1, 64, 1200, 1024, 0.05, 4.0),  # decode-shaped: two key groups, merge and second pass
 ])
 def test_fp8_pipeline(sa, seed, b, s, h, rows, topk, hole, boost):
     """fp8 storage at d = 512 (codes and scales gathered into raw slots two tiles ahead,
