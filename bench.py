@@ -226,11 +226,18 @@ KERNEL_SOURCES = ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "s
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: line and block comments and whitespace are left
+    out (the sources hold no comment markers inside string literals), so that an edit of a
+    comment does not orphan counters taken on identical code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_latent_attention_attn_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_latent_attention_attn_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

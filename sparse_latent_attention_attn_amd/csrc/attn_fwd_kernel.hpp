@@ -5,9 +5,9 @@
 //
 // Work inside a workgroup of NW waves (NW = 1, 2 or 4), HPW blocks of 16 heads per wave:
 //   * key tiles of 32 index columns are gathered row by row from HBM straight into LDS
-//     (buffer_load_dwordx4 ... lds, 16 B per lane) through a ring of 4 buffers, 3 tiles in
-//     flight, so the gathers overlap the matrix work. All waves of the workgroup read the
-//     same tile: one gather serves every head of the query in the workgroup. Rows carry a
+//     (buffer_load_dwordx4 ... lds, 16 B per lane) through a ring of 4 buffers, 2 tiles in
+//     flight ahead of the two being worked on. All waves of the workgroup read the same
+//     tile: one gather serves every head of the query in the workgroup. Rows carry a
 //     16-byte-chunk XOR swizzle so that both LDS read patterns below avoid bank conflicts.
 //   * scores are computed transposed, S^T[key][head] = K . Q^T, on v_mfma_f32_16x16x32_bf16:
 //     K comes from LDS as the A operand (each read feeds the HPW head blocks), Q stays in
@@ -17,12 +17,19 @@
 //   * the probabilities are rounded to bf16 in registers and are already the B operand of
 //     O^T[d][head] += V^T . P^T (a 32-key step); V^T is read from the same LDS tile with the
 //     transposing ds_read_b64_tr_b16, so the tile is stored once and is both K and V.
+//   * the key loop is software-pipelined: iteration t scores tile t, then multiplies the
+//     probabilities of tile t-1 while tile t's softmax steps run between those matrix
+//     instructions.
 //   * softmax against a fixed reference per head (taken at the first tile that names a row,
 //     from the sink and that tile's scores), with a rare second pass over the keys when a
 //     later score exceeds it by too much: O is never rescaled inside the key loop and stays
 //     in accumulator registers (4 f32 per lane per 16-wide slice of d and head block).
 //   * the sink enters the running sum as exp(sink - reference), in one lane group and in
-//     split 0 only, which puts it in the denominator.
+//     split 0 and key group 0 only, which puts it in the denominator.
+//   * key groups (KG > 1): the waves share a query's heads and split its tiles; their
+//     partial results are merged in LDS.
+//   * fp8 storage: tiles of e4m3 codes and e8m0 scales are gathered into raw slots and
+//     converted in LDS to the bf16 tiles above (exact), so the products are the same.
 //   * with more than one split, unnormalised partials (O, reference, sum) go to the
 //     workspace and a small combine kernel merges them; otherwise the epilogue (divide,
 //     bf16, optional inverse RoPE) runs here.
