@@ -430,3 +430,18 @@ def test_full_size_sampled(sa, name):
     ref = oracle_run(w, qsel=sel, rope=True)
     got = u16(out).reshape(-1, w.h, w.d)[sel]
     assert_close(got, ref, f"full {name}")
+
+
+@pytest.mark.parametrize("name", ["decode_window", "decode_compress"])
+def test_full_size_sampled_fp8(sa, name):
+    """The decode workloads at full size with fp8 storage (codes and block-32 scales); their
+    rows are fp8-round-tripped already, so the oracle runs on the same values."""
+    _say("full fp8", name)
+    w = W.make(name)
+    assert w.kv_roundtrip
+    out, idx = gpu_run(w, "fp8", True)
+    sel = np.array(FULL[name], np.int64)
+    assert np.array_equal(idx.cpu().numpy(), oracle_indices(w))
+    ref = oracle_run(w, qsel=sel, rope=True)
+    got = u16(out).reshape(-1, w.h, w.d)[sel]
+    assert_close(got, ref, f"full fp8 {name}")
