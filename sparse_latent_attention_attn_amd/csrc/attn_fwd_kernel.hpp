@@ -258,18 +258,35 @@ __device__ __forceinline__ void convert_raw_fp8(SA_LDS const uint8_t* slot, SA_L
                                                 SA_LDS uint8_t* buf, int wid, int lane) {
     using G = Geo<D>;
     static_assert(G::kChunks == kWave, "one bf16 row per wave and step");
+    constexpr int kSteps = kTileKeys / NW;                      // rows per wave
+    constexpr int kBatch = kSteps < 4 ? kSteps : 4;
+    // The reads of a batch of rows go out before its writes: the compiler cannot tell that a
+    // write to the bf16 tile never meets a later read of the raw slot, so row by row it would
+    // wait for each read in turn.
 #pragma unroll
-    for (int j = 0; j < kTileKeys / NW; ++j) {
-        const int r = j * NW + wid;
-        const u32x2 codes = *(SA_LDS const u32x2*)(slot + r * D + 8 * lane);
-        const float sc = bits_f32((uint32_t)slot[RawSlot<D>::kCodes + r * (D / 32) + (lane >> 2)] << 23);
-        u32x4 o;
-        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
-        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
-        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
-        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
-        if (tidx[r] < 0) o = u32x4{0, 0, 0, 0};
-        *(SA_LDS u32x4*)(buf + r * G::kRowBytes + ((lane ^ swz<G::kChunks>(r)) << 4)) = o;
+    for (int j0 = 0; j0 < kSteps; j0 += kBatch) {
+        u32x2 codes[kBatch];
+        uint32_t sbyte[kBatch];
+        bool skip[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int r = (j0 + u) * NW + wid;
+            codes[u] = *(SA_LDS const u32x2*)(slot + r * D + 8 * lane);
+            sbyte[u] = slot[RawSlot<D>::kCodes + r * (D / 32) + (lane >> 2)];
+            skip[u] = tidx[r] < 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int r = (j0 + u) * NW + wid;
+            const float sc = bits_f32(sbyte[u] << 23);
+            u32x4 o;
+            o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][0], sc, false));
+            o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][0], sc, true));
+            o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][1], sc, false));
+            o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][1], sc, true));
+            if (skip[u]) o = u32x4{0, 0, 0, 0};
+            *(SA_LDS u32x4*)(buf + r * G::kRowBytes + ((lane ^ swz<G::kChunks>(r)) << 4)) = o;
+        }
     }
 }
 
