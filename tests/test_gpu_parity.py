@@ -316,6 +316,27 @@ def test_key_groups(sa, seed, b, h, topk, hole):
         assert_close(u16(out).reshape(-1, h, 512), ref, f"key groups {seed}")
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_key_groups_with_splits(sa, fmt):
+    """A list longer than one workgroup stages (4500 columns: 4096 with bf16 storage, 3072
+    with fp8) on a decode-shaped problem: key groups inside each workgroup and two splits
+    merged by the combine kernel, with a late large score in the second split."""
+    _say("key groups + splits", fmt)
+    q, kv, sink, idx = W.rand_problem(74, 2, 1, 64, 512, 6000, 4500, 0.05, False)
+    row = int(idx[1, 0, 4400]) if idx[1, 0, 4400] >= 0 else 0
+    kv[1, row] = (q[1, 0, 7].float() * 2.0).to(torch.bfloat16)
+    scale = float(np.float32(512 ** -0.5))
+    kvd, kv_scale, kv_ref = kv.cuda(), None, u16(kv)
+    if fmt == "fp8":
+        kvd, kv_scale = sa.quant_kv_fp8(kvd, want=("codes", "scales"))
+        kv_ref = oracle.act_quant(u16(kv).reshape(-1, 512))[0].reshape(kv.shape)
+    args = sa.make_args(q.cuda(), kvd, sink.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()), kv_scale=kv_scale)
+    assert sa.sparse_attn_workspace_bytes(args) > 0, "expected a plan with splits"
+    out = sa.sparse_attn(q.cuda(), kvd, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale)
+    ref = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, 64, 512), ref, f"key groups + splits {fmt}")
+
+
 def test_empty_lists_and_no_sink(sa):
     q, kv, sink, idx = W.rand_problem(31, 1, 3, 16, 64, 20, 40, 0.0, False)
     idx[0, 1] = -1
