@@ -70,8 +70,9 @@ struct Geo {
 // Direct-to-LDS gather of one key tile (bf16 storage). The tile's row indices are read
 // from the index stage in LDS (-1 = skip). Every wave issues exactly kInsts/NW loads per
 // tile, whatever the indices, so that waiting for the oldest tile in flight is an exact
-// vmcnt: a skipped row loads row 0 of the sequence instead, and zero_skipped_rows clears it
-// once it has landed (a zero row can never turn a zero probability into a NaN).
+// vmcnt: a skipped row is loaded from an offset past the end of the buffer, for which the
+// buffer's range check returns zeros without a memory access, so it lands as a zero row (a
+// zero row can never turn a zero probability into a NaN).
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at lds + 16 i
@@ -107,6 +108,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
     return r;
 }
 
+// A buffer offset past every kv buffer (the host rejects kv buffers of 2^31 bytes or more,
+// and their sizes are multiples of 16).
+constexpr int kPastEnd = 0x7ffffff0;
+
 // Wave wid issues loads wid*kPer .. wid*kPer+kPer-1 of the tile; load j covers rows
 // j*kRowsPerInst .. +kRowsPerInst-1. All row indices are read before the first load issues.
 template <int D, int NW>
@@ -126,23 +131,8 @@ __device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_
     for (int j = 0; j < kPer; ++j) {
         const int r0 = (wid * kPer + j) * G::kRowsPerInst;
         const int r = r0 + sub;
-        const int voff = max(rows[j], 0) * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        const int voff = rows[j] < 0 ? kPastEnd : rows[j] * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
         dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
-    }
-}
-
-// Zero the rows of a landed tile whose column is a skip (only the rows this wave loaded).
-template <int D, int NW>
-__device__ __forceinline__ void zero_skipped_rows(SA_LDS const int32_t* tidx, SA_LDS uint8_t* buf,
-                                                  int wid, int lane) {
-    using G = Geo<D>;
-    constexpr int kPer = kTileKeys / G::kRowsPerInst / NW;
-    const int sub = lane / G::kChunks;
-    const int pc = lane % G::kChunks;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int r = (wid * kPer + j) * G::kRowsPerInst + sub;
-        if (tidx[r] < 0) *(SA_LDS u32x4*)(buf + r * G::kRowBytes + pc * 16) = u32x4{0, 0, 0, 0};
     }
 }
 
@@ -839,15 +829,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 lds_barrier();             // super tile su converted; its raw slots free
                 if (su + 1 < nsuper) gather_super(su + 1);
             } else {
-#pragma unroll
-                for (int g = 0; g < KG; ++g) {
-                    const int ti = su * KG + g;
-                    if (ti < ntiles) {
-                        SA_LDS const int32_t* tix = istage + ti * kTileKeys;
-                        const uint32_t v = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
-                        if (v != 0 && v != 0xffffffffu) zero_skipped_rows<D, NW>(tix, tile((su % NS) * KG + g), wid, lane);
-                    }
-                }
                 lds_barrier();             // super tile su visible to all
                 if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             }
@@ -932,7 +913,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 } else {
                     if (it + 1 < ntiles) wait_vmcnt<PP::kLoadsPerWave>();
                     else wait_vmcnt<0>();
-                    if (valid != 0 && valid != 0xffffffffu) zero_skipped_rows<D, NW>(tidx, cur, wid, lane);
                     lds_barrier();         // tile it visible to all; buffer of tile it-2 free
                     if (it + kAh < ntiles)
                         gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);

@@ -337,6 +337,31 @@ def test_key_groups_with_splits(sa, fmt):
     assert_close(u16(out).reshape(-1, 64, 512), ref, f"key groups + splits {fmt}")
 
 
+@pytest.mark.parametrize("seed,b,s,h,rows,topk,hole", [
+    (91, 40, 1, 128, 900, 600, 0.1),   # key groups: decode-shaped, 40 queries x 128 heads
+    (92, 2, 24, 64, 700, 300, 0.2),    # the pipelined loop, one head block per wave
+    (93, 1, 256, 128, 300, 96, 0.3),   # the pipelined loop, two head blocks per wave
+])
+def test_skipped_columns_read_nothing(sa, seed, b, s, h, rows, topk, hole):
+    """Every kv row that no index names holds NaN, row 0 among them: a skipped column (-1)
+    must bring no row's values into the tile, so the output stays finite and matches the
+    oracle (which reads named rows only)."""
+    _say("skipped columns read nothing", seed, b, s, h)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, 512, rows, topk, hole, False)
+    idx[idx == 0] = -1
+    for bi in range(b):
+        named = torch.zeros(rows, dtype=torch.bool)
+        v = idx[bi].reshape(-1)
+        named[v[v >= 0].long()] = True
+        assert not named.all()
+        kv[bi, ~named] = float("nan")
+    scale = float(np.float32(512 ** -0.5))
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
+    assert torch.isfinite(out.float()).all()
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, 512), ref, f"skipped columns {seed}")
+
+
 def test_empty_lists_and_no_sink(sa):
     q, kv, sink, idx = W.rand_problem(31, 1, 3, 16, 64, 20, 40, 0.0, False)
     idx[0, 1] = -1
