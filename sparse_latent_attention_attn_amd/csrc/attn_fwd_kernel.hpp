@@ -979,7 +979,47 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     float l_tot[HPW];
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) l_tot[hb] = sum4groups(l_run[hb]);
-    if constexpr (KG > 1) {
+    // With two key groups each group finishes one half of d (group g: d0 = g * D/2) and all
+    // waves share the epilogue; otherwise a wave finishes all of d.
+    constexpr bool kHalves = KG == 2;
+    constexpr int kEpiD = kHalves ? D / 2 : D;                  // elements of d this wave finishes
+    constexpr int kEpiBlocks = kEpiD / 16;
+    const int d0 = kHalves ? kg * kEpiD : 0;
+    if constexpr (kHalves) {
+        // Each wave leaves the half of O it does not finish, with its (m, l), in LDS behind
+        // the staging area of the epilogue (the tile buffers are free: a barrier ended the key
+        // loop), and adds the other group's part of its own half: m = max(m_0, m_1),
+        // O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m), l likewise. Its finished half then sits in
+        // o_acc[0 .. kEpiBlocks-1] (group 1 moves its upper half down) for the epilogue.
+        constexpr int kSlotO = HPW * kEpiBlocks * kWave * 16;
+        constexpr int kSlot = kSlotO + HPW * kWave * 8;
+        SA_LDS uint8_t* mrg = tiles + NW * kHeadsPerWave * (2 * kEpiD + 16);
+        SA_LDS uint8_t* mine = mrg + wid * kSlot;
+        SA_LDS const uint8_t* other = mrg + ((1 - kg) * HB + hbw) * kSlot;
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+#pragma unroll
+            for (int db = 0; db < kEpiBlocks; ++db)
+                *(SA_LDS f32x4*)(mine + ((hb * kEpiBlocks + db) * kWave + lane) * 16) =
+                    kg == 0 ? o_acc[db + kEpiBlocks][hb] : o_acc[db][hb];
+            *(SA_LDS f32x2*)(mine + kSlotO + (hb * kWave + lane) * 8) = f32x2{m_ref[hb], l_tot[hb]};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+            const f32x2 ml = *(SA_LDS const f32x2*)(other + kSlotO + (hb * kWave + lane) * 8);
+            const float m = fmaxf(m_ref[hb], ml[0]);
+            const float w0 = m_ref[hb] == -INFINITY ? 0.0f : fast_exp2(m_ref[hb] - m);   // no row and no sink
+            const float w1 = ml[0] == -INFINITY ? 0.0f : fast_exp2(ml[0] - m);
+#pragma unroll
+            for (int db = 0; db < kEpiBlocks; ++db) {
+                const f32x4 own = kg == 0 ? o_acc[db][hb] : o_acc[db + kEpiBlocks][hb];
+                o_acc[db][hb] = own * w0 + *(SA_LDS const f32x4*)(other + ((hb * kEpiBlocks + db) * kWave + lane) * 16) * w1;
+            }
+            m_ref[hb] = m;
+            l_tot[hb] = l_tot[hb] * w0 + ml[1] * w1;
+        }
+    } else if constexpr (KG > 1) {
         // Merge the key groups into group 0: m = max m_g, O = sum O_g 2^(m_g - m),
         // l = sum l_g 2^(m_g - m). Groups 1.. leave O (accumulator layout, 16 bytes per lane
         // and slice) and (m, l) in LDS behind the epilogue's output staging area; the tile
@@ -1043,15 +1083,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         // This code runs once per workgroup, so its instructions are fetched cold: it is kept
         // short and nearly free of branches (the rotation is a small loop over the staged rows
         // rather than a test in every slice of d, and the stores take one uniform branch).
-        constexpr int kOutStride = 2 * D + 16;                      // bytes per staged row
-        constexpr int kLanesPerRow = 2 * D / 16;                    // 16-byte pieces per row
+        constexpr int kOutStride = 2 * kEpiD + 16;                  // bytes per staged row
+        constexpr int kLanesPerRow = 2 * kEpiD / 16;                // 16-byte pieces per row
         constexpr int kRowsPerRead = kWave / kLanesPerRow;
         constexpr int kReads = kHeadsPerWave / kRowsPerRead;
         SA_LDS uint8_t* ob = tiles + wid * (kHeadsPerWave * kOutStride);
         const int r0 = D - p.rope_dim;
         const int wave_head0 = head0 - l16;                         // first head of block 0
         const int prow = lane / kLanesPerRow, pcol = lane % kLanesPerRow;
-        uint16_t* out_q = p.out + (int64_t)seq * p.out_seq_stride + (int64_t)t * p.h * D;
+        uint16_t* out_q = p.out + (int64_t)seq * p.out_seq_stride + (int64_t)t * p.h * D + d0;
         // inverse RoPE (apply_rotary_emb with inverse=True: the bf16 pair times the conjugate
         // of (cos, sin) in f32, back to bf16). With one head block per wave and rope_dim = 64
         // the rotated elements are the last four slices of d, rotated in registers before
@@ -1059,15 +1099,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         // otherwise they are rotated in the staged rows: lane takes row lane / 4 and its pairs
         // lane % 4, +4, ... (with two head blocks per wave the in-register form measured 1%
         // slower over the whole kernel, the loop 5% faster per workgroup on one block).
-        constexpr int kTail = HPW == 1 ? G::kDBlocks - 4 : G::kDBlocks;   // first slice of the tail
-        const bool rot_tail = HPW == 1 && cs_g != nullptr && p.rope_dim == 64;
-        SA_LDS uint8_t* rot_row = ob + (lane >> 2) * kOutStride + 2 * r0;
-        const int rot_pairs = cs_g != nullptr && !rot_tail ? p.rope_dim / 2 : 0;
+        // (Rotated pairs in this wave's part of d, d0 .. d0+kEpiD-1: the in-register form needs
+        // the tail of d; the staged form takes pairs rot_lo .. rot_hi-1 of the rotated part.)
+        constexpr int kTail = HPW == 1 ? kEpiBlocks - 4 : kEpiBlocks;     // first slice of the tail
+        const bool rot_tail = HPW == 1 && cs_g != nullptr && p.rope_dim == 64 && d0 + kEpiD == D;
+        SA_LDS uint8_t* rot_row = ob + (lane >> 2) * kOutStride + 2 * (r0 - d0);
+        const int rot_lo = max(0, (d0 - r0) / 2);
+        const int rot_hi = cs_g != nullptr && !rot_tail ? min(p.rope_dim / 2, (d0 + kEpiD - r0) / 2) : 0;
 #pragma unroll
         for (int hb = 0; hb < HPW; ++hb) {
             const float inv_l = l_tot[hb] > 0.0f ? 1.0f / l_tot[hb] : 0.0f;
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db) {
+            for (int db = 0; db < kEpiBlocks; ++db) {
                 const f32x4 o = o_acc[db][hb] * inv_l;
                 uint32_t w[2] = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                 if (db >= kTail) {
@@ -1083,7 +1126,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 *(SA_LDS u32x2*)(ob + l16 * kOutStride + 2 * (16 * db + 4 * q4)) = u32x2{w[0], w[1]};
             }
             // the wave's own LDS accesses complete in order: no barrier between the phases
-            for (int i = lane & 3; i < rot_pairs; i += 4) {
+            for (int i = rot_lo + (lane & 3); i < rot_hi; i += 4) {
                 SA_LDS uint32_t* e = (SA_LDS uint32_t*)(rot_row + 4 * i);
                 const f32x2 cs = *(SA_LDS const f32x2*)(cs_lds + 2 * i);
                 const uint32_t w = *e;
@@ -1113,10 +1156,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int hb = 0; hb < HPW; ++hb) {
             if (head_of(hb) >= p.h) continue;
             const int64_t slot = ((int64_t)qi * p.splits + split) * p.h_pad + head_of(hb);
-            float* wo = p.ws_o + slot * D;
+            float* wo = p.ws_o + slot * D + d0;
 #pragma unroll
-            for (int db = 0; db < G::kDBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db][hb];
-            if (q4 == 0) {
+            for (int db = 0; db < kEpiBlocks; ++db) *(f32x4*)(wo + 16 * db + 4 * q4) = o_acc[db][hb];
+            if (q4 == 0 && d0 == 0) {
                 p.ws_ml[slot * 2 + 0] = m_ref[hb];
                 p.ws_ml[slot * 2 + 1] = l_tot[hb];
             }
@@ -1135,7 +1178,10 @@ inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     constexpr size_t lds = (size_t)KL::kStageCols * 4 + 64 + (size_t)D * 4 + (kTiles > kOut ? kTiles : kOut);
     static_assert(lds <= 160 * 1024, "LDS plan exceeds 160 KB");
     // the key-group merge slots sit behind the output staging area
-    static_assert(KG == 1 || (size_t)(NW / KG) * kHeadsPerWave * (2 * D + 16) +
+    static_assert(KG != 2 || (size_t)NW * kHeadsPerWave * (D + 16) +
+                                 (size_t)NW * (HPW * (G::kDBlocks / 2) * kWave * 16 + HPW * kWave * 8) <= kTiles,
+                  "key-group merge does not fit the tile region");
+    static_assert(KG <= 2 || (size_t)(NW / KG) * kHeadsPerWave * (2 * D + 16) +
                                  (size_t)(KG - 1) * (NW / KG) * (HPW * G::kDBlocks * kWave * 16 + HPW * kWave * 8) <= kTiles,
                   "key-group merge does not fit the tile region");
     auto k = attn_fwd_kernel<D, FP8, NW, HPW, KG>;
