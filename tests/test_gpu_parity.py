@@ -300,10 +300,12 @@ def test_key_groups(sa, seed, b, h, topk, hole):
     """Decode-shaped problems (one query per sequence, d = 512) with long key lists and few
     queries, which the planner gives to key groups (the waves of a workgroup share out each
     query's tiles) instead of splits; ragged tile counts leave groups idle at the end, and a
-    query whose list names nothing leaves every group empty."""
+    query whose list names nothing leaves every group empty, and a query with a single tile
+    leaves every group but the first without rows."""
     _say("key groups", seed, b, h, topk)
     q, kv, sink, idx = W.rand_problem(seed, b, 1, h, 512, 400, topk, hole, False)
     idx[b // 2, 0] = -1
+    idx[b // 3, 0, 20:] = -1          # one tile only: the other key groups have no rows
     scale = float(np.float32(512 ** -0.5))
     args = sa.make_args(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
     assert sa.sparse_attn_workspace_bytes(args) == 0
