@@ -900,7 +900,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             f32x4 s_acc[2][HPW];
             if (it < ntiles) {
                 SA_LDS const int32_t* tidx = istage + it * kTileKeys;
-                valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
+                // this tile's column indices are read before the waits and turned into the
+                // valid-key mask after them, so the LDS read's latency hides behind the waits
+                const int tv = tidx[lane & 31];
                 if constexpr (kFp8Pipe) {
                     using RG = RawGather<D, NW>;
                     if (it + 2 < ntiles) wait_vmcnt<RG::kLoads>();
@@ -917,6 +919,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     if (it + kAh < ntiles)
                         gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
                 }
+                valid = (uint32_t)__ballot(lane < kTileKeys && tv >= 0);
                 pin_offsets();
                 qk(cur, s_acc);
             } else {
