@@ -818,6 +818,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         };
         if (nsuper > 0) gather_super(0);
         for (int su = 0; su < nsuper; ++su) {
+            const int ti = su * KG + kg;
+            // the wave's tile's column indices, read before the waits (the valid-key mask is
+            // formed after them, so the LDS read's latency hides behind the waits)
+            const int tv = ti < ntiles ? istage[ti * kTileKeys + (lane & 31)] : -1;
             wait_vmcnt<0>();
             if constexpr (kFp8Pipe) {
                 lds_barrier();             // super tile su's codes; every wave done with su-1
@@ -832,12 +836,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 lds_barrier();             // super tile su visible to all
                 if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             }
-            const int ti = su * KG + kg;
-            uint32_t valid = 0;
-            if (ti < ntiles) {
-                SA_LDS const int32_t* tix = istage + ti * kTileKeys;
-                valid = (uint32_t)__ballot(lane < kTileKeys && tix[lane & 31] >= 0);
-            }
+            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tv >= 0);
             if (valid != 0) {
                 SA_LDS const uint8_t* cur = tile((su % NS) * KG + kg);
                 pin_offsets();
