@@ -1,24 +1,34 @@
 """Benchmark of the sparse latent attention hot path on one MI355X.
 
 A step is one pass of the whole path over one batch: the window index lists
-(sa_window_topk_idxs) followed by sparse_attn with the inverse-RoPE epilogue, bf16 KV
-storage, on the decode workload by default (32 sequences x 1 query, 64 heads, d 512,
-128-slot ring). Inputs are seeded and synthetic and already resident in HBM.
+(sa_window_topk_idxs) followed by sparse_attn with the inverse-RoPE epilogue. Inputs are
+seeded and synthetic and already resident in HBM.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kv fp8]
+The default run reports the long-context prefill with compression (1 sequence of 8192
+queries, 128 heads, d 512, 128 window + 2048 compressed columns, bf16 storage) as the
+headline line, and in the same JSON line, under "workloads", the other workloads: the
+window-only decode (32 x 1 query, 64 heads, 128-slot ring), the window-only prefill (4096
+queries, 64 heads, window 128) and the window + compressed decode (64 x 1 query, 128
+heads, 640 columns), each with bf16 and with fp8 storage, and the long prefill with fp8
+storage. Each record carries its own roofline and CPU baseline.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME] [--kv bf16|fp8]
 
 Timing:
-  * value / ms_per_step: K steps replayed from one captured HIP graph, bracketed by
-    device synchronisations. The graph walks through enough distinct input sets (each
-    its own q, kv, index and output buffers) that together they exceed twice the 256 MB
-    Infinity Cache, so every step reads its inputs from HBM.
-  * roofline: the attention kernel's own duration, from HIP events recorded on the
-    launch stream around batches of back-to-back calls, after a GPU spin that lets the host
-    enqueue every launch first (no host gaps inside the intervals). achieved = algorithmic
-    bytes (decode) or flops (prefill) per call / average duration. traffic = HBM bytes per
-    call from the committed FETCH_SIZE / WRITE_SIZE counter summary of the same kernel
-    sources (profiles/traffic_*.json), null when the sources have changed since.
-  * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+  * value / ms_per_step: exactly K steps replayed from one captured HIP graph, bracketed by
+    device synchronisations, after W warm-up steps. The steps walk through enough distinct
+    input sets (each its own q, kv, index and output buffers) that together they exceed
+    twice the 256 MB Infinity Cache, and a pass over every set runs before the warm-up, so
+    the timed steps read their inputs from HBM.
+  * roofline: the attention kernel's own duration, from HIP events recorded on the launch
+    stream around batches of back-to-back calls, after a GPU spin that lets the host enqueue
+    every launch first (no host gaps inside the intervals). achieved = algorithmic bytes
+    (HBM-bound workloads: both decodes and the window-only prefill) or flops (the long
+    prefill) per call / average duration. traffic = HBM bytes per call from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary of the same kernel sources
+    (profiles/traffic_*.json), null when the sources have changed since.
+  * cpu_baseline: the CPU oracle (window lists, sparse_attn, inverse RoPE) on a bounded
+    sample of the same workload's queries, scaled to one step.
 One JSON line goes to stdout.
 """
 from __future__ import annotations
@@ -44,6 +54,13 @@ BF16_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4
 MALL_BYTES = 256 << 20
 
 DECODE = {"decode_window", "decode_compress"}
+# the roofline that bounds each workload's kernel (arithmetic intensity against the ridge
+# of 2516.6 TFLOP/s / 8 TB/s = 315 flop/B): the window-only prefill does 126 flop/B
+HBM_BOUND = {"decode_window", "decode_compress", "prefill_window"}
+HEADLINE = ("prefill_compress", "bf16")
+SUB_RECORDS = [("decode_window", "bf16"), ("decode_window", "fp8"), ("prefill_window", "bf16"),
+               ("prefill_window", "fp8"), ("decode_compress", "bf16"), ("decode_compress", "fp8"),
+               ("prefill_compress", "fp8")]
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -128,9 +145,19 @@ def make_sets(w: W.Workload, kv_format: str, touched_bytes: int, dev, epilogue: 
 
 
 # ------------------------------------------------------------------ timing
-def time_graph(sets, steps: int, warmup: int):
-    """Capture one pass over all sets in a HIP graph; replay it to cover warmup and the K
-    timed steps. Returns ms per step."""
+def _capture(stream, calls):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
+    return g
+
+
+def time_steps(sets, steps: int, warmup: int):
+    """Exactly `steps` timed steps, replayed from one captured HIP graph. Before them: one
+    pass over every input set (so each timed step's set was last touched more than twice the
+    Infinity Cache ago), then `warmup` steps on the sets the timed steps use last. Returns
+    ms per step."""
     n = len(sets)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -139,21 +166,19 @@ def time_graph(sets, steps: int, warmup: int):
             s.run()
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for s in sets:
-            s.run()
+    g_all = _capture(stream, [s.run for s in sets])
+    g_warm = _capture(stream, [sets[(n - 1 - i) % n].run for i in range(warmup)]) if warmup > 0 else None
+    g_timed = _capture(stream, [sets[i % n].run for i in range(steps)])
     torch.cuda.synchronize()
-    for _ in range(max(1, math.ceil(warmup / n))):
-        g.replay()
+    g_all.replay()
+    if g_warm is not None:
+        g_warm.replay()
     torch.cuda.synchronize()
-    reps = max(1, math.ceil(steps / n))
     t0 = time.perf_counter()
-    for _ in range(reps):
-        g.replay()
+    g_timed.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    return dt * 1e3 / (reps * n), reps * n, g
+    return dt * 1e3 / steps
 
 
 def time_kernel(sets, calls: int):
@@ -185,39 +210,71 @@ def time_kernel(sets, calls: int):
     return float(np.mean(per)), float(np.min(per))
 
 
-def cpu_baseline(w: W.Workload, kv_format: str, alg, budget_s: float = 12.0, rope: bool = True):
-    """The oracle (plain C, OpenMP over queries) on a bounded sample of queries, scaled to
-    the metric's unit."""
+_CPU_CACHE = {}
+
+
+def cpu_step_seconds(w: W.Workload, budget_s: float, rope: bool = True):
+    """Seconds one step takes the oracle (plain C, OpenMP over queries) on the host: window
+    lists, sparse_attn and the inverse RoPE of a bounded sample of queries, scaled to all
+    queries. The kv rows are stored round-tripped before the timed region, as on the GPU.
+    Cached per workload (the storage format does not change the oracle's work)."""
+    key = (w.name, rope)
+    if key in _CPU_CACHE:
+        return _CPU_CACHE[key]
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
-    from sa_harness import oracle_indices, oracle_run  # noqa: F401
+    from sa_harness import oracle_kv, u16
     nq = w.b * w.s
     threads = oracle.max_threads()
-    # per-query cost estimate from one query, then a sample sized to the budget
+    sp = None if w.win_start_pos is None else w.win_start_pos.numpy()
+    win = oracle.window_topk_idxs(w.window, w.win_seqlen, sp, nseq=w.win_nseq).reshape(w.b, w.s, -1)
+    idx = win if w.comp_idx is None else np.ascontiguousarray(np.concatenate([win, w.comp_idx.numpy()], -1))
+
+    def sample(n):
+        return np.unique(np.linspace(0, nq - 1, n).round().astype(np.int64))
+
+    q16, sink = u16(w.q), w.sink.numpy()
+    cs = oracle.freqs_cis(w.rd, w.max_pos, w.rope_base) if rope else None
+    pos = w.pos.numpy().reshape(-1)
+
+    def run(sel, kv):
+        sp_ = None if w.win_start_pos is None else w.win_start_pos.numpy()
+        oracle.window_topk_idxs(w.window, w.win_seqlen, sp_, nseq=w.win_nseq)
+        out = oracle.sparse_attn(q16, kv, sink, idx, w.scale, qsel=sel, nthreads=threads)
+        if rope:
+            oracle.apply_rotary(out, w.rd, cs, pos[sel], inverse=True)
+
+    # per-query cost from one query, then a sample sized to the budget
+    one_sel = np.array([nq - 1])
+    kv1 = oracle_kv(w, w.kv_roundtrip, [int(nq - 1) // w.s], idx, one_sel)
     t0 = time.perf_counter()
-    oracle_run(w, qsel=np.array([nq - 1]), rope=rope, round_trip=w.kv_roundtrip, nthreads=1)
+    run(one_sel, kv1)
     one = time.perf_counter() - t0
-    n = int(max(1, min(nq, budget_s * threads / max(one, 1e-6))))
-    sel = np.linspace(0, nq - 1, n).round().astype(np.int64)
-    sel = np.unique(sel)
-    # when the whole step is cheaper than the budget, repeat it (at least 2 s of work)
+    sel = sample(int(max(1, min(nq, budget_s * threads / max(one, 1e-6)))))
+    kv = oracle_kv(w, w.kv_roundtrip, sorted({int(i) // w.s for i in sel}), idx, sel)
     reps = 1
     t0 = time.perf_counter()
-    while True:
-        oracle_run(w, qsel=sel, rope=rope, round_trip=w.kv_roundtrip, nthreads=threads)
+    while True:                      # a step cheaper than the budget is repeated (>= 2 s of work)
+        run(sel, kv)
         dt = time.perf_counter() - t0
         if sel.size < nq or dt >= 2.0 or reps >= 100:
             break
         reps += 1
     per_step = dt / reps * nq / sel.size
+    _CPU_CACHE[key] = (per_step, sel.size, nq, reps, dt, threads)
+    return _CPU_CACHE[key]
+
+
+def cpu_baseline(w: W.Workload, alg, budget_s: float, rope: bool = True):
+    per_step, n, nq, reps, dt, threads = cpu_step_seconds(w, budget_s, rope)
     if w.name in DECODE:
         value, unit = alg["kv_bytes"] / per_step / 1e9, "GB/s"
     else:
         value, unit = alg["flops"] / per_step / 1e12, "TFLOP/s"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{sel.size} of {nq} queries (all heads) x {reps} run(s), oracle incl. "
-                      f"fp8 round trip of their rows, window lists{' and inverse RoPE' if rope else ''}; {dt:.1f} s "
-                      f"wall, scaled to one step"}
+            "sample": f"{n} of {nq} queries (all heads) x {reps} run(s): window lists, "
+                      f"sparse_attn{' and inverse RoPE' if rope else ''}; {dt:.1f} s wall, "
+                      f"scaled to one step"}
 
 
 # ------------------------------------------------------------------ HBM traffic counters
@@ -312,25 +369,88 @@ def pmc_summary(workload: str, kv: str, fetch_csv: str, write_csv: str):
     print(json.dumps(rec, indent=1))
 
 
+def prepare(w: W.Workload, kv: str, dev, epilogue: bool):
+    """The algorithmic counts of one step (from the library's own index lists) and the
+    device input sets."""
+    probe_idx = torch.empty(w.b, w.s, w.topk, dtype=torch.int32, device=dev)
+    view = probe_idx.view(w.win_nseq, w.win_seqlen, w.topk)
+    sa.window_topk_idxs(w.window, w.win_seqlen, w.win_nseq,
+                        start_pos=None if w.win_start_pos is None else w.win_start_pos.to(dev), out=view)
+    if w.comp_idx is not None:
+        probe_idx[:, :, w.win_cols:] = w.comp_idx.to(dev)
+    alg = algorithmic(w, probe_idx.cpu().numpy(), kv, epilogue=epilogue)
+    del probe_idx
+    return alg, make_sets(w, kv, alg["attn_bytes"], dev, epilogue=epilogue)
+
+
+def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool,
+            cpu_budget_s: float | None):
+    """One record: step rate, kernel roofline and CPU baseline of workload w with storage kv."""
+    alg, sets = prepare(w, kv, dev, epilogue)
+    ms_step = time_steps(sets, steps, warmup)
+    k_mean, k_best = time_kernel(sets, calls=min(400, max(50, steps * 5 if w.name in DECODE else steps)))
+    if w.name in DECODE:
+        value = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
+        metric, unit = "sparse_attn KV GB/s (decode)", "GB/s"
+    else:
+        value = alg["flops"] / (ms_step * 1e-3) / 1e12
+        metric, unit = "sparse_attn TFLOP/s (prefill)", "TFLOP/s"
+    if w.name in HBM_BOUND:
+        achieved = alg["attn_bytes"] / (k_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = alg["flops"] / (k_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+    roof["traffic"] = stored_traffic(w.name, kv) if epilogue else None
+    roof["kernel"] = "sparse_attn (attn_fwd_kernel [+ attn_combine_kernel])"
+    roof["kernel_ms_mean"] = k_mean
+    roof["kernel_ms_best_batch"] = k_best
+    roof["algorithmic_bytes_per_launch"] = alg["attn_bytes"]
+    roof["algorithmic_flops_per_launch"] = alg["flops"]
+    if w.name == "prefill_window":
+        roof["mfma_frac"] = alg["flops"] / (k_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    cpu = cpu_baseline(w, alg, cpu_budget_s, rope=epilogue) if cpu_budget_s else None
+    del sets
+    torch.cuda.empty_cache()
+    return {
+        "metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step, "steps": steps,
+        "dtype": "bf16" if kv == "bf16" else "fp8-e4m3 storage, bf16 compute",
+        "config": {"workload": w.name, "sequences": w.b, "queries_per_sequence": w.s, "heads": w.h,
+                   "head_dim": w.d, "rope_dim": w.rd, "topk": w.topk, "kv_rows_per_sequence": w.kv_rows,
+                   "kv_storage": kv, "epilogue": "inverse RoPE" if epilogue else "none",
+                   "kv_bytes_per_step": alg["kv_bytes"], "distinct_kv_rows": alg["distinct_rows"],
+                   "valid_pairs": alg["valid_pairs"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode_window", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(W.WORKLOADS))
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="storage of a single --workload (the default run times both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="time sparse_attn without the inverse-RoPE epilogue (plain bf16 output)")
     ap.add_argument("--profile-calls", type=int, default=0,
-                    help="counter-collection mode: N eager steps over the input sets, then "
-                         "the copy kernel of known size that calibrates the byte counters; "
-                         "no timing, no JSON line")
+                    help="counter-collection mode (single --workload): N eager steps over the "
+                         "input sets, then the copy kernel of known size that calibrates the "
+                         "byte counters; no timing, no JSON line")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "--profile-calls into profiles/traffic_<workload>_<kv>.json")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
     if args.pmc_summary:
+        if args.workload == "all":
+            ap.error("--pmc-summary needs --workload")
         pmc_summary(args.workload, args.kv, *args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -340,64 +460,51 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sa.lib()
+    epilogue = not args.no_epilogue
 
-    w = W.make(args.workload)
-    sets = None
-    # the reference step's index lists, for the algorithmic counts
-    probe_idx = torch.empty(w.b, w.s, w.topk, dtype=torch.int32, device=dev)
-    view = probe_idx.view(w.win_nseq, w.win_seqlen, w.topk)
-    sa.window_topk_idxs(w.window, w.win_seqlen, w.win_nseq,
-                        start_pos=None if w.win_start_pos is None else w.win_start_pos.to(dev), out=view)
-    if w.comp_idx is not None:
-        probe_idx[:, :, w.win_cols:] = w.comp_idx.to(dev)
-    alg = algorithmic(w, probe_idx.cpu().numpy(), args.kv, epilogue=not args.no_epilogue)
-    del probe_idx
-
-    sets = make_sets(w, args.kv, alg["attn_bytes"], dev, epilogue=not args.no_epilogue)
     if args.profile_calls:
+        if args.workload == "all":
+            ap.error("--profile-calls needs --workload")
+        _, sets = prepare(W.make(args.workload), args.kv, dev, epilogue)
         profile_pass(sets, args.profile_calls, dev)
         return
-    ms_step, timed_steps, _g = time_graph(sets, args.steps, args.warmup)
-    k_mean, k_best = time_kernel(sets, calls=min(400, max(50, args.steps // 5)))
 
-    decode = w.name in DECODE
-    if decode:
-        value = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
-        metric, unit = "sparse_attn KV GB/s (decode)", "GB/s"
-        achieved = alg["attn_bytes"] / (k_mean * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    cpu = not args.no_cpu_baseline
+    if args.workload != "all":
+        head = (args.workload, args.kv)
+        subs = []
     else:
-        value = alg["flops"] / (ms_step * 1e-3) / 1e12
-        metric, unit = "sparse_attn TFLOP/s (prefill)", "TFLOP/s"
-        achieved = alg["flops"] / (k_mean * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None}
-    roof["traffic"] = stored_traffic(w.name, args.kv)
-    roof["kernel"] = "sparse_attn (attn_fwd_kernel [+ attn_combine_kernel])"
-    roof["kernel_ms_mean"] = k_mean
-    roof["kernel_ms_best_batch"] = k_best
-    roof["algorithmic_bytes_per_launch"] = alg["attn_bytes"]
-    roof["algorithmic_flops_per_launch"] = alg["flops"]
+        head, subs = HEADLINE, SUB_RECORDS
+    t_start = time.perf_counter()
+    made = {}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.kv, alg, rope=not args.no_epilogue)
+    def workload(name):
+        if name not in made:
+            made.clear()
+            made[name] = W.make(name)
+        return made[name]
 
-    rec = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": timed_steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if args.kv == "bf16" else "fp8-e4m3 storage, bf16 compute",
-        "data": "synthetic",
-        "config": {"workload": w.name, "sequences": w.b, "queries_per_sequence": w.s, "heads": w.h,
-                   "head_dim": w.d, "rope_dim": w.rd, "topk": w.topk, "kv_rows_per_sequence": w.kv_rows,
-                   "kv_storage": args.kv, "epilogue": "none" if args.no_epilogue else "inverse RoPE", "input_sets": len(sets),
-                   "kv_bytes_per_step": alg["kv_bytes"], "distinct_kv_rows": alg["distinct_rows"],
-                   "valid_pairs": alg["valid_pairs"]},
-        "roofline": roof,
-        "cpu_baseline": cpu,
+    records = []
+    # sub-records first, grouped by workload; the headline's workload last (shared draws)
+    for name, kv in subs:
+        rec = measure(workload(name), kv, dev, args.steps, args.warmup, epilogue, 4.0 if cpu else None)
+        records.append(rec)
+        print(f"[bench] {name} {kv}: {rec['value']:.4g} {rec['unit']}, kernel "
+              f"{rec['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {rec['roofline']['frac']:.3f} of "
+              f"{rec['roofline']['bound']} ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+    rec = measure(workload(head[0]), head[1], dev, args.steps, args.warmup, epilogue, 15.0 if cpu else None)
+    print(f"[bench] {head[0]} {head[1]}: {rec['value']:.4g} {rec['unit']} "
+          f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+    line = {
+        "metric": rec["metric"], "value": rec["value"], "unit": rec["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec["dtype"],
+        "data": "synthetic", "config": rec["config"], "roofline": rec["roofline"],
+        "cpu_baseline": rec["cpu_baseline"],
     }
-    print(json.dumps(rec))
+    if records:
+        line["workloads"] = records
+    print(json.dumps(line))
 
 
 if __name__ == "__main__":

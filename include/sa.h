@@ -143,6 +143,21 @@ int sa_window_topk_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int3
 int sa_quant_kv_fp8(const void *kv, int64_t rows, int32_t d, uint8_t *e4m3_out,
                     uint8_t *e8m0_out, void *bf16_out, void *stream);
 
+/* The (cos, sin) table that the inverse-RoPE epilogue reads (rope_cos_sin above):
+ * precompute_freqs_cis of Attention.__init__ (atlas.klimoza.dev/.../attention/output,
+ * precompute_freqs_cis; attention API docs, "freqs_cis"), evaluated on the device with the
+ * page's f32 roundings. Pair i of the rope tail has frequency f_i = 1 / base^(2i/rope_dim);
+ * with original_seq_len > 0 the YaRN correction of the same function blends f_i towards
+ * f_i / factor across the pairs between those that complete beta_fast and beta_slow turns
+ * over original_seq_len positions (original_seq_len = 0: no YaRN, the ratio-0 layers'
+ * form). Entry p of the table is (cos, sin) of the f32 angle p * f_i.
+ *   cos_sin: device f32 [max_pos][rope_dim/2][2], caller-owned, 8-byte aligned.
+ *   rope_dim even and >= 2, max_pos >= 1, base > 1 and finite; with YaRN also factor > 0
+ *   and beta_fast > beta_slow > 0 (the model config's 16, 32 and 1). Errors:
+ *   SA_ERR_INVALID for any other argument. */
+int sa_rope_table(int32_t rope_dim, int32_t max_pos, int32_t original_seq_len, float base,
+                  float factor, float beta_fast, float beta_slow, float *cos_sin, void *stream);
+
 /* A static description of a status code. */
 const char *sa_status_string(int status);
 

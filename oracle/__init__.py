@@ -17,19 +17,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sa_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SA_ORACLE_LIB names another build of the same source (the sanitizer build of the tests)
+_LIB_PATH = os.environ.get("SA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction, OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+
+def build(force: bool = True, out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction, OpenMP). With
+    sanitize, an AddressSanitizer + UndefinedBehaviorSanitizer build at -O1 (load it with
+    libasan preloaded)."""
+    out = out or _LIB_PATH
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+        cmd = ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
                "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, out)
+    return out
 
 
 class AttnProblem(C.Structure):
@@ -69,6 +77,7 @@ def lib():
             "orc_sparse_attn_f64": (C.c_int, [C.POINTER(AttnProblem), P, I64, P, I32]),
             "orc_sparse_attn_weights_f64": (C.c_int, [C.POINTER(AttnProblem), I64, I32, P, P]),
             "orc_freqs_cis": (None, [I32, I32, F, P]),
+            "orc_freqs_cis_yarn": (C.c_int, [I32, I32, I32, F, F, F, F, P]),
             "orc_apply_rotary": (C.c_int, [P, I64, I32, I32, I32, P, I32, P, I32]),
             "orc_max_threads": (I32, []),
         }
@@ -151,15 +160,22 @@ def fp8_storage_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- window indices / ring
-def window_topk_idxs(window: int, seqlen: int, start_pos) -> np.ndarray:
-    """int32 [nseq][seqlen][cols]; raises on the cases the oracle rejects."""
-    sp = np.ascontiguousarray(np.atleast_1d(np.asarray(start_pos, np.int32)))
+def window_topk_idxs(window: int, seqlen: int, start_pos=None, nseq: int = 1) -> np.ndarray:
+    """int32 [nseq][seqlen][cols]. start_pos None: prefill of nseq sequences from position 0;
+    otherwise a decode step, one position per sequence. Raises on the cases the oracle
+    rejects."""
+    if start_pos is None:
+        sp, n = None, nseq
+    else:
+        sp = np.ascontiguousarray(np.atleast_1d(np.asarray(start_pos, np.int32)))
+        n = sp.size
+    spp = None if sp is None else _ptr(sp)
     cols = np.zeros(1, np.int32)
-    rc = lib().orc_window_cols(window, seqlen, _ptr(sp), sp.size, _ptr(cols))
+    rc = lib().orc_window_cols(window, seqlen, spp, n, _ptr(cols))
     if rc:
         raise ValueError(f"window_topk_idxs: status {rc}")
-    out = np.empty((sp.size, seqlen, int(cols[0])), np.int32)
-    rc = lib().orc_window_topk_idxs(window, seqlen, _ptr(sp), sp.size, _ptr(out), _ptr(cols))
+    out = np.empty((n, seqlen, int(cols[0])), np.int32)
+    rc = lib().orc_window_topk_idxs(window, seqlen, spp, n, _ptr(out), _ptr(cols))
     if rc:
         raise ValueError(f"window_topk_idxs: status {rc}")
     return out
@@ -232,9 +248,17 @@ def sparse_attn_weights_f64(q, kv, sink, idx, scale, query: int, head: int):
 
 
 # ---------------------------------------------------------------- rotary
-def freqs_cis(rd: int, max_pos: int, base: float = 10000.0) -> np.ndarray:
+def freqs_cis(rd: int, max_pos: int, base: float = 10000.0, original_seq_len: int = 0,
+              factor: float = 1.0, beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """f32 [max_pos][rd/2][2] of (cos, sin); YaRN when original_seq_len > 0."""
     out = np.empty((max_pos, rd // 2, 2), np.float32)
-    lib().orc_freqs_cis(rd, max_pos, float(base), _ptr(out))
+    if original_seq_len == 0:
+        lib().orc_freqs_cis(rd, max_pos, float(base), _ptr(out))
+        return out
+    rc = lib().orc_freqs_cis_yarn(rd, max_pos, original_seq_len, float(base), float(factor),
+                                  float(beta_fast), float(beta_slow), _ptr(out))
+    if rc:
+        raise ValueError("orc_freqs_cis_yarn rejected its arguments")
     return out
 
 

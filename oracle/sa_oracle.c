@@ -176,19 +176,23 @@ int orc_fp8_storage_decode(const uint8_t *codes, const uint8_t *scale_bytes, int
 /* Readings: prefill cols = min(seqlen, window) (the list is [queries][cols], not        */
 /* [queries][window]); valid entries come first, oldest first, -1 padding at the end;    */
 /* decode lets every sequence carry its own start position; start_pos > 0 with more than */
-/* one query (chunked prefill) is not defined by the pages and is rejected.              */
+/* one query (chunked prefill) is not defined by the pages and is rejected. The mode is  */
+/* the caller's, as on the pages (prefill vs decode): start_pos == NULL is a prefill     */
+/* from position 0, start_pos != NULL a decode step, whose list is the whole ring        */
+/* (cols = window) at any position, P = 0 included (the ring then holds token 0 only).   */
 /* ------------------------------------------------------------------------------------ */
 int orc_window_cols(int32_t window, int32_t seqlen, const int32_t *start_pos, int32_t nseq,
                     int32_t *cols)
 {
-    if (window <= 0 || seqlen <= 0 || nseq <= 0 || !start_pos || !cols) return -1;
-    int any_pos = 0;
-    for (int32_t n = 0; n < nseq; ++n) {
-        if (start_pos[n] < 0) return -1;
-        if (start_pos[n] > 0) any_pos = 1;
+    if (window <= 0 || seqlen <= 0 || nseq <= 0 || !cols) return -1;
+    if (start_pos) {
+        for (int32_t n = 0; n < nseq; ++n)
+            if (start_pos[n] < 0) return -1;
+        if (seqlen > 1) return -2;                       /* chunked prefill: undefined */
+        *cols = window;
+    } else {
+        *cols = seqlen < window ? seqlen : window;
     }
-    if (any_pos && seqlen > 1) return -2;
-    *cols = any_pos ? window : (seqlen < window ? seqlen : window);
     return 0;
 }
 
@@ -201,16 +205,16 @@ int orc_window_topk_idxs(int32_t window, int32_t seqlen, const int32_t *start_po
     if (!idx) return -1;
     *cols = c;
     for (int32_t n = 0; n < nseq; ++n) {
-        int32_t P = start_pos[n];
         for (int32_t t = 0; t < seqlen; ++t) {
             int32_t *row = idx + ((int64_t)n * seqlen + t) * c;
-            if (P == 0 && seqlen > 1) {
+            if (!start_pos) {
                 /* prefill: chunk rows lo..t, lo = max(0, t - window + 1) */
                 int32_t lo = t - window + 1 > 0 ? t - window + 1 : 0;
                 for (int32_t j = 0; j < c; ++j) row[j] = (lo + j <= t) ? lo + j : -1;
-            } else if (P == 0 && seqlen == 1 && c == 1) {
-                row[0] = 0;                              /* a one-token prefill */
-            } else if (P >= window - 1) {
+                continue;
+            }
+            int32_t P = start_pos[n];
+            if (P >= window - 1) {
                 /* full ring: the oldest token P-window+1 sits in slot (P+1) mod window */
                 for (int32_t j = 0; j < c; ++j) row[j] = (P + 1 + j) % window;
             } else {
@@ -427,21 +431,62 @@ int orc_sparse_attn_weights_f64(const orc_attn_problem *p, int64_t query, int32_
 }
 
 /* ------------------------------------------------------------------------------------ */
-/* Rotary table. [attn-fwd] precompute_freqs_cis with original_seq_len = 0 (the no-YaRN  */
-/* form that [attn-docs] freqs_cis names): freq_i = 1 / base^(2i/rd), angle = pos *      */
-/* freq_i, entry = (cos, sin) of the angle. Computed in f32 as the page does.           */
+/* Rotary table. [attn-fwd] precompute_freqs_cis: freq_i = 1 / base^(2i/rd) for pair i,  */
+/* angle = pos * freq_i, entry = (cos, sin) of the angle, everything in f32 as the page's */
+/* torch code computes it (one rounding per operation, no fused multiply-add). With      */
+/* original_seq_len > 0, the YaRN correction of the same function: corrected_dim(r) is   */
+/* the pair index whose wavelength fits r times into original_seq_len; pairs below       */
+/* low = max(floor(corrected_dim(beta_fast)), 0) keep their frequency, pairs above        */
+/* high = min(ceil(corrected_dim(beta_slow)), rd - 1) are divided by factor, and a linear */
+/* ramp blends the two in between. The band limits are computed in f64 (the page uses    */
+/* Python's math module for them), the rest in f32. [attn-docs] freqs_cis names the      */
+/* no-YaRN form (original_seq_len = 0) for the ratio-0 layers.                            */
 /* ------------------------------------------------------------------------------------ */
-void orc_freqs_cis(int32_t rd, int32_t max_pos, float base, float *cos_sin)
+static double yarn_corrected_dim(int32_t rd, int32_t original_seq_len, double rotations,
+                                 double base)
 {
+    const double pi = 3.14159265358979323846;
+    return rd * log((double)original_seq_len / (rotations * 2.0 * pi)) / (2.0 * log(base));
+}
+
+int orc_freqs_cis_yarn(int32_t rd, int32_t max_pos, int32_t original_seq_len, float base,
+                       float factor, float beta_fast, float beta_slow, float *cos_sin)
+{
+    if (rd < 2 || rd % 2 || max_pos < 1 || !cos_sin || !(base > 0.0f)) return -1;
     const int32_t half = rd / 2;
-    for (int32_t i = 0; i < half; ++i) {
-        float freq = 1.0f / powf(base, (float)(2 * i) / (float)rd);
-        for (int32_t pos = 0; pos < max_pos; ++pos) {
-            float ang = (float)pos * freq;
+    float *freq = (float *)malloc(sizeof(float) * (size_t)half);
+    if (!freq) return -1;
+    for (int32_t i = 0; i < half; ++i)
+        freq[i] = 1.0f / powf(base, (float)(2 * i) / (float)rd);
+    if (original_seq_len > 0) {
+        double lo = floor(yarn_corrected_dim(rd, original_seq_len, beta_fast, base));
+        double hi = ceil(yarn_corrected_dim(rd, original_seq_len, beta_slow, base));
+        int32_t low = lo > 0.0 ? (int32_t)lo : 0;
+        int32_t high = hi < (double)(rd - 1) ? (int32_t)hi : rd - 1;
+        float span = high - low > 0 ? (float)(high - low) : 1e-3f;   /* max(high - low, 1e-3) */
+        for (int32_t i = 0; i < half; ++i) {
+            float ramp = ((float)i - (float)low) / span;
+            if (ramp < 0.0f) ramp = 0.0f;
+            if (ramp > 1.0f) ramp = 1.0f;
+            float smooth = 1.0f - ramp;
+            float scaled = freq[i] / factor * (1.0f - smooth);
+            float kept = freq[i] * smooth;
+            freq[i] = scaled + kept;
+        }
+    }
+    for (int32_t pos = 0; pos < max_pos; ++pos)
+        for (int32_t i = 0; i < half; ++i) {
+            float ang = (float)pos * freq[i];
             cos_sin[((int64_t)pos * half + i) * 2 + 0] = cosf(ang);
             cos_sin[((int64_t)pos * half + i) * 2 + 1] = sinf(ang);
         }
-    }
+    free(freq);
+    return 0;
+}
+
+void orc_freqs_cis(int32_t rd, int32_t max_pos, float base, float *cos_sin)
+{
+    orc_freqs_cis_yarn(rd, max_pos, 0, base, 1.0f, 32.0f, 1.0f, cos_sin);
 }
 
 /* ------------------------------------------------------------------------------------ */

@@ -54,9 +54,11 @@ int orc_fp8_storage_decode(const uint8_t *codes, const uint8_t *scale_bytes, int
                            int32_t d, uint16_t *y);
 
 /* ---- window index lists ([attn-docs] window_topk_idxs and ring-cache paragraph) ----
- * Writes idx [nseq][seqlen][cols] and *cols. Prefill (every start_pos == 0):
- * cols = min(seqlen, window). Decode (seqlen == 1 and some start_pos > 0): cols = window.
- * Returns 0, -1 on invalid arguments, -2 for start_pos > 0 with seqlen > 1 (undefined). */
+ * Writes idx [nseq][seqlen][cols] and *cols. Prefill (start_pos == NULL, every sequence
+ * from position 0): cols = min(seqlen, window). Decode (start_pos != NULL, one position
+ * P >= 0 per sequence, seqlen == 1): cols = window.
+ * Returns 0, -1 on invalid arguments, -2 for a decode call with seqlen > 1 (a chunked
+ * prefill, which the pages do not define). */
 int orc_window_topk_idxs(int32_t window, int32_t seqlen, const int32_t *start_pos, int32_t nseq,
                          int32_t *idx, int32_t *cols);
 /* query the column count only (same rules) */
@@ -97,6 +99,10 @@ int orc_sparse_attn_weights_f64(const orc_attn_problem *p, int64_t query, int32_
 /* ---- rotary table ([attn-fwd] precompute_freqs_cis without YaRN; [attn-docs] freqs_cis)
  * cos_sin: f32 [max_pos][rd/2][2] = (cos, sin) of pos * base^(-2i/rd), computed in f32. */
 void orc_freqs_cis(int32_t rd, int32_t max_pos, float base, float *cos_sin);
+/* the same with the YaRN correction of precompute_freqs_cis when original_seq_len > 0
+ * (factor, beta_fast, beta_slow as the page names them). Returns 0, or -1. */
+int orc_freqs_cis_yarn(int32_t rd, int32_t max_pos, int32_t original_seq_len, float base,
+                       float factor, float beta_fast, float beta_slow, float *cos_sin);
 
 /* ---- rotary ([attn-fwd] apply_rotary_emb; [attn-docs] apply_rotary) on the last rd
  * elements of every d-wide row of x (bf16 [n][h][d], in place); row i at position pos[i].

@@ -76,6 +76,8 @@ def lib():
         L.sa_sparse_attn_workspace.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
         L.sa_window_topk_idxs.restype = C.c_int
         L.sa_window_topk_idxs.argtypes = [I32, I32, I32, P, P, I64, I64, C.POINTER(I32), P]
+        L.sa_rope_table.restype = C.c_int
+        L.sa_rope_table.argtypes = [I32, I32, I32, C.c_float, C.c_float, C.c_float, C.c_float, P, P]
         L.sa_quant_kv_fp8.restype = C.c_int
         L.sa_quant_kv_fp8.argtypes = [P, I64, I32, P, P, P, P]
         if L.sa_abi_version() != 1:
@@ -242,11 +244,17 @@ def quant_kv_fp8(kv, *, codes=None, scales=None, roundtrip=None, want=("codes", 
     return tuple(res[w] for w in want)
 
 
-def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda"):
-    """The caller's (cos, sin) table of the inverse-RoPE epilogue, f32 [max_pos][rd/2][2]:
-    precompute_freqs_cis without YaRN (Attention.__init__ for ratio-0 layers), evaluated as
-    the page does, in f32 torch arithmetic, then copied to the device."""
-    freqs = 1.0 / (base ** (torch.arange(0, rope_dim, 2, dtype=torch.float32) / rope_dim))
-    ang = torch.outer(torch.arange(max_pos, dtype=torch.float32), freqs)
-    fc = torch.polar(torch.ones_like(ang), ang)
-    return torch.view_as_real(fc).contiguous().to(device)
+def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda", *,
+               original_seq_len: int = 0, factor: float = 1.0, beta_fast: float = 32.0,
+               beta_slow: float = 1.0, out=None):
+    """The (cos, sin) table of the inverse-RoPE epilogue, f32 [max_pos][rope_dim/2][2],
+    computed by sa_rope_table on the device (include/sa.h)."""
+    if out is None:
+        out = torch.empty(max_pos, rope_dim // 2, 2, dtype=torch.float32, device=device)
+    _need(out, torch.float32, "out")
+    if not out.is_contiguous() or tuple(out.shape) != (max_pos, rope_dim // 2, 2):
+        raise ValueError("out must be a contiguous f32 [max_pos][rope_dim/2][2]")
+    _check("sa_rope_table", lib().sa_rope_table(
+        rope_dim, max_pos, original_seq_len, base, factor, beta_fast, beta_slow, _ptr(out),
+        C.c_void_p(_stream(out.device))))
+    return out

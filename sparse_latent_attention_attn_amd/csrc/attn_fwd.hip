@@ -75,8 +75,9 @@ static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int kg
     hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, kg, blocks, st)
                        : launch_fwd_nw<D, false>(p, nw, hpw, kg, blocks, st);
     if (e != hipSuccess || p.splits == 1) return e;
-    const int waves = p.b * p.s * p.h;
-    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((waves + 3) / 4), dim3(256), 0, st, p);
+    // one wave per (query, head); the host keeps b * s * h within int32 for split plans
+    const int64_t waves = (int64_t)p.b * p.s * p.h;
+    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -81,9 +81,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 // every such load in flight before each LDS read and each barrier, which serialises the
 // tile pipeline. Completion is tracked here with explicit vmcnt waits instead (wait_vmcnt),
 // and the "memory" clobber keeps the compiler from moving LDS accesses across the issue.
+// M0 is an operand ("{m0}"), so the compiler itself writes it and knows it is changed; the
+// s_nop covers the wait state between an M0 write and an LDS-DMA load.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(lds) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
@@ -570,9 +572,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     float m_ref[HPW], m_seen[HPW], l_run[HPW];                 // log2 domain, per head
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
-        m_ref[hb] = sink2[hb];
+        // finite even for a sink of -inf, so that exp2(score - m_ref) of a skipped key (-inf)
+        // is 0 and never NaN before the first tile with a row sets the reference
+        m_ref[hb] = fmaxf(sink2[hb], -FLT_MAX);
         m_seen[hb] = -INFINITY;                                // this lane's maximum score
-        l_run[hb] = sink_lane ? 1.0f : 0.0f;                   // exp2(sink2 - m_ref)
+        l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
     }
     bool have_ref = false;                                     // same in all lanes of a wave
     bool over = false;                                         // a score passed m_ref + kSlack
@@ -963,7 +967,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     __syncthreads();                                           // every wave has read the flag
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
-        m_ref[hb] = fmaxf(sink2[hb], max4groups(m_seen[hb]));
+        // finite also for a key group that saw no row while another one flagged the pass
+        m_ref[hb] = fmaxf(fmaxf(sink2[hb], max4groups(m_seen[hb])), -FLT_MAX);
         l_run[hb] = sink_lane ? fast_exp2(sink2[hb] - m_ref[hb]) : 0.0f;
     }
     have_ref = true;

@@ -145,4 +145,46 @@ hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ rotary table
+// precompute_freqs_cis (attention output page; the attention API docs, "freqs_cis"): pair
+// i of the rope tail turns at f_i = 1 / base^(2i/rope_dim) per position, optionally with the
+// YaRN blend towards f_i / factor between pairs low and high (band limits from the host);
+// entry (p, i) = (cos, sin) of the f32 angle p * f_i. Every step is rounded to f32 as the
+// page's torch code does, with no contraction into fused multiply-adds; base^e is evaluated
+// in f64 and rounded (the correctly rounded f32 power), cos and sin in f64 and rounded.
+__global__ __launch_bounds__(256) void rope_table_kernel(int32_t rope_dim, int32_t max_pos, float base, int32_t yarn,
+                                                         int32_t low, int32_t high, float factor,
+                                                         float* __restrict__ cs) {
+#pragma clang fp contract(off)
+    const int32_t half = rope_dim / 2;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)max_pos * half) return;
+    const int32_t i = (int32_t)(e % half);
+    const int32_t pos = (int32_t)(e / half);
+    const float expo = (float)(2 * i) / (float)rope_dim;
+    const float pw = (float)pow((double)base, (double)expo);
+    float f = 1.0f / pw;
+    if (yarn) {
+        const float span = high - low > 0 ? (float)(high - low) : 1e-3f;
+        const float ramp = fminf(fmaxf(((float)i - (float)low) / span, 0.0f), 1.0f);
+        const float smooth = 1.0f - ramp;
+        const float scaled = f / factor * (1.0f - smooth);
+        const float kept = f * smooth;
+        f = scaled + kept;
+    }
+    const float ang = (float)pos * f;
+    cs[2 * e + 0] = (float)cos((double)ang);
+    cs[2 * e + 1] = (float)sin((double)ang);
+}
+
+hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int32_t yarn, int32_t low,
+                             int32_t high, float factor, float* cs, hipStream_t st) {
+    const int64_t n = (int64_t)max_pos * (rope_dim / 2);
+    const int64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)grid), dim3(256), 0, st, rope_dim, max_pos, base, yarn,
+                       low, high, factor, cs);
+    return hipGetLastError();
+}
+
 }  // namespace sa

@@ -180,10 +180,12 @@ SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
     rc = check_pointers(a);
     if (rc != SA_OK) return rc;
     const sa::Plan pl = make_plan(a, cu_count());
-    if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 16)))
-        return SA_ERR_WORKSPACE;
     const int64_t blocks = (int64_t)a->b * a->s * pl.head_blocks * pl.splits;
     if (blocks > INT32_MAX) return SA_ERR_UNSUPPORTED;
+    // the combine kernel of a split plan indexes its waves, one per (query, head), in int32
+    if (pl.splits > 1 && (int64_t)a->b * a->s * a->h > INT32_MAX - 3) return SA_ERR_UNSUPPORTED;
+    if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 16)))
+        return SA_ERR_WORKSPACE;
 
     sa::KParams p{};
     p.b = a->b; p.s = a->s; p.h = a->h; p.d = a->d; p.topk = a->topk; p.kv_rows = a->kv_rows;
@@ -233,5 +235,30 @@ SA_EXPORT int sa_quant_kv_fp8(const void* kv, int64_t rows, int32_t d, uint8_t* 
     if (rows == 0) return SA_OK;
     const hipError_t e = sa::launch_quant_fp8((const uint16_t*)kv, rows, d, e4m3_out, e8m0_out,
                                               (uint16_t*)bf16_out, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}
+
+SA_EXPORT int sa_rope_table(int32_t rope_dim, int32_t max_pos, int32_t original_seq_len, float base,
+                            float factor, float beta_fast, float beta_slow, float* cos_sin, void* stream) {
+    if (rope_dim < 2 || (rope_dim & 1) || max_pos < 1 || original_seq_len < 0 || !cos_sin) return SA_ERR_INVALID;
+    if (!std::isfinite(base) || !(base > 1.0f) || !aligned(cos_sin, 8)) return SA_ERR_INVALID;
+    int32_t low = 0, high = 0;
+    const int yarn = original_seq_len > 0;
+    if (yarn) {
+        if (!std::isfinite(factor) || !(factor > 0.0f) || !std::isfinite(beta_fast) || !std::isfinite(beta_slow) ||
+            !(beta_slow > 0.0f) || !(beta_fast > beta_slow))
+            return SA_ERR_INVALID;
+        // the pair index whose wavelength fits `rotations` times into original_seq_len
+        // (precompute_freqs_cis, corrected_dim), in f64 as the page evaluates it
+        auto corrected_dim = [&](double rotations) {
+            return rope_dim * std::log((double)original_seq_len / (rotations * 2.0 * M_PI)) / (2.0 * std::log((double)base));
+        };
+        const double lo = std::floor(corrected_dim(beta_fast));
+        const double hi = std::ceil(corrected_dim(beta_slow));
+        low = lo > 0.0 ? (int32_t)std::min(lo, (double)INT32_MAX / 2) : 0;
+        high = hi < (double)(rope_dim - 1) ? (int32_t)std::max(hi, -(double)INT32_MAX / 2) : rope_dim - 1;
+    }
+    const hipError_t e = sa::launch_rope_table(rope_dim, max_pos, base, yarn, low, high, factor, cos_sin,
+                                               (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }

@@ -50,6 +50,8 @@ hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int k
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
                               hipStream_t st);
+hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int32_t yarn, int32_t low,
+                             int32_t high, float factor, float* cs, hipStream_t st);
 hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
                             uint8_t* scales, uint16_t* rt, hipStream_t st);
 

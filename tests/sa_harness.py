@@ -62,37 +62,55 @@ def gpu_run(w: W.Workload, kv_format: str = "bf16", rope: bool = True, device="c
 
 # ------------------------------------------------------------------ oracle side
 def oracle_indices(w: W.Workload) -> np.ndarray:
-    sp = [0] * w.win_nseq if w.win_start_pos is None else w.win_start_pos.numpy()
-    win = oracle.window_topk_idxs(w.window, w.win_seqlen, sp).reshape(w.b, w.s, -1)
+    sp = None if w.win_start_pos is None else w.win_start_pos.numpy()
+    win = oracle.window_topk_idxs(w.window, w.win_seqlen, sp, nseq=w.win_nseq).reshape(w.b, w.s, -1)
     if w.comp_idx is None:
         return np.ascontiguousarray(win)
     return np.ascontiguousarray(np.concatenate([win, w.comp_idx.numpy()], axis=-1))
 
 
-def oracle_kv(w: W.Workload, round_trip: bool, seqs=None) -> np.ndarray:
+def oracle_kv(w: W.Workload, round_trip: bool, seqs=None, idx=None, qsel=None) -> np.ndarray:
+    """The kv rows the oracle reads: the raw draws, or their block-32 fp8 round trip. With
+    idx and qsel given, only the rows the selected queries name are round-tripped (the
+    oracle reads no other row)."""
     kv = u16(w.kv)
     if not round_trip:
         return kv
     out = kv.copy()
     for sq in (range(w.b) if seqs is None else seqs):
-        out[sq] = oracle.act_quant(kv[sq])[0]
+        if idx is None or qsel is None:
+            out[sq] = oracle.act_quant(kv[sq])[0]
+            continue
+        q_of_seq = [int(i) % w.s for i in qsel if int(i) // w.s == sq]
+        named = idx[sq, q_of_seq].reshape(-1)
+        rows = np.unique(named[named >= 0])
+        if rows.size:
+            out[sq, rows] = oracle.act_quant(np.ascontiguousarray(kv[sq, rows]))[0]
     return out
+
+
+def oracle_core(w: W.Workload, qsel=None, round_trip=None, nthreads: int = 0):
+    """sparse_attn of the oracle, before the epilogue: bf16 (u16) [nsel][h][d]."""
+    rt = w.kv_roundtrip if round_trip is None else round_trip
+    seqs = None if qsel is None else sorted({int(i) // w.s for i in qsel})
+    idx = oracle_indices(w)
+    kv = oracle_kv(w, rt, seqs, idx, qsel)
+    return oracle.sparse_attn(u16(w.q), kv, w.sink.numpy(), idx, w.scale, qsel=qsel,
+                              nthreads=nthreads)
+
+
+def oracle_rotate(w: W.Workload, core: np.ndarray, qsel=None):
+    """The inverse-RoPE epilogue of the oracle on core outputs of the queries qsel."""
+    cs = oracle.freqs_cis(w.rd, w.max_pos, w.rope_base)
+    pos = w.pos.numpy().reshape(-1)
+    pos = pos if qsel is None else pos[np.asarray(qsel)]
+    return oracle.apply_rotary(core, w.rd, cs, pos, inverse=True)
 
 
 def oracle_run(w: W.Workload, qsel=None, rope: bool = True, round_trip=None, nthreads: int = 0):
     """bf16 (u16) [nsel][h][d] for the flattened queries qsel (all if None)."""
-    rt = w.kv_roundtrip if round_trip is None else round_trip
-    seqs = None if qsel is None else sorted({int(i) // w.s for i in qsel})
-    kv = oracle_kv(w, rt, seqs)
-    idx = oracle_indices(w)
-    out = oracle.sparse_attn(u16(w.q), kv, w.sink.numpy(), idx, w.scale, qsel=qsel,
-                             nthreads=nthreads)
-    if rope:
-        cs = oracle.freqs_cis(w.rd, w.max_pos, w.rope_base)
-        pos = w.pos.numpy().reshape(-1)
-        pos = pos if qsel is None else pos[np.asarray(qsel)]
-        out = oracle.apply_rotary(out, w.rd, cs, pos, inverse=True)
-    return out
+    out = oracle_core(w, qsel, round_trip, nthreads)
+    return oracle_rotate(w, out, qsel) if rope else out
 
 
 def assert_close(gpu_u16: np.ndarray, ref_u16: np.ndarray, what: str = ""):
@@ -101,9 +119,10 @@ def assert_close(gpu_u16: np.ndarray, ref_u16: np.ndarray, what: str = ""):
     assert g.shape == r.shape, (g.shape, r.shape)
     err = np.abs(g - r)
     bound = ATOL + RTOL * np.abs(r)
-    bad = err > bound
+    # NaN in either side is a failure: ~(err <= bound) is True where err is NaN
+    bad = ~(err <= bound)
     if bad.any():
-        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        i = np.unravel_index(np.argmax(np.where(np.isnan(err), np.inf, err - bound)), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} elements outside "
                              f"|gpu-oracle| <= {ATOL} + {RTOL}|oracle|; worst at {i}: "
                              f"gpu {g[i]} oracle {r[i]}")

@@ -104,3 +104,30 @@ def test_quant_validation(sa):
     assert L.sa_quant_kv_fp8(fake, 4, 64, None, None, None, None) == -1       # no output
     assert L.sa_quant_kv_fp8(None, 4, 64, fake, None, None, None) == -1
     assert L.sa_quant_kv_fp8(fake, 0, 64, fake, None, None, None) == 0        # nothing to do
+
+
+def test_split_plans_keep_the_combine_grid_in_int32(sa):
+    """A list longer than one workgroup stages (5000 columns) forces a split plan; with
+    b * s * h above the int32 range the combine kernel's wave index would overflow, so the
+    call is refused on the host."""
+    a = _args(sa, s=32768, h=65536, d=256, topk=5000, kv_rows=8, q_seq_stride=0,
+              out_seq_stride=0, kv_seq_stride=0, idx_seq_stride=0)
+    n = C.c_size_t(0)
+    assert sa.lib().sa_sparse_attn_workspace(C.byref(a), C.byref(n)) == 0 and n.value > 0
+    assert sa.lib().sa_sparse_attn(C.byref(a), None) == -2
+
+
+def test_rope_table_validation(sa):
+    L = sa.lib()
+    fake = C.c_void_p(0x10000)
+    ok = (64, 16, 0, 10000.0, 1.0, 32.0, 1.0, fake, None)
+    for i, bad in ((0, 3), (0, 0), (1, 0), (2, -1), (3, 1.0), (3, float("nan")), (7, None)):
+        args = list(ok)
+        args[i] = bad
+        assert L.sa_rope_table(*args) == -1, (i, bad)
+    yarn = list(ok)
+    yarn[2] = 65536
+    for i, bad in ((4, 0.0), (5, 1.0), (6, 0.0), (5, float("inf"))):
+        args = list(yarn)
+        args[i] = bad
+        assert L.sa_rope_table(*args) == -1, (i, bad)

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import sa_workloads as W
-from sa_harness import (ATOL, RTOL, assert_close, gpu_indices, gpu_inputs, gpu_run, oracle_indices,
-                        oracle_run, u16)
+from sa_harness import (ATOL, RTOL, assert_close, gpu_indices, gpu_inputs, gpu_run, oracle_core,
+                        oracle_indices, oracle_rotate, oracle_run, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def sa():
 def test_prefill_lists_bit_exact(sa, window, seqlen):
     _say("prefill lists", window, seqlen)
     got = sa.window_topk_idxs(window, seqlen, 2, device="cuda").cpu().numpy()
-    ref = oracle.window_topk_idxs(window, seqlen, [0, 0])
+    ref = oracle.window_topk_idxs(window, seqlen, nseq=2)
     assert np.array_equal(got, ref)
 
 
@@ -48,12 +48,25 @@ def test_decode_lists_bit_exact(sa):
         assert np.array_equal(got, ref)
 
 
-def test_decode_lists_zero_and_negative_position(sa):
-    P = torch.tensor([0, -3, 5], dtype=torch.int32)
-    got = sa.window_topk_idxs(8, 1, 3, start_pos=P.cuda()).cpu().numpy()
-    assert got[0, 0].tolist() == [0] + [-1] * 7
-    assert got[1, 0].tolist() == [-1] * 8
-    assert got[2, 0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
+@pytest.mark.parametrize("positions", [[0], [0, 0, 0], [0, 5, 1]])
+def test_decode_lists_at_position_zero(sa, positions):
+    """A decode step at position 0 (the ring holds token 0 only), alone and beside other
+    sequences: the whole ring's list, against the oracle."""
+    P = torch.tensor(positions, dtype=torch.int32)
+    for window in (8, 128):
+        got = sa.window_topk_idxs(window, 1, P.numel(), start_pos=P.cuda()).cpu().numpy()
+        ref = oracle.window_topk_idxs(window, 1, P.numpy())
+        assert got.shape == ref.shape == (P.numel(), 1, window)
+        assert np.array_equal(got, ref)
+
+
+def test_decode_lists_negative_position(sa):
+    """A negative position is a caller error (the oracle rejects it); the library writes a
+    row of -1 for it, as include/sa.h documents, and the other rows as usual."""
+    P = torch.tensor([-3, 5], dtype=torch.int32)
+    got = sa.window_topk_idxs(8, 1, 2, start_pos=P.cuda()).cpu().numpy()
+    assert got[0, 0].tolist() == [-1] * 8
+    assert np.array_equal(got[1:], oracle.window_topk_idxs(8, 1, [5]))
 
 
 def test_lists_written_in_place_leave_other_columns(sa):
@@ -122,7 +135,7 @@ def test_ring_cache_sequence(sa):
                 kv_dev = rows_dev.view(1, S, d)
                 idx = sa.window_topk_idxs(Wn, S, 1, device="cuda")
                 kv_orc = rows_orc.reshape(1, S, d)
-                idx_orc = oracle.window_topk_idxs(Wn, S, [0])
+                idx_orc = oracle.window_topk_idxs(Wn, S)
                 pos = torch.arange(S, dtype=torch.int32).view(1, S)
                 for p_ in range(max(0, S - Wn), S):             # ring writes of the prefill
                     ring_dev[0, p_ % Wn] = rows_dev[p_]
@@ -455,41 +468,175 @@ def test_graph_replays_match_eager(sa, name):
         assert torch.equal(got, ref), f"replay {r}: output differs from the eager call"
 
 
-# ------------------------------------------------------------------ full sizes, sampled
-FULL = {
-    "decode_window": [0, 7, 19, 31],
-    "prefill_window": [0, 1, 126, 127, 128, 2047, 4095],
-    "decode_compress": [0, 13, 63],
-    "prefill_compress": [0, 3, 126, 127, 1000, 4097, 8191],
-}
+# ------------------------------------------------------------------ rotary table
+@pytest.mark.parametrize("rd,max_pos,base,yarn", [
+    (16, 300, 10000.0, False), (64, 70000, 10000.0, False), (64, 70000, 160000.0, True),
+    (128, 1000, 160000.0, True),
+])
+def test_rope_table_vs_oracle(sa, rd, max_pos, base, yarn):
+    """sa_rope_table against the oracle's precompute_freqs_cis (f32 roundings of the page):
+    the frequencies and angles agree bit for bit, so cos and sin differ by at most one f32
+    rounding of the same angle."""
+    kw = dict(original_seq_len=65536, factor=16.0, beta_fast=32.0, beta_slow=1.0) if yarn else {}
+    got = sa.rope_table(rd, max_pos, base, "cuda", **kw).cpu().numpy()
+    ref = oracle.freqs_cis(rd, max_pos, base, **kw)
+    assert got.shape == ref.shape
+    diff = np.abs(got.astype(np.float64) - ref)
+    assert diff.max() <= 6e-8, diff.max()
+    assert (diff == 0).mean() > 0.99
 
 
-@pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(sa, name):
-    """The workload at its full size in the configuration the bench times (bf16 storage,
-    epilogue on); the oracle computes a sample of queries one by one."""
-    _say("full", name)
-    w = W.make(name)
-    out, idx = gpu_run(w, "bf16", True)
-    sel = np.array(FULL[name], np.int64)
-    ref_idx = oracle_indices(w)
-    got_idx = idx.cpu().numpy()
-    assert np.array_equal(got_idx, ref_idx)
-    ref = oracle_run(w, qsel=sel, rope=True)
-    got = u16(out).reshape(-1, w.h, w.d)[sel]
-    assert_close(got, ref, f"full {name}")
+# ------------------------------------------------------------------ full sizes
+def _full_selection(w):
+    """Every query of the decode workloads; for the prefills 72 (64) queries: 9 (8) per XCD
+    slot of the kernel's work order (a query's slot is its index mod 8), from the first
+    queries (short, partly -1 lists) to the last (the longest lists)."""
+    nq = w.b * w.s
+    if nq <= 64:
+        return np.arange(nq, dtype=np.int64)
+    ks = [0, 2, 7, 15, 40, 200, 511, 700, 1023] if nq >= 8192 else [0, 2, 7, 15, 40, 200, 400, 511]
+    sel = np.array(sorted(8 * k + r for k in ks for r in range(8) if 8 * k + r < nq), np.int64)
+    assert set(sel % 8) == set(range(8))
+    return sel
 
 
-@pytest.mark.parametrize("name", ["decode_window", "decode_compress"])
-def test_full_size_sampled_fp8(sa, name):
-    """The decode workloads at full size with fp8 storage (codes and block-32 scales); their
-    rows are fp8-round-tripped already, so the oracle runs on the same values."""
-    _say("full fp8", name)
-    w = W.make(name)
-    assert w.kv_roundtrip
-    out, idx = gpu_run(w, "fp8", True)
-    sel = np.array(FULL[name], np.int64)
+_FULL = {}
+
+
+def _full(name):
+    """(workload, selection, oracle core of the selection); one workload cached at a time."""
+    if name not in _FULL:
+        _FULL.clear()
+        w = W.make(name)
+        sel = _full_selection(w)
+        core = oracle_core(w, qsel=sel)
+        _FULL[name] = (w, sel, core)
+    return _FULL[name]
+
+
+FULL_CASES = [(n, f, r) for n in ("decode_window", "decode_compress", "prefill_window", "prefill_compress")
+              for f, r in (("bf16", True), ("bf16", False), ("fp8", True))]
+
+
+@pytest.mark.parametrize("name,fmt,rope", FULL_CASES)
+def test_full_size(sa, name, fmt, rope):
+    """The workload at full size in the launch configuration the bench times (bf16 storage
+    with the epilogue), and also without the epilogue and with fp8 storage: index lists bit
+    for bit, the whole output finite, and the selected queries against the oracle."""
+    w, sel, core = _full(name)
+    _say("full", name, fmt, "rope" if rope else "no epilogue", f"{sel.size} queries")
+    out, idx = gpu_run(w, fmt, rope)
     assert np.array_equal(idx.cpu().numpy(), oracle_indices(w))
-    ref = oracle_run(w, qsel=sel, rope=True)
-    got = u16(out).reshape(-1, w.h, w.d)[sel]
-    assert_close(got, ref, f"full fp8 {name}")
+    assert bool(torch.isfinite(out.float()).all()), "non-finite output"
+    got = u16(out.view(-1, w.h, w.d)[torch.from_numpy(sel).cuda()])
+    ref = oracle_rotate(w, core, sel) if rope else core
+    assert_close(got, ref, f"full {name} {fmt} rope={rope}")
+    del out, idx
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ edge cases of the softmax
+@pytest.mark.parametrize("d,b,s,h,topk,empty,want_ws", [
+    (64, 1, 3, 16, 64, [(0, 32)], False),              # pipelined loop, a leading empty tile
+    (512, 2, 3, 64, 160, [(0, 64)], False),            # d = 512, two leading empty tiles
+    (512, 1, 160, 256, 96, [(0, 32)], False),          # two head blocks per wave
+    (256, 2, 1, 64, 1024, [(0, 256)], True),           # four splits, split 0 (the sink's) empty
+    (256, 2, 1, 64, 1024, [(512, 768)], True),         # a middle split empty
+])
+def test_no_sink_with_empty_tiles(sa, d, b, s, h, topk, empty, want_ws):
+    """sink = -inf (no sink) with tiles or whole splits whose columns are all -1 ahead of the
+    rows: the empty tiles and splits contribute exactly nothing (no NaN from -inf - -inf)."""
+    _say("no sink, empty tiles", d, b, s, h, topk, empty)
+    q, kv, sink, idx = W.rand_problem(110 + d + topk, b, s, h, d, 4 * topk, topk, 0.05, False)
+    for lo, hi in empty:
+        idx[..., lo:hi] = -1
+    sk = torch.full_like(sink, -math.inf)
+    scale = float(np.float32(d ** -0.5))
+    args = sa.make_args(q.cuda(), kv.cuda(), sk.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
+    assert (sa.sparse_attn_workspace_bytes(args) > 0) == want_ws
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sk.cuda(), idx.cuda(), scale)
+    assert bool(torch.isfinite(out.float()).all())
+    ref = oracle.sparse_attn(u16(q), u16(kv), sk.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, d), ref, f"no sink {d} {empty}")
+
+
+def test_no_sink_key_group_without_rows_in_second_pass(sa):
+    """Key groups (decode-shaped, d = 512): every tile of key group 0 is empty while a late
+    large score in group 1 triggers the second pass over the keys; with no sink, group 0 must
+    still contribute exactly nothing to the merge."""
+    q, kv, sink, idx = W.rand_problem(121, 2, 1, 64, 512, 1200, 1024, 0.0, False)
+    for t0 in range(0, 1024, 128):                      # tiles 0, 4, 8, ... (four key groups)
+        idx[..., t0:t0 + 32] = -1
+    for bb in range(2):
+        row = int(idx[bb, 0, 5 * 32 + 3])               # tile 5: group 1's second tile
+        kv[bb, row] = (q[bb, 0, 5].float() * 2.0).to(torch.bfloat16)
+    sk = torch.full_like(sink, -math.inf)
+    scale = float(np.float32(512 ** -0.5))
+    args = sa.make_args(q.cuda(), kv.cuda(), sk.cuda(), idx.cuda(), scale, torch.empty_like(q.cuda()))
+    assert sa.sparse_attn_workspace_bytes(args) == 0, "expected the key-group plan"
+    for s_ in (sk, sink):
+        out = sa.sparse_attn(q.cuda(), kv.cuda(), s_.cuda(), idx.cuda(), scale)
+        assert bool(torch.isfinite(out.float()).all())
+        ref = oracle.sparse_attn(u16(q), u16(kv), s_.numpy(), idx.numpy(), scale)
+        assert_close(u16(out).reshape(-1, 64, 512), ref, "key group 0 empty")
+
+
+@pytest.mark.parametrize("d,b,s,h,topk", [
+    (64, 1, 4, 16, 40),         # one workgroup per query, epilogue in the key-loop kernel
+    (512, 2, 2, 64, 1024),      # key groups, the merged epilogue
+    (256, 2, 2, 64, 1024),      # splits: the combine kernel runs the epilogue
+])
+def test_check_idx_reports_positions_outside_the_table(sa, d, b, s, h, topk):
+    """With the epilogue on, a query whose position has no row in the (cos, sin) table is
+    left unrotated and, with SA_FLAG_CHECK_IDX, sets bit value 2 of the error word; the other
+    queries are rotated as usual."""
+    _say("check_idx positions", d, b, s, h, topk)
+    q, kv, sink, idx = W.rand_problem(130 + d, b, s, h, d, 2000, topk, 0.1, False)
+    rd, max_pos = min(64, d // 4), 50
+    pos = torch.arange(b * s, dtype=torch.int32).view(b, s) * 7 % max_pos
+    bad = [(b - 1, s - 1, max_pos), (0, 0, -3)] if b * s > 1 else [(0, 0, max_pos)]
+    for bb, tt, v in bad:
+        pos[bb, tt] = v
+    scale = float(np.float32(d ** -0.5))
+    table = sa.rope_table(rd, max_pos, 10000.0, "cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, rope=(table, pos.cuda()),
+                         err_word=err, check_idx=True)
+    assert int(err.item()) == 2
+    core = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    cs = oracle.freqs_cis(rd, max_pos, 10000.0)
+    flat = pos.view(-1).numpy()
+    ok = (flat >= 0) & (flat < max_pos)
+    ref = core.copy()
+    ref[ok] = oracle.apply_rotary(core[ok], rd, cs, flat[ok], inverse=True)
+    assert_close(u16(out).reshape(-1, h, d), ref, "positions outside the table")
+    # without the flag the rows are the same and nothing is reported
+    err.zero_()
+    out2 = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale, rope=(table, pos.cuda()))
+    assert torch.equal(out, out2) and int(err.item()) == 0
+
+
+@pytest.mark.parametrize("seed,b,s,h,d,rows,topk,hole,dup", [
+    (101, 2, 3, 16, 64, 50, 40, 0.2, True),
+    (102, 1, 4, 48, 128, 300, 200, 0.1, False),
+    (103, 2, 2, 64, 256, 100, 64, 0.3, True),
+    (104, 1, 2, 32, 256, 3000, 2500, 0.05, False),     # splits and the combine kernel
+    (105, 3, 2, 100, 128, 900, 700, 0.5, False),
+])
+def test_fp8_storage_other_head_dims(sa, seed, b, s, h, d, rows, topk, hole, dup):
+    """fp8 storage (e4m3 codes + block-32 scale bytes) at head dims 64, 128 and 256, where the
+    tiles are converted by a plain loop, against the oracle on the round-tripped rows, with
+    the epilogue on."""
+    _say("fp8 other d", seed, d, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, d, rows, topk, hole, dup)
+    scale = float(np.float32(d ** -0.5))
+    codes, kv_scale = sa.quant_kv_fp8(kv.cuda(), want=("codes", "scales"))
+    kv_ref = oracle.act_quant(u16(kv).reshape(-1, d))[0].reshape(kv.shape)
+    rd = d // 4
+    pos = torch.randint(0, 3000, (b, s), generator=torch.Generator().manual_seed(seed), dtype=torch.int32)
+    table = sa.rope_table(rd, 3000, 10000.0, "cuda")
+    out = sa.sparse_attn(q.cuda(), codes, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale,
+                         rope=(table, pos.cuda()))
+    core = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
+    ref = oracle.apply_rotary(core, rd, oracle.freqs_cis(rd, 3000, 10000.0), pos.view(-1).numpy(), inverse=True)
+    assert_close(u16(out).reshape(-1, h, d), ref, f"fp8 d={d}")

@@ -44,7 +44,7 @@ def test_ring_cache_worked_example(orc):
     orc.ring_prefill(ring, rows[:S])
     assert ring[:, 0].tolist() == g["ring_after_prefill"]
     # prefill lists: one causal window per query into the chunk
-    idx = orc.window_topk_idxs(Wn, S, [0])[0]
+    idx = orc.window_topk_idxs(Wn, S)[0]
     assert idx.shape == (S, Wn)
     assert idx[0].tolist() == [0] + [-1] * 7
     assert idx[3].tolist() == [0, 1, 2, 3] + [-1] * 4
@@ -73,7 +73,7 @@ def _simulate_ring(window, P):
 
 def test_decode_lists_brute_force(orc):
     for window in range(1, 17):
-        for P in range(1, 64):
+        for P in range(0, 64):
             got = orc.window_topk_idxs(window, 1, [P])[0, 0].tolist()
             assert got == _simulate_ring(window, P), (window, P)
     # several sequences at their own positions in one call
@@ -86,7 +86,7 @@ def test_decode_lists_brute_force(orc):
 def test_prefill_lists_brute_force(orc):
     for window in (1, 3, 8, 16):
         for S in (2, 5, 8, 17, 40):
-            got = orc.window_topk_idxs(window, S, [0, 0])
+            got = orc.window_topk_idxs(window, S, nseq=2)
             cols = min(S, window)
             assert got.shape == (2, S, cols)
             for t in range(S):
@@ -99,7 +99,9 @@ def test_window_rejects_chunked_prefill(orc):
     with pytest.raises(ValueError):
         orc.window_topk_idxs(8, 4, [3])
     with pytest.raises(ValueError):
-        orc.window_topk_idxs(0, 4, [0])
+        orc.window_topk_idxs(0, 4)
+    with pytest.raises(ValueError):
+        orc.window_topk_idxs(8, 1, [-1])
 
 
 # ------------------------------------------------------------------ sparse_attn
