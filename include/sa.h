@@ -38,7 +38,9 @@ enum {
     SA_ERR_INVALID = -1,      /* a null pointer, a negative or zero size, a bad stride ... */
     SA_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement */
     SA_ERR_HIP = -3,          /* the HIP runtime reported an error at launch */
-    SA_ERR_WORKSPACE = -4     /* workspace missing or smaller than sa_sparse_attn_workspace */
+    SA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than sa_sparse_attn_workspace */
+    SA_ERR_SCRATCH = -5       /* sa_sparse_attn_noalloc: the plan needs more workspace than
+                                 SA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* KV storage formats */
@@ -111,6 +113,21 @@ typedef struct sa_attn_args {
  * the top of this file, followed by the optional inverse-RoPE epilogue. Queries whose
  * index list selects nothing produce zeros (the sink takes the whole mass). */
 int sa_sparse_attn(const sa_attn_args *a, void *stream);
+
+/* sa_sparse_attn without a caller workspace and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The split partials of plans that need a workspace go
+ * to a static device buffer of SA_NOALLOC_SCRATCH_BYTES held by the library on each GPU it
+ * runs on until the process ends; a->workspace and a->workspace_bytes are ignored. Plans
+ * needing more than that (sa_sparse_attn_workspace reports the bytes) are refused with
+ * SA_ERR_SCRATCH before any HIP call. Nothing in the buffer has to start at zero: a call
+ * writes every partial it reads. All calls on one GPU share its buffer, so calls that
+ * overlap in time on one GPU (other streams, other threads) race; calls ordered on one
+ * stream do not. The first call on a device looks up the buffer's device address there
+ * (hipGetSymbolAddress, no allocation and no stream operation). Otherwise the same
+ * arguments, results and errors as sa_sparse_attn. */
+#define SA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int sa_sparse_attn_noalloc(const sa_attn_args *a, void *stream);
 
 /* Bytes of workspace sa_sparse_attn needs for these arguments on the current device (only
  * the sizes, kv_format and flags are read; pointers may be NULL). Writes *bytes. */

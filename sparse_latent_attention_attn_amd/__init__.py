@@ -14,14 +14,15 @@ import os
 import torch
 
 __all__ = [
-    "SaError", "lib", "sparse_attn", "sparse_attn_workspace_bytes", "window_topk_idxs",
+    "SaError", "lib", "sparse_attn", "sparse_attn_noalloc", "sparse_attn_workspace_bytes", "window_topk_idxs",
     "quant_kv_fp8", "rope_table", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 
-SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE, SA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_BF16, KV_FP8 = 0, 1
 FLAG_CHECK_IDX = 1
 
@@ -72,6 +73,8 @@ def lib():
         L.sa_status_string.argtypes = [C.c_int]
         L.sa_sparse_attn.restype = C.c_int
         L.sa_sparse_attn.argtypes = [C.POINTER(AttnArgs), P]
+        L.sa_sparse_attn_noalloc.restype = C.c_int
+        L.sa_sparse_attn_noalloc.argtypes = [C.POINTER(AttnArgs), P]
         L.sa_sparse_attn_workspace.restype = C.c_int
         L.sa_sparse_attn_workspace.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
         L.sa_window_topk_idxs.restype = C.c_int
@@ -194,6 +197,16 @@ def sparse_attn(q, kv, sink, idx, scale, *, out=None, kv_scale=None, rope=None,
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _check("sa_sparse_attn", lib().sa_sparse_attn(C.byref(a), C.c_void_p(_stream(q.device))))
+    return out
+
+
+def sparse_attn_noalloc(q, kv, sink, idx, scale, *, out, kv_scale=None, rope=None,
+                       err_word=None, check_idx=False):
+    """sparse_attn through sa_sparse_attn_noalloc (include/sa.h): no workspace and no
+    allocation by the library; `out` must be given. Returns out."""
+    a = make_args(q, kv, sink, idx, scale, out, kv_scale=kv_scale, rope=rope,
+                  err_word=err_word, check_idx=check_idx)
+    _check("sa_sparse_attn_noalloc", lib().sa_sparse_attn_noalloc(C.byref(a), C.c_void_p(_stream(q.device))))
     return out
 
 

@@ -31,6 +31,7 @@ SOURCES = {
     "attn_fwd.hip": VGPR_ACC,
     "attn_fwd_wide.hip": [],
     "aux_kernels.hip": VGPR_ACC,
+    "noalloc.hip": [],
 }
 
 _NOISE = ("is not a recognized feature for this target", "(ignoring feature)")

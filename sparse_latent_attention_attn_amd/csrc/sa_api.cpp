@@ -162,6 +162,7 @@ SA_EXPORT const char* sa_status_string(int status) {
         case SA_ERR_UNSUPPORTED: return "unsupported argument combination";
         case SA_ERR_HIP: return "HIP runtime error";
         case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SA_ERR_SCRATCH: return "the plan needs more than the library's static scratch buffer holds";
         default: return "unknown status";
     }
 }
@@ -174,20 +175,25 @@ SA_EXPORT int sa_sparse_attn_workspace(const sa_attn_args* a, size_t* bytes) {
     return SA_OK;
 }
 
-SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
+namespace sa {
+
+// Validation, plan and kernel parameters of one sparse_attn call, shared by the entry points
+// that take a caller workspace and the one that uses the library's static scratch buffer.
+// ws / ws_bytes: the split partials' buffer (may be null when the plan needs none).
+int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParams& p, Plan& pl) {
     int rc = check_shape(a);
     if (rc != SA_OK) return rc;
     rc = check_pointers(a);
     if (rc != SA_OK) return rc;
-    const sa::Plan pl = make_plan(a, cu_count());
+    pl = make_plan(a, cu_count());
     const int64_t blocks = (int64_t)a->b * a->s * pl.head_blocks * pl.splits;
     if (blocks > INT32_MAX) return SA_ERR_UNSUPPORTED;
     // the combine kernel of a split plan indexes its waves, one per (query, head), in int32
     if (pl.splits > 1 && (int64_t)a->b * a->s * a->h > INT32_MAX - 3) return SA_ERR_UNSUPPORTED;
-    if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 16)))
+    if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes || !aligned(ws, 16)))
         return SA_ERR_WORKSPACE;
 
-    sa::KParams p{};
+    p = KParams{};
     p.b = a->b; p.s = a->s; p.h = a->h; p.d = a->d; p.topk = a->topk; p.kv_rows = a->kv_rows;
     p.q = (const uint16_t*)a->q; p.q_seq_stride = a->q_seq_stride;
     p.kv = (const uint8_t*)a->kv;
@@ -203,10 +209,20 @@ SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
     p.head_blocks = pl.head_blocks; p.h_pad = pl.h_pad;
     if (pl.splits > 1) {
         const size_t slots = (size_t)a->b * a->s * pl.splits * pl.h_pad;
-        p.ws_o = (float*)a->workspace;
+        p.ws_o = (float*)ws;
         p.ws_ml = p.ws_o + slots * a->d;
     }
     p.flags = a->flags; p.err_word = a->err_word;
+    return SA_OK;
+}
+
+}  // namespace sa
+
+SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
+    sa::KParams p;
+    sa::Plan pl;
+    const int rc = sa::prepare_sparse_attn(a, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, p, pl);
+    if (rc != SA_OK) return rc;
     const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, pl.hpw, pl.kg, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/sa.h"
+
 namespace sa {
 
 // Tiling shared by the planner (sa_api.cpp) and the kernels (attn_fwd.hip).
@@ -46,6 +48,9 @@ struct Plan {
     size_t ws_bytes;
 };
 
+// Validation, plan and kernel parameters of a sparse_attn call (sa_api.cpp); returns an SA_*
+// status. ws / ws_bytes: the buffer of the split partials.
+int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParams& p, Plan& pl);
 hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st);
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
