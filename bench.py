@@ -58,9 +58,9 @@ DECODE = {"decode_window", "decode_compress"}
 # of 2516.6 TFLOP/s / 8 TB/s = 315 flop/B): the window-only prefill does 126 flop/B
 HBM_BOUND = {"decode_window", "decode_compress", "prefill_window"}
 HEADLINE = ("prefill_compress", "bf16")
-SUB_RECORDS = [("decode_window", "bf16"), ("decode_window", "fp8"), ("prefill_window", "bf16"),
-               ("prefill_window", "fp8"), ("decode_compress", "bf16"), ("decode_compress", "fp8"),
-               ("prefill_compress", "fp8")]
+SUB_RECORDS = [("prefill_compress", "fp8"), ("decode_window", "bf16"), ("decode_window", "fp8"),
+               ("prefill_window", "bf16"), ("prefill_window", "fp8"), ("decode_compress", "bf16"),
+               ("decode_compress", "fp8")]
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -427,6 +427,126 @@ def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool
     }
 
 
+# ------------------------------------------------------------------ other steps of the path
+def time_launches(fns, calls: int):
+    """Average duration of one launch of fns[i % len(fns)]: HIP events on the current stream
+    around `calls` back-to-back launches after a GPU spin (as time_kernel). Returns (mean ms,
+    best-batch ms)."""
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        fns[i % len(fns)]()
+    spin_s = max(0.005, 2.0 * (time.perf_counter() - t0))
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * spin_s))
+        e0.record(st)
+        for i in range(calls):
+            fns[i % len(fns)]()
+        e1.record(st)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / calls)
+    return float(np.mean(per)), float(np.min(per))
+
+
+def time_graph_steps(fns, steps: int, warmup: int):
+    """Exactly `steps` launches replayed from one captured graph after a pass over every input
+    set and `warmup` launches; ms per launch."""
+    n = len(fns)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g_all = _capture(stream, fns)
+    g_warm = _capture(stream, [fns[(n - 1 - i) % n] for i in range(warmup)]) if warmup > 0 else None
+    g_timed = _capture(stream, [fns[i % n] for i in range(steps)])
+    torch.cuda.synchronize()
+    g_all.replay()
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_timed.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _oracle_seconds(fn, min_s: float = 1.0):
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s or reps >= 1000:
+            return dt / reps, reps, dt
+
+
+KV_WRITE = {   # name: (sequences, rows per sequence, ring positions start)
+    "kv_write_prefill": (1, 8192, 0),        # the long prefill's chunk: 8192 tokens, ring of 128
+    "kv_write_decode": (64, 1, 65535),       # one token for each of 64 sequences
+}
+
+
+def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool):
+    """The KV write path (sa_kv_write): normalised rows -> forward RoPE -> fp8 round trip ->
+    ring slot, bf16 storage, with the rows returned for the prefill. HBM-bound: bytes = rows
+    read + positions + (cos, sin) rows + rows returned + rows stored."""
+    b, s, p0 = KV_WRITE[name]
+    d, rd, window = 512, 64, 128
+    g = torch.Generator().manual_seed(31)
+    x0 = torch.randn(b, s, d, generator=g).to(torch.bfloat16)
+    pos0 = (torch.arange(s, dtype=torch.int32)[None] + p0).repeat(b, 1)
+    max_pos = int(pos0.max()) + 1
+    table = sa.rope_table(rd, max_pos, 10000.0, dev)
+    want_rows = s > 1
+    stored = b * min(s, window)
+    alg_bytes = b * s * (2 * d + 4 + rd // 2 * 8) + (b * s * 2 * d if want_rows else 0) + stored * 2 * d
+    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / alg_bytes)))
+    sets = []
+    for _ in range(nsets):
+        x, pos = x0.to(dev), pos0.to(dev)
+        ring = torch.zeros(b, window, d, dtype=torch.bfloat16, device=dev)
+        rows = torch.empty(b, s, d, dtype=torch.bfloat16, device=dev) if want_rows else None
+        sets.append((x, pos, ring, rows))
+    fns = [(lambda x=x, pos=pos, ring=ring, rows=rows:
+            sa.kv_write(x, pos, ring, rope=table, window=window, rows_out=rows)) for x, pos, ring, rows in sets]
+    ms_step = time_graph_steps(fns, steps, warmup)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
+    achieved = alg_bytes / (k_mean * 1e-3) / 1e9
+    rec = {
+        "metric": "kv_write GB/s", "value": alg_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
+        "ms_per_step": ms_step, "steps": steps, "dtype": "bf16 rows, f32 rotation, fp8 round trip",
+        "config": {"workload": name, "sequences": b, "rows_per_sequence": s, "head_dim": d,
+                   "rope_dim": rd, "window": window, "kv_storage": "bf16", "rows_returned": want_rows},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kv_write_kernel",
+                     "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": None,
+    }
+    if cpu:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+        from sa_harness import u16
+        xo, po = u16(x0), pos0.numpy()
+        cs = oracle.freqs_cis(rd, max_pos, 10000.0)
+        ring_o = np.zeros((b, window, d), np.uint16)
+        per, reps, dt = _oracle_seconds(lambda: oracle.kv_write(xo, po, rd, cs, window, window,
+                                                                cache_bf16=ring_o, want_rows=want_rows))
+        rec["cpu_baseline"] = {"value": alg_bytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole step x {reps} run(s), {dt:.1f} s wall (single-threaded)"}
+    del sets, fns
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,16 +605,27 @@ def main():
         return made[name]
 
     records = []
-    # sub-records first, grouped by workload; the headline's workload last (shared draws)
+    # the headline first (its CPU baseline gets the larger budget), then the sub-records
+    # grouped by workload (shared draws)
+    rec = measure(workload(head[0]), head[1], dev, args.steps, args.warmup, epilogue, 12.0 if cpu else None)
+    head_rec = rec
+    print(f"[bench] {head[0]} {head[1]}: {rec['value']:.4g} {rec['unit']} "
+          f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
     for name, kv in subs:
         rec = measure(workload(name), kv, dev, args.steps, args.warmup, epilogue, 4.0 if cpu else None)
         records.append(rec)
         print(f"[bench] {name} {kv}: {rec['value']:.4g} {rec['unit']}, kernel "
               f"{rec['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {rec['roofline']['frac']:.3f} of "
               f"{rec['roofline']['bound']} ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
-    rec = measure(workload(head[0]), head[1], dev, args.steps, args.warmup, epilogue, 15.0 if cpu else None)
-    print(f"[bench] {head[0]} {head[1]}: {rec['value']:.4g} {rec['unit']} "
-          f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+    if args.workload == "all":
+        made.clear()
+        for name in KV_WRITE:
+            r = measure_kv_write(name, dev, args.steps, args.warmup, cpu)
+            records.append(r)
+            print(f"[bench] {name}: {r['value']:.4g} {r['unit']}, kernel "
+                  f"{r['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {r['roofline']['frac']:.3f} of hbm "
+                  f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+    rec = head_rec
     line = {
         "metric": rec["metric"], "value": rec["value"], "unit": rec["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],

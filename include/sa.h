@@ -56,8 +56,9 @@ enum {
     SA_FLAG_CHECK_IDX = 1u    /* report errors found on the device in *err_word (bits are
                                  OR-ed in): bit 0 (value 1) an index >= kv_rows, bit 1
                                  (value 2) a position outside [0, max_pos) with the RoPE
-                                 epilogue on. Without the flag nothing is reported; the
-                                 handling below is the same either way */
+                                 epilogue on, bit 2 (value 4) a row sa_kv_write could not
+                                 store. Without the flag nothing is reported; the
+                                 handling is the same either way */
 };
 
 typedef struct sa_attn_args {
@@ -159,6 +160,47 @@ int sa_window_topk_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int3
  *   trip codes * s, which is exact in bf16. At least one output must be given. */
 int sa_quant_kv_fp8(const void *kv, int64_t rows, int32_t d, uint8_t *e4m3_out,
                     uint8_t *e8m0_out, void *bf16_out, void *stream);
+
+/* The KV write path, the step before sparse_attn on the same cache and formats (attention
+ * API docs, module notes: "a single latent KV row per token ... RoPE on the last
+ * rope_head_dim ... the KV row quantised to fp8 in place (block 32, ue8m0 scale), a
+ * sliding-window ring cache", and the ring-cache paragraph; Attention.forward and
+ * apply_rotary_emb on the attention output page). For every row t of sequence n, in order:
+ *   1. rotate the last rope_dim elements forward at position p = pos[n][t]: adjacent pairs
+ *      times (cos, sin) = rope_cos_sin[p][pair], in f32, back to bf16;
+ *   2. quantise to fp8 in blocks of 32 (as sa_quant_kv_fp8) and take the round trip;
+ *   3. store it: window > 0: into slot p mod window of sequence n's ring (cache rows
+ *      [0, window)), only for the last `window` rows of the call (t >= s - window: a prefill
+ *      of s tokens leaves tokens s-window .. s-1, as in the ring-cache paragraph);
+ *      window == 0: at cache row row0[n] + t (a linear cache such as the compressed one).
+ *      kv_format SA_KV_BF16 stores the bf16 round trip (what the pages' cache holds);
+ *      SA_KV_FP8_E4M3_B32 stores the codes and scale bytes (sparse_attn's fp8 form).
+ *   rows_out (nullable) receives the bf16 round trip of every row (the chunk's kv rows that
+ *   a prefill's sparse_attn reads).
+ * The input rows are the normalised latent rows (after wkv and kv_norm). A row whose
+ * position is negative, or >= max_pos with rope_dim > 0, is neither stored nor written to
+ * rows_out; a linear destination outside [0, cache_rows) is not stored; with
+ * SA_FLAG_CHECK_IDX either case ORs bit value 4 into *err_word. */
+typedef struct sa_kv_write_args {
+    int32_t b, s, d;        /* sequences, rows per sequence, row width (64, 128, 256, 512) */
+    int32_t rope_dim;       /* 0, or even and <= d */
+    const void *x;          int64_t x_seq_stride;       /* bf16 [b][s][d]; [s][d] contiguous */
+    const float *rope_cos_sin; int32_t max_pos;         /* f32 [max_pos][rope_dim/2][2] */
+    const int32_t *pos;     int64_t pos_seq_stride;     /* int32 [b][s] token positions */
+    int32_t window;                                     /* ring slots, or 0 for a linear cache */
+    const int32_t *row0;                                /* int32 [b] first row (window == 0) */
+    int32_t cache_rows;                                 /* rows per sequence (>= window) */
+    int32_t kv_format;                                  /* SA_KV_* */
+    void *cache;            int64_t cache_seq_stride;   /* bf16 [b][cache_rows][d], or e4m3
+                                                           bytes [b][cache_rows][d] */
+    uint8_t *cache_scale;   int64_t cache_scale_seq_stride; /* e8m0 [b][cache_rows][d/32],
+                                                           fp8 only */
+    void *rows_out;         int64_t rows_out_seq_stride; /* bf16 [b][s][d] or NULL */
+    uint32_t flags;                                     /* SA_FLAG_CHECK_IDX or 0 */
+    int32_t *err_word;                                  /* device int32, with the flag */
+} sa_kv_write_args;
+
+int sa_kv_write(const sa_kv_write_args *a, void *stream);
 
 /* The (cos, sin) table that the inverse-RoPE epilogue reads (rope_cos_sin above):
  * precompute_freqs_cis of Attention.__init__ (atlas.klimoza.dev/.../attention/output,

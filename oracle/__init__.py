@@ -80,6 +80,7 @@ def lib():
             "orc_freqs_cis_yarn": (C.c_int, [I32, I32, I32, F, F, F, F, P]),
             "orc_apply_rotary": (C.c_int, [P, I64, I32, I32, I32, P, I32, P, I32]),
             "orc_max_threads": (I32, []),
+            "orc_kv_write": (C.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -273,3 +274,28 @@ def apply_rotary(x: np.ndarray, rd: int, cos_sin: np.ndarray, pos, inverse: bool
     if rc:
         raise ValueError("orc_apply_rotary rejected its arguments")
     return y
+
+
+# ---------------------------------------------------------------- KV write path
+def kv_write(x, pos, rd: int, cos_sin, window: int, cache_rows: int, row0=None,
+             cache_bf16=None, cache_codes=None, cache_scales=None, want_rows: bool = True):
+    """x: bf16 (u16) [b][s][d]; pos int32 [b][s]. Updates the given caches in place
+    ([b][cache_rows][d] u16, [b][cache_rows][d] u8, [b][cache_rows][d/32] u8) and returns the
+    processed rows (bf16 u16 [b][s][d]) when want_rows."""
+    x = _u16(x)
+    b, s, d = x.shape
+    pos = np.ascontiguousarray(pos, np.int32).reshape(b, s)
+    cs = np.ascontiguousarray(cos_sin, np.float32) if rd > 0 else np.zeros((1, 1, 2), np.float32)
+    r0 = None if row0 is None else np.ascontiguousarray(row0, np.int32)
+    for c in (cache_bf16, cache_codes, cache_scales):
+        assert c is None or (c.flags.c_contiguous and c.shape[0] == b and c.shape[1] == cache_rows)
+    rows = np.empty_like(x) if want_rows else None
+    rc = lib().orc_kv_write(_ptr(x), b, s, d, rd, _ptr(cs), cs.shape[0], _ptr(pos), window,
+                            None if r0 is None else _ptr(r0), cache_rows,
+                            None if cache_bf16 is None else _ptr(cache_bf16),
+                            None if cache_codes is None else _ptr(cache_codes),
+                            None if cache_scales is None else _ptr(cache_scales),
+                            None if rows is None else _ptr(rows))
+    if rc:
+        raise ValueError("orc_kv_write rejected its arguments")
+    return rows

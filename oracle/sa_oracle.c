@@ -522,3 +522,57 @@ int orc_apply_rotary(uint16_t *x, int64_t n, int32_t h, int32_t d, int32_t rd,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* KV write path. [attn-docs] module notes: each token's latent KV row (after wkv and    */
+/* kv_norm) gets RoPE on its last rope_dim elements, is quantised to fp8 in place (block  */
+/* 32, ue8m0) and goes into the sliding-window ring cache; [attn-fwd] Attention.forward  */
+/* rotates with freqs_cis[start_pos + t] (apply_rotary_emb, forward); [attn-docs] ring-   */
+/* cache paragraph: the slot of token p is p mod window. The steps, in that order, on a  */
+/* normalised row x: forward rotation (orc_apply_rotary), fp8 round trip                 */
+/* (orc_act_quant_rows), store.                                                          */
+/* Readings: rows of one call that share a slot are stored last-wins, i.e. only the last */
+/* `window` rows of a sequence are stored (the prefill writes tokens S-window..S-1); with */
+/* window == 0 row t goes to cache row row0[n] + t (a linear cache, e.g. the compressed  */
+/* one). A position outside [0, max_pos) or a destination outside the cache stores      */
+/* nothing. fp8 storage keeps the codes and scale bytes instead of the bf16 round trip.  */
+/* ------------------------------------------------------------------------------------ */
+int orc_kv_write(const uint16_t *x, int32_t b, int32_t s, int32_t d, int32_t rd,
+                 const float *cos_sin, int32_t max_pos, const int32_t *pos, int32_t window,
+                 const int32_t *row0, int32_t cache_rows, uint16_t *cache_bf16,
+                 uint8_t *cache_codes, uint8_t *cache_scales, uint16_t *rows_out)
+{
+    if (!x || !pos || b < 1 || s < 1 || d < 32 || d % 32 || rd < 0 || rd > d || rd % 2) return -1;
+    if (window < 0 || (window == 0 && !row0) || cache_rows < 1) return -1;
+    if (rd > 0 && !cos_sin) return -1;
+    const int nb = d / 32;
+    uint16_t *row = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    uint16_t *rt = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)d);
+    uint8_t *codes = (uint8_t *)malloc((size_t)d);
+    uint8_t *scales = (uint8_t *)malloc((size_t)nb);
+    if (!row || !rt || !codes || !scales) { free(row); free(rt); free(codes); free(scales); return -1; }
+    for (int32_t n = 0; n < b; ++n)
+        for (int32_t t = 0; t < s; ++t) {
+            const int64_t i = (int64_t)n * s + t;
+            const int32_t p = pos[i];
+            if (p < 0 || p >= max_pos) continue;
+            memcpy(row, x + i * d, sizeof(uint16_t) * (size_t)d);
+            if (rd > 0) orc_apply_rotary(row, 1, 1, d, rd, cos_sin, max_pos, &p, 0);
+            orc_act_quant_rows(row, 1, d, rt, codes, scales);
+            if (rows_out) memcpy(rows_out + i * d, rt, sizeof(uint16_t) * (size_t)d);
+            int64_t dst;
+            if (window > 0) {
+                if (t < s - window) continue;                 /* a later row takes the slot */
+                dst = p % window;
+            } else {
+                dst = (int64_t)row0[n] + t;
+            }
+            if (dst < 0 || dst >= cache_rows) continue;
+            const int64_t r = (int64_t)n * cache_rows + dst;
+            if (cache_bf16) memcpy(cache_bf16 + r * d, rt, sizeof(uint16_t) * (size_t)d);
+            if (cache_codes) memcpy(cache_codes + r * d, codes, (size_t)d);
+            if (cache_scales) memcpy(cache_scales + r * nb, scales, (size_t)nb);
+        }
+    free(row); free(rt); free(codes); free(scales);
+    return 0;
+}

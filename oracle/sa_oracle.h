@@ -110,6 +110,18 @@ int orc_freqs_cis_yarn(int32_t rd, int32_t max_pos, int32_t original_seq_len, fl
 int orc_apply_rotary(uint16_t *x, int64_t n, int32_t h, int32_t d, int32_t rd,
                      const float *cos_sin, int32_t max_pos, const int32_t *pos, int32_t inverse);
 
+/* ---- KV write path ([attn-docs] module notes and ring-cache paragraph; [attn-fwd]
+ * Attention.forward, apply_rotary_emb): x bf16 [b][s][d] normalised latent rows, pos int32
+ * [b][s]; each row is rotated forward on its last rd elements at pos, fp8 round-tripped
+ * (block 32) and stored: window > 0: slot pos mod window of sequence n's ring, only for
+ * t >= s - window; window == 0: row row0[n] + t. Caches are [b][cache_rows][...]: bf16 rows
+ * (cache_bf16) and/or e4m3 codes + e8m0 scale bytes; rows_out (nullable) bf16 [b][s][d]
+ * gets every processed row. Returns 0, or -1. */
+int orc_kv_write(const uint16_t *x, int32_t b, int32_t s, int32_t d, int32_t rd,
+                 const float *cos_sin, int32_t max_pos, const int32_t *pos, int32_t window,
+                 const int32_t *row0, int32_t cache_rows, uint16_t *cache_bf16,
+                 uint8_t *cache_codes, uint8_t *cache_scales, uint16_t *rows_out);
+
 /* threads an nthreads <= 0 call uses (the OpenMP default), 1 without OpenMP */
 int32_t orc_max_threads(void);
 

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "SaError", "lib", "sparse_attn", "sparse_attn_noalloc", "sparse_attn_workspace_bytes", "window_topk_idxs",
-    "quant_kv_fp8", "rope_table", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
+    "quant_kv_fp8", "rope_table", "kv_write", "KvWriteArgs", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +55,22 @@ class AttnArgs(C.Structure):
     ]
 
 
+class KvWriteArgs(C.Structure):
+    """Mirror of sa_kv_write_args in include/sa.h (field order and types must match)."""
+    _fields_ = [
+        ("b", C.c_int32), ("s", C.c_int32), ("d", C.c_int32), ("rope_dim", C.c_int32),
+        ("x", C.c_void_p), ("x_seq_stride", C.c_int64),
+        ("rope_cos_sin", C.c_void_p), ("max_pos", C.c_int32),
+        ("pos", C.c_void_p), ("pos_seq_stride", C.c_int64),
+        ("window", C.c_int32), ("row0", C.c_void_p), ("cache_rows", C.c_int32),
+        ("kv_format", C.c_int32),
+        ("cache", C.c_void_p), ("cache_seq_stride", C.c_int64),
+        ("cache_scale", C.c_void_p), ("cache_scale_seq_stride", C.c_int64),
+        ("rows_out", C.c_void_p), ("rows_out_seq_stride", C.c_int64),
+        ("flags", C.c_uint32), ("err_word", C.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +97,8 @@ def lib():
         L.sa_window_topk_idxs.argtypes = [I32, I32, I32, P, P, I64, I64, C.POINTER(I32), P]
         L.sa_rope_table.restype = C.c_int
         L.sa_rope_table.argtypes = [I32, I32, I32, C.c_float, C.c_float, C.c_float, C.c_float, P, P]
+        L.sa_kv_write.restype = C.c_int
+        L.sa_kv_write.argtypes = [C.POINTER(KvWriteArgs), P]
         L.sa_quant_kv_fp8.restype = C.c_int
         L.sa_quant_kv_fp8.argtypes = [P, I64, I32, P, P, P, P]
         if L.sa_abi_version() != 1:
@@ -255,6 +273,58 @@ def quant_kv_fp8(kv, *, codes=None, scales=None, roundtrip=None, want=("codes", 
         C.c_void_p(_stream(kv.device))))
     res = {"codes": codes, "scales": scales, "roundtrip": roundtrip}
     return tuple(res[w] for w in want)
+
+
+def kv_write(x, pos, cache, *, rope=None, window=0, row0=None, cache_scale=None,
+             rows_out=None, err_word=None, check_idx=False):
+    """The KV write path (sa_kv_write in include/sa.h). x: bf16 [b][s][d] normalised rows;
+    pos: int32 [b][s]; cache: bf16 [b][R][d] (bf16 storage) or uint8 [b][R][d] with
+    cache_scale uint8 [b][R][d/32] (fp8 storage); rope = cos_sin table f32
+    [max_pos][rd/2][2] or None; window > 0: ring of `window` slots, else row0 int32 [b].
+    rows_out: optional bf16 [b][s][d]. Returns rows_out."""
+    dev = x.device
+    _need(x, torch.bfloat16, "x", dev)
+    _need(pos, torch.int32, "pos", dev)
+    if x.dim() != 3 or pos.shape != x.shape[:2] or cache.dim() != 3 or cache.shape[0] != x.shape[0] \
+            or cache.shape[2] != x.shape[2]:
+        raise ValueError("shapes: x [b][s][d], pos [b][s], cache [b][R][d]")
+    a = KvWriteArgs()
+    a.b, a.s, a.d = x.shape
+    a.x, a.x_seq_stride = _ptr(x), _seq_major(x, "x", 2)
+    a.pos, a.pos_seq_stride = _ptr(pos), _seq_major(pos, "pos", 1)
+    if rope is not None:
+        _need(rope, torch.float32, "rope", dev)
+        if not rope.is_contiguous() or rope.dim() != 3:
+            raise ValueError("rope table [max_pos][rd/2][2] contiguous")
+        a.rope_dim, a.rope_cos_sin, a.max_pos = rope.shape[1] * 2, _ptr(rope), rope.shape[0]
+    a.window = window
+    if row0 is not None:
+        _need(row0, torch.int32, "row0", dev)
+        a.row0 = _ptr(row0)
+    a.cache_rows = cache.shape[1]
+    if cache.dtype == torch.bfloat16:
+        _need(cache, torch.bfloat16, "cache", dev)
+        a.kv_format = KV_BF16
+    else:
+        _need(cache, torch.uint8, "cache", dev)
+        if cache_scale is None:
+            raise ValueError("fp8 cache needs cache_scale")
+        _need(cache_scale, torch.uint8, "cache_scale", dev)
+        a.kv_format = KV_FP8
+        a.cache_scale, a.cache_scale_seq_stride = _ptr(cache_scale), _seq_major(cache_scale, "cache_scale", 2)
+    a.cache, a.cache_seq_stride = _ptr(cache), _seq_major(cache, "cache", 2)
+    if rows_out is not None:
+        _need(rows_out, torch.bfloat16, "rows_out", dev)
+        if rows_out.shape != x.shape:
+            raise ValueError("rows_out must be shaped like x")
+        a.rows_out, a.rows_out_seq_stride = _ptr(rows_out), _seq_major(rows_out, "rows_out", 2)
+    if check_idx:
+        if err_word is None:
+            raise ValueError("check_idx needs err_word")
+        _need(err_word, torch.int32, "err_word", dev)
+        a.flags, a.err_word = FLAG_CHECK_IDX, _ptr(err_word)
+    _check("sa_kv_write", lib().sa_kv_write(C.byref(a), C.c_void_p(_stream(dev))))
+    return rows_out
 
 
 def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda", *,

@@ -112,9 +112,12 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     amax = fmaxf(amax, 1e-4f);
     const float s = pow2_ceil_f32(amax / 448.0f);
     if (!live) return;
+    // x / s: s is a power of two whose reciprocal is a normal f32 (2^-120 .. 2^22), so the
+    // product with the exact reciprocal rounds exactly as the division would
+    const float inv_s = 1.0f / s;
     uint32_t c[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] / s);   // exact division by 2^k
+    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] * inv_s);
     if (codes) {
         u32x2 w;
         w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
@@ -184,6 +187,109 @@ hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int3
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)grid), dim3(256), 0, st, rope_dim, max_pos, base, yarn,
                        low, high, factor, cs);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ KV write path
+// The step before sparse_attn on the same cache (attention API docs: module notes and the
+// ring-cache paragraph; Attention.forward and apply_rotary_emb): each normalised latent row
+// is rotated forward on its last rope_dim elements at its position (pairs times (cos, sin)
+// in f32, back to bf16), quantised to fp8 in blocks of 32 (the round trip is stored as bf16,
+// or the codes and scale bytes), and stored: into slot pos mod window of its sequence's ring
+// (only the last `window` rows of a call, later rows win a shared slot), or at row
+// row0[n] + t of a linear cache. One thread per 8 elements (16 bytes) of a row, a 32-element
+// block per 4 threads. No contraction into fused multiply-adds, as in the page's f32 steps.
+template <int D>
+__global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {
+#pragma clang fp contract(off)
+    constexpr int kLanesPerRow = D / 8;
+    const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = gtid / kLanesPerRow;
+    const int part = (int)(gtid % kLanesPerRow);
+    const bool live = row < (int64_t)p.b * p.s;
+    const int n = live ? (int)(row / p.s) : 0;
+    const int t = live ? (int)(row % p.s) : 0;
+    const int pos = live ? p.pos[(int64_t)n * p.pos_seq_stride + t] : 0;
+    const bool pos_ok = live && pos >= 0 && (p.rope_dim == 0 || pos < p.max_pos);
+    u32x4 v = pos_ok ? *(const u32x4*)(p.x + (int64_t)n * p.x_seq_stride + (int64_t)t * D + 8 * part)
+                     : u32x4{0, 0, 0, 0};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { x[2 * k] = bf16_lo(v[k]); x[2 * k + 1] = bf16_hi(v[k]); }
+    // forward rotation of the pairs in the rope tail
+    const int r0 = D - p.rope_dim;
+    if (pos_ok && 8 * part + 8 > r0) {
+        const float* cs = p.rope_cs + (int64_t)pos * p.rope_dim;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = 8 * part + 2 * k;
+            if (e >= r0) {
+                const float c = cs[e - r0], sn = cs[e - r0 + 1];
+                const float a = x[2 * k], b = x[2 * k + 1];
+                const float re = a * c - b * sn;
+                const float im = a * sn + b * c;
+                const uint32_t w = pack_bf16x2(re, im);
+                x[2 * k] = bf16_lo(w);
+                x[2 * k + 1] = bf16_hi(w);
+            }
+        }
+    }
+    // block-32 fp8 round trip (the four threads of a block share its maximum)
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    amax = fmaxf(amax, 1e-4f);
+    const float sc = pow2_ceil_f32(amax / 448.0f);
+    if (!live) return;
+    int64_t dst = -1;
+    if (pos_ok) {
+        if (p.window > 0) dst = t >= p.s - p.window ? pos % p.window : -2;   // -2: a later row wins
+        else dst = (int64_t)p.row0[n] + t;
+    }
+    const bool store = dst >= 0 && dst < p.cache_rows;
+    if ((p.flags & 1u) && part == 0 && (!pos_ok || (dst != -2 && !store))) atomicOr(p.err_word, 4);
+    if (!pos_ok) return;
+    const float inv_sc = 1.0f / sc;                                  // exact (a power of two)
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] * inv_sc);
+    u32x4 rt;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = f32_bits(e4m3_decode(c[2 * k]) * sc) >> 16;
+        const uint32_t hi = f32_bits(e4m3_decode(c[2 * k + 1]) * sc) >> 16;
+        rt[k] = lo | (hi << 16);
+    }
+    if (p.rows_out) *(u32x4*)(p.rows_out + (int64_t)n * p.rows_out_seq_stride + (int64_t)t * D + 8 * part) = rt;
+    if (!store) return;
+    const int64_t off = (int64_t)n * p.cache_seq_stride + dst * D + 8 * part;
+    if (p.cache_bf16) {
+        *(u32x4*)(p.cache_bf16 + off) = rt;
+    } else {
+        u32x2 w;
+        w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        *(u32x2*)(p.cache_codes + off) = w;
+        if ((part & 3) == 0)
+            p.cache_scales[(int64_t)n * p.cache_scale_seq_stride + dst * (D / 32) + part / 4] =
+                (uint8_t)((f32_bits(sc) >> 23) & 0xffu);
+    }
+}
+
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st) {
+    const int64_t threads = (int64_t)p.b * p.s * (p.d / 8);
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), blk(256);
+    switch (p.d) {
+        case 64: hipLaunchKernelGGL(kv_write_kernel<64>, g, blk, 0, st, p); break;
+        case 128: hipLaunchKernelGGL(kv_write_kernel<128>, g, blk, 0, st, p); break;
+        case 256: hipLaunchKernelGGL(kv_write_kernel<256>, g, blk, 0, st, p); break;
+        case 512: hipLaunchKernelGGL(kv_write_kernel<512>, g, blk, 0, st, p); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -278,3 +278,46 @@ SA_EXPORT int sa_rope_table(int32_t rope_dim, int32_t max_pos, int32_t original_
                                                (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }
+
+SA_EXPORT int sa_kv_write(const sa_kv_write_args* a, void* stream) {
+    if (!a) return SA_ERR_INVALID;
+    if (a->b < 1 || a->s < 1 || a->cache_rows < 1 || a->window < 0) return SA_ERR_INVALID;
+    if (a->d != 64 && a->d != 128 && a->d != 256 && a->d != 512) return SA_ERR_UNSUPPORTED;
+    if (a->rope_dim < 0 || a->rope_dim > a->d || (a->rope_dim & 1)) return SA_ERR_INVALID;
+    if (a->kv_format != SA_KV_BF16 && a->kv_format != SA_KV_FP8_E4M3_B32) return SA_ERR_INVALID;
+    if ((a->flags & ~(uint32_t)SA_FLAG_CHECK_IDX) != 0) return SA_ERR_INVALID;
+    if (!a->x || !a->pos || !a->cache) return SA_ERR_INVALID;
+    if (a->rope_dim > 0 && (!a->rope_cos_sin || a->max_pos < 1 || !aligned(a->rope_cos_sin, 8))) return SA_ERR_INVALID;
+    if (a->window > 0 ? a->cache_rows < a->window : !a->row0) return SA_ERR_INVALID;
+    const bool fp8 = a->kv_format == SA_KV_FP8_E4M3_B32;
+    if (fp8 && !a->cache_scale) return SA_ERR_INVALID;
+    if ((a->flags & SA_FLAG_CHECK_IDX) && !a->err_word) return SA_ERR_INVALID;
+    if (!aligned(a->x, 16) || !aligned(a->cache, fp8 ? 8 : 16) || !aligned(a->pos, 4) ||
+        (a->rows_out && !aligned(a->rows_out, 16)) || (a->row0 && !aligned(a->row0, 4)))
+        return SA_ERR_INVALID;
+    const int64_t sd = (int64_t)a->s * a->d, rd_ = (int64_t)a->cache_rows * a->d;
+    if (a->x_seq_stride % 8 || a->cache_seq_stride % 8 || (a->rows_out && a->rows_out_seq_stride % 8))
+        return SA_ERR_INVALID;
+    if (a->b > 1) {
+        if (a->x_seq_stride < sd || a->pos_seq_stride < a->s || a->cache_seq_stride < rd_) return SA_ERR_INVALID;
+        if (a->rows_out && a->rows_out_seq_stride < sd) return SA_ERR_INVALID;
+        if (fp8 && a->cache_scale_seq_stride < (int64_t)a->cache_rows * (a->d / 32)) return SA_ERR_INVALID;
+    }
+    sa::KvWriteParams p{};
+    p.b = a->b; p.s = a->s; p.d = a->d; p.rope_dim = a->rope_dim;
+    p.x = (const uint16_t*)a->x; p.x_seq_stride = a->x_seq_stride;
+    p.rope_cs = a->rope_cos_sin; p.max_pos = a->max_pos;
+    p.pos = a->pos; p.pos_seq_stride = a->pos_seq_stride;
+    p.window = a->window; p.row0 = a->row0; p.cache_rows = a->cache_rows;
+    if (fp8) {
+        p.cache_codes = (uint8_t*)a->cache;
+        p.cache_scales = a->cache_scale; p.cache_scale_seq_stride = a->cache_scale_seq_stride;
+    } else {
+        p.cache_bf16 = (uint16_t*)a->cache;
+    }
+    p.cache_seq_stride = a->cache_seq_stride;
+    p.rows_out = (uint16_t*)a->rows_out; p.rows_out_seq_stride = a->rows_out_seq_stride;
+    p.flags = a->flags; p.err_word = a->err_word;
+    const hipError_t e = sa::launch_kv_write(p, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}

@@ -36,6 +36,24 @@ struct KParams {
     int32_t* err_word;
 };
 
+// One sa_kv_write launch (pointers already offset to element 0; strides in elements of the
+// pointed-to type).
+struct KvWriteParams {
+    int32_t b, s, d, rope_dim;
+    const uint16_t* x;       int64_t x_seq_stride;
+    const float* rope_cs;    int32_t max_pos;
+    const int32_t* pos;      int64_t pos_seq_stride;
+    int32_t window;
+    const int32_t* row0;
+    int32_t cache_rows;
+    uint16_t* cache_bf16;    int64_t cache_seq_stride;          // bf16 storage
+    uint8_t* cache_codes;                                      // fp8 storage (same stride, bytes)
+    uint8_t* cache_scales;   int64_t cache_scale_seq_stride;
+    uint16_t* rows_out;      int64_t rows_out_seq_stride;
+    uint32_t flags;
+    int32_t* err_word;
+};
+
 // Split plan shared by sa_sparse_attn and sa_sparse_attn_workspace.
 struct Plan {
     int nw;             // waves per workgroup
@@ -57,6 +75,7 @@ hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, cons
                               hipStream_t st);
 hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int32_t yarn, int32_t low,
                              int32_t high, float factor, float* cs, hipStream_t st);
+hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
 hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
                             uint8_t* scales, uint16_t* rt, hipStream_t st);
 

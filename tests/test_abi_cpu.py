@@ -131,3 +131,31 @@ def test_rope_table_validation(sa):
         args = list(yarn)
         args[i] = bad
         assert L.sa_rope_table(*args) == -1, (i, bad)
+
+
+def _kv_args(sa, **kw):
+    a = sa.KvWriteArgs()
+    a.b, a.s, a.d, a.rope_dim = 1, 4, 64, 16
+    a.x = a.pos = a.cache = a.rope_cos_sin = 0x10000
+    a.max_pos, a.window, a.cache_rows, a.kv_format = 16, 8, 8, 0
+    a.x_seq_stride, a.pos_seq_stride, a.cache_seq_stride = 256, 4, 512
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("b", 0, -1), ("s", 0, -1), ("d", 96, -2), ("rope_dim", 3, -1), ("rope_dim", 80, -1),
+    ("kv_format", 3, -1), ("flags", 2, -1), ("x", 0, -1), ("pos", 0, -1), ("cache", 0, -1),
+    ("cache_rows", 4, -1), ("window", -1, -1), ("x", 0x10008, -1), ("x_seq_stride", 12, -1),
+    ("kv_format", 1, -1),          # fp8 without cache_scale
+    ("flags", 1, -1),              # checking without err_word
+])
+def test_kv_write_rejects_before_any_hip_call(sa, field, value, status):
+    a = _kv_args(sa, **{field: value})
+    assert sa.lib().sa_kv_write(C.byref(a), None) == status
+
+
+def test_kv_write_linear_needs_row0(sa):
+    assert sa.lib().sa_kv_write(C.byref(_kv_args(sa, window=0)), None) == -1
+    assert sa.lib().sa_kv_write(None, None) == -1
