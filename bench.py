@@ -547,6 +547,93 @@ def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool):
     return rec
 
 
+INDEXER = {   # name: (sequences, queries per sequence, compressed positions, query positions)
+    "indexer_decode": (64, 1, 16384, "decode"),     # the window + compressed decode's lists
+    "indexer_prefill": (1, 8192, 2048, "prefill"),  # the long prefill's lists
+}
+
+
+def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool):
+    """The indexer (sa_indexer_topk: MFMA scores, then the radix-select top-k lists) with 32
+    index heads of 128, ratio 4, 512 picks, and select_candidate_blocks (sa_candidate_blocks,
+    2048 blocks of 8) on its scores. Decode reads 4 MB of index keys per sequence and is
+    HBM-bound; the prefill does 2 h d flops per visible (query, position) pair and is bound by
+    the MFMA roofline."""
+    b, s, n_pos, kind = INDEXER[name]
+    h, d, ratio, topk = 32, 128, 4, 512
+    g = torch.Generator().manual_seed(41)
+    q0 = torch.randn(b, s, h, d, generator=g).to(torch.bfloat16)
+    k0 = torch.randn(b, n_pos, d, generator=g).to(torch.bfloat16)
+    w0 = torch.randn(b, s, h, generator=g) * (d ** -0.5 * h ** -0.5)
+    pos0 = (torch.full((b, s), 65535, dtype=torch.int32) if kind == "decode"
+            else torch.arange(s, dtype=torch.int32)[None].repeat(b, 1))
+    vis = torch.clamp((pos0.long() + 1) // ratio, max=n_pos)
+    pairs = int(vis.sum())
+    flops = 2.0 * h * d * pairs
+    key_bytes = b * n_pos * d * 2
+    alg_bytes = key_bytes + b * s * (h * d * 2 + h * 4 + 4 + topk * 4)
+    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / alg_bytes)))
+    sets = []
+    for _ in range(nsets):
+        sets.append(dict(q=q0.to(dev), k=k0.to(dev), w=w0.to(dev), pos=pos0.to(dev),
+                         sc=torch.empty(b, s, n_pos, dtype=torch.float32, device=dev),
+                         idx=torch.empty(b, s, topk, dtype=torch.int32, device=dev),
+                         mask=torch.empty(b, s, n_pos, dtype=torch.uint8, device=dev)))
+    fns = [(lambda x=x: sa.indexer_topk(x["q"], x["k"], x["w"], x["pos"], ratio, topk=topk, offset=128,
+                                        scores=x["sc"], idx=x["idx"])) for x in sets]
+    ms_step = time_graph_steps(fns, steps, warmup)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
+    cand_fns = [(lambda x=x: sa.candidate_blocks(x["sc"], x["pos"], ratio, 2048, 8, mask=x["mask"])) for x in sets]
+    c_mean, _ = time_launches(cand_fns, calls=min(400, max(50, 5 * steps)))
+    if kind == "decode":
+        achieved = alg_bytes / (k_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        value, unit, metric = key_bytes / (ms_step * 1e-3) / 1e9, "GB/s", "indexer key GB/s (decode)"
+    else:
+        achieved = flops / (k_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+        value, unit, metric = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", "indexer TFLOP/s (prefill)"
+    roof.update({"traffic": None, "kernel": "sa_indexer_topk (index_scores_kernel + index_topk_kernel)",
+                 "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
+                 "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops})
+    cand_bytes = b * s * n_pos * 5
+    rec = {
+        "metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step, "steps": steps,
+        "dtype": "bf16 inputs, f32 scores",
+        "config": {"workload": name, "sequences": b, "queries_per_sequence": s, "index_heads": h,
+                   "index_head_dim": d, "compressed_positions": n_pos, "ratio": ratio, "topk": topk,
+                   "visible_pairs": pairs},
+        "roofline": roof,
+        "candidate_blocks": {"kernel_ms_mean": c_mean, "topk_blocks": 2048, "block_size": 8,
+                             "bytes_per_launch": cand_bytes,
+                             "hbm_frac": cand_bytes / (c_mean * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": None,
+    }
+    if cpu:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+        from sa_harness import u16
+        nq = b * s
+        sel = np.unique(np.linspace(0, nq - 1, 4 if kind == "decode" else 32).round().astype(np.int64))
+        bs_, ss_ = sel // s, sel % s
+        qs, ws, ps = u16(q0[bs_, ss_].reshape(-1, 1, h, d)), w0[bs_, ss_].reshape(-1, 1, h).numpy(), pos0[bs_, ss_].view(-1, 1).numpy()
+        ks = u16((k0[bs_] if b > 1 else k0.expand(sel.size, -1, -1)).contiguous())
+        threads = oracle.max_threads()
+        per, reps, dt = _oracle_seconds(lambda: oracle.index_topk(
+            oracle.index_scores(qs, ks, ws, ps, ratio, nthreads=threads), topk, 128), 2.0)
+        sel_pairs = int(vis[bs_, ss_].sum())
+        per_step = per * pairs / max(sel_pairs, 1)
+        val = (key_bytes / per_step / 1e9, "GB/s") if kind == "decode" else (flops / per_step / 1e12, "TFLOP/s")
+        rec["cpu_baseline"] = {"value": val[0], "unit": val[1], "cores": threads, "kind": "oracle",
+                               "sample": f"{sel.size} of {nq} queries x {reps} run(s), {dt:.1f} s wall, "
+                                         f"scaled by visible pairs to one step"}
+    del sets, fns, cand_fns
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -619,6 +706,13 @@ def main():
               f"{rec['roofline']['bound']} ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
     if args.workload == "all":
         made.clear()
+        for name in INDEXER:
+            r = measure_indexer(name, dev, args.steps, args.warmup, cpu)
+            records.append(r)
+            print(f"[bench] {name}: {r['value']:.4g} {r['unit']}, kernel "
+                  f"{r['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {r['roofline']['frac']:.3f} of "
+                  f"{r['roofline']['bound']}; candidate blocks {r['candidate_blocks']['kernel_ms_mean'] * 1e3:.2f} us "
+                  f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
         for name in KV_WRITE:
             r = measure_kv_write(name, dev, args.steps, args.warmup, cpu)
             records.append(r)

@@ -202,6 +202,57 @@ typedef struct sa_kv_write_args {
 
 int sa_kv_write(const sa_kv_write_args *a, void *stream);
 
+/* The indexer, which produces the compressed half of sparse_attn's index lists (indexer
+ * page, open-model-atlas.../source-layer/attention?inspect=indexer, Indexer.forward).
+ * For query t of sequence n at absolute position p = pos[n][t], the first
+ * (p + 1) / ratio compressed positions are visible (p = t in a prefill from 0, end_pos - 1
+ * in decode: the page's (t+1)//ratio and end_pos//ratio). For each visible position u:
+ *   score[u] = sum over heads hh of w[n][t][hh] * relu(q[n][t][hh] . k[n][u])
+ * in f32 from bf16 q and k (w is the caller's weights_proj output times softmax_scale *
+ * h^-0.5). Positions not visible, and with cand != NULL (the second level of the two-level
+ * top-k) positions whose cand byte is 0, score -inf. The scores go to `scores` (always
+ * written: select_candidate_blocks reads them as its logits). With idx != NULL each query
+ * then lists the topk positions with the best finite scores, in ascending position order
+ * (equal scores: the lower position first), each plus `offset` (the rows before the
+ * compressed ones in sparse_attn's kv), then -1 up to topk columns; the pages' list length
+ * is min(index_topk, end_pos // ratio). Output: idx[n * idx_seq_stride + t * idx_row_stride
+ * + j] for j < topk (other columns untouched, so the window part of a list can share the
+ * row). Supported: h = 16, 32 or 64 (64 with d <= 128), d = 64, 128 or 256, n_pos <= 32768
+ * when idx != NULL. Pointers are device pointers, caller-owned; q, k 16-byte aligned. */
+typedef struct sa_indexer_args {
+    int32_t b, s, h, d;     /* sequences, queries per sequence, index heads, index head dim */
+    int32_t n_pos;          /* compressed positions of k per sequence */
+    int32_t ratio;          /* compress ratio (>= 1) */
+    const void *q;          int64_t q_seq_stride;        /* bf16 [b][s][h][d] */
+    const void *k;          int64_t k_seq_stride;        /* bf16 [b][n_pos][d] */
+    const float *w;         int64_t w_seq_stride;        /* f32 [b][s][h] */
+    const int32_t *pos;     int64_t pos_seq_stride;      /* int32 [b][s] */
+    const uint8_t *cand;    int64_t cand_seq_stride;     /* uint8 [b][s][n_pos] or NULL */
+    float *scores;          int64_t scores_seq_stride;   /* f32 [b][s][n_pos] (output) */
+    int32_t topk;           /* columns of each list (>= 1) */
+    int32_t offset;         /* added to every listed position */
+    int32_t *idx;           int64_t idx_seq_stride, idx_row_stride; /* int32 or NULL */
+} sa_indexer_args;
+
+int sa_indexer_topk(const sa_indexer_args *a, void *stream);
+
+/* Level one of the two-level top-k (indexer page, select_candidate_blocks): for query t of
+ * sequence n, the logits (sa_indexer_topk's scores, -inf where unreachable) are cut into
+ * blocks of block_size positions, the last one padded with -inf; a block scores its
+ * maximum, the block of the newest visible position ((len - 1) / block_size with floor
+ * division, len = (pos + 1) / ratio as above; none when len = 0) scores +inf; the
+ * min(topk_blocks, blocks) best blocks are kept if their score is above -inf (equal
+ * scores: the lower block first); mask[n][t][u] = 1 for the positions u of kept blocks,
+ * else 0. Supported: n_pos / block_size <= 32768 blocks. */
+typedef struct sa_candidate_args {
+    int32_t b, s, n_pos, ratio, topk_blocks, block_size;
+    const float *logits;    int64_t logits_seq_stride;   /* f32 [b][s][n_pos] */
+    const int32_t *pos;     int64_t pos_seq_stride;      /* int32 [b][s] */
+    uint8_t *mask;          int64_t mask_seq_stride;     /* uint8 [b][s][n_pos] (output) */
+} sa_candidate_args;
+
+int sa_candidate_blocks(const sa_candidate_args *a, void *stream);
+
 /* The (cos, sin) table that the inverse-RoPE epilogue reads (rope_cos_sin above):
  * precompute_freqs_cis of Attention.__init__ (atlas.klimoza.dev/.../attention/output,
  * precompute_freqs_cis; attention API docs, "freqs_cis"), evaluated on the device with the

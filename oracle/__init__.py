@@ -81,6 +81,9 @@ def lib():
             "orc_apply_rotary": (C.c_int, [P, I64, I32, I32, I32, P, I32, P, I32]),
             "orc_max_threads": (I32, []),
             "orc_kv_write": (C.c_int, [P, I32, I32, I32, I32, P, I32, P, I32, P, I32, P, P, P, P]),
+            "orc_index_scores": (C.c_int, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I32]),
+            "orc_index_topk": (C.c_int, [P, I32, I32, I32, I32, I32, P]),
+            "orc_candidate_blocks": (C.c_int, [P, P, I32, I32, I32, I32, I32, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -299,3 +302,41 @@ def kv_write(x, pos, rd: int, cos_sin, window: int, cache_rows: int, row0=None,
     if rc:
         raise ValueError("orc_kv_write rejected its arguments")
     return rows
+
+
+# ---------------------------------------------------------------- indexer
+def index_scores(q, k, w, pos, ratio: int, cand=None, nthreads: int = 0) -> np.ndarray:
+    """q bf16 (u16) [b][s][h][d], k bf16 (u16) [b][n_pos][d], w f32 [b][s][h], pos int32
+    [b][s], cand uint8 [b][s][n_pos] or None -> f32 [b][s][n_pos]."""
+    q, k = _u16(q), _u16(k)
+    b, s, h, d = q.shape
+    n_pos = k.shape[1]
+    w = np.ascontiguousarray(w, np.float32).reshape(b, s, h)
+    pos = np.ascontiguousarray(pos, np.int32).reshape(b, s)
+    c = None if cand is None else np.ascontiguousarray(cand, np.uint8).reshape(b, s, n_pos)
+    out = np.empty((b, s, n_pos), np.float32)
+    rc = lib().orc_index_scores(_ptr(q), _ptr(k), _ptr(w), _ptr(pos), None if c is None else _ptr(c),
+                                b, s, h, d, n_pos, ratio, _ptr(out), nthreads)
+    if rc:
+        raise ValueError("orc_index_scores rejected its arguments")
+    return out
+
+
+def index_topk(scores, topk: int, offset: int) -> np.ndarray:
+    scores = np.ascontiguousarray(scores, np.float32)
+    b, s, n_pos = scores.shape
+    out = np.empty((b, s, topk), np.int32)
+    if lib().orc_index_topk(_ptr(scores), b, s, n_pos, topk, offset, _ptr(out)):
+        raise ValueError("orc_index_topk rejected its arguments")
+    return out
+
+
+def candidate_blocks(logits, pos, ratio: int, topk_blocks: int, block_size: int) -> np.ndarray:
+    logits = np.ascontiguousarray(logits, np.float32)
+    b, s, n_pos = logits.shape
+    pos = np.ascontiguousarray(pos, np.int32).reshape(b, s)
+    out = np.empty((b, s, n_pos), np.uint8)
+    if lib().orc_candidate_blocks(_ptr(logits), _ptr(pos), b, s, n_pos, ratio, topk_blocks,
+                                  block_size, _ptr(out)):
+        raise ValueError("orc_candidate_blocks rejected its arguments")
+    return out

@@ -576,3 +576,151 @@ int orc_kv_write(const uint16_t *x, int32_t b, int32_t s, int32_t d, int32_t rd,
     free(row); free(rt); free(codes); free(scales);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Indexer scores. [indexer] Indexer.forward: index_score = einsum(q, index_k) over the   */
+/* index head dim, rectified, times the per-head weights (the caller's weights_proj      */
+/* output already times softmax_scale * n_heads^-0.5), summed over heads; positions a   */
+/* query cannot see are -inf. A query at absolute position p sees the first (p+1)/ratio  */
+/* compressed positions ("a block becomes visible once the query has passed its last    */
+/* token": (t+1)//ratio in prefill, end_pos//ratio in decode). With a candidate mask     */
+/* (the second level of select_candidate_blocks' two-level top-k) non-candidates are -inf */
+/* too.                                                                                   */
+/* Reading: the scores are kept in f32 (the page's torch code rounds the einsum, the      */
+/* product and the head sum to bf16); the sums run in index order.                        */
+/* ------------------------------------------------------------------------------------ */
+static int64_t visible_positions(int32_t pos, int32_t ratio, int32_t n_pos)
+{
+    if (pos < 0) return 0;
+    int64_t v = ((int64_t)pos + 1) / ratio;
+    return v < n_pos ? v : n_pos;
+}
+
+int orc_index_scores(const uint16_t *q, const uint16_t *k, const float *w, const int32_t *pos,
+                     const uint8_t *cand, int32_t b, int32_t s, int32_t h, int32_t d,
+                     int32_t n_pos, int32_t ratio, float *scores, int32_t nthreads)
+{
+    if (!q || !k || !w || !pos || !scores || b < 1 || s < 1 || h < 1 || d < 1 || n_pos < 1 || ratio < 1)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t qi = 0; qi < (int64_t)b * s; ++qi) {
+        const int64_t n = qi / s;
+        const int64_t vis = visible_positions(pos[qi], ratio, n_pos);
+        float *row = scores + qi * n_pos;
+        for (int32_t t = 0; t < n_pos; ++t) {
+            if (t >= vis || (cand && !cand[qi * n_pos + t])) { row[t] = -INFINITY; continue; }
+            const uint16_t *kt = k + (n * n_pos + t) * (int64_t)d;
+            float acc = 0.0f;
+            for (int32_t hh = 0; hh < h; ++hh) {
+                const uint16_t *qh = q + (qi * h + hh) * (int64_t)d;
+                float dot = 0.0f;
+                for (int32_t c = 0; c < d; ++c) dot += orc_bf16_to_f32(qh[c]) * orc_bf16_to_f32(kt[c]);
+                const float r = dot > 0.0f ? dot : 0.0f;                 /* relu */
+                acc += r * w[qi * h + hh];
+            }
+            row[t] = acc;
+        }
+    }
+    (void)nthreads;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Indexer top-k. [indexer] Indexer.forward, last lines: take the `topk` best positions   */
+/* by score, re-sort them into position order, shift them by `offset`, and mark as -1    */
+/* what the query cannot reach.                                                          */
+/* Readings: the pages leave ties open; equal scores go to the lower position first.     */
+/* Only positions with a finite score are ever listed (the page's where() also lists a   */
+/* reachable -inf pick, which a candidate mask can leave; it never arises with the       */
+/* config's 2048 candidate blocks); the list is then padded with -1.                     */
+/* ------------------------------------------------------------------------------------ */
+typedef struct { float v; int32_t t; } scored_pos;
+
+static int by_score_then_position(const void *a, const void *b)
+{
+    const scored_pos *x = (const scored_pos *)a, *y = (const scored_pos *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+static int by_position(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+int orc_index_topk(const float *scores, int32_t b, int32_t s, int32_t n_pos, int32_t topk,
+                   int32_t offset, int32_t *idx)
+{
+    if (!scores || !idx || b < 1 || s < 1 || n_pos < 1 || topk < 1) return -1;
+    scored_pos *buf = (scored_pos *)malloc(sizeof(scored_pos) * (size_t)n_pos);
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)topk);
+    if (!buf || !sel) { free(buf); free(sel); return -1; }
+    for (int64_t qi = 0; qi < (int64_t)b * s; ++qi) {
+        const float *row = scores + qi * n_pos;
+        int32_t nf = 0;
+        for (int32_t t = 0; t < n_pos; ++t)
+            if (row[t] > -INFINITY) { buf[nf].v = row[t]; buf[nf].t = t; ++nf; }
+        qsort(buf, (size_t)nf, sizeof(scored_pos), by_score_then_position);
+        const int32_t m = nf < topk ? nf : topk;
+        for (int32_t j = 0; j < m; ++j) sel[j] = buf[j].t;
+        qsort(sel, (size_t)m, sizeof(int32_t), by_position);
+        int32_t *out = idx + qi * topk;
+        for (int32_t j = 0; j < topk; ++j) out[j] = j < m ? sel[j] + offset : -1;
+    }
+    free(buf);
+    free(sel);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Candidate blocks. [indexer] select_candidate_blocks, level one of the two-level top-k: */
+/* a block of block_size positions scores the maximum of its logits (the last block      */
+/* padded with -inf); the block holding the query's newest visible position,             */
+/* (compress_len - 1) // block_size with floor division, is pinned to +inf; the          */
+/* min(topk_blocks, num_blocks) best blocks are taken and those whose score is above     */
+/* -inf are kept; the mask repeats each block's flag over its positions.                 */
+/* compress_len = (pos + 1) / ratio as in orc_index_scores.                               */
+/* Reading: ties between equal block scores go to the lower block first.                 */
+/* ------------------------------------------------------------------------------------ */
+int orc_candidate_blocks(const float *logits, const int32_t *pos, int32_t b, int32_t s,
+                         int32_t n_pos, int32_t ratio, int32_t topk_blocks, int32_t block_size,
+                         uint8_t *mask)
+{
+    if (!logits || !pos || !mask || b < 1 || s < 1 || n_pos < 1 || ratio < 1 || topk_blocks < 1 ||
+        block_size < 1)
+        return -1;
+    const int32_t nblk = (n_pos + block_size - 1) / block_size;
+    scored_pos *blk = (scored_pos *)malloc(sizeof(scored_pos) * (size_t)nblk);
+    uint8_t *keep = (uint8_t *)malloc((size_t)nblk);
+    if (!blk || !keep) { free(blk); free(keep); return -1; }
+    for (int64_t qi = 0; qi < (int64_t)b * s; ++qi) {
+        const float *row = logits + qi * n_pos;
+        const int64_t len = pos[qi] < 0 ? 0 : ((int64_t)pos[qi] + 1) / ratio;
+        /* floor division: len = 0 pins block -1, i.e. none */
+        const int64_t last = len > 0 ? (len - 1) / block_size : -1;
+        for (int32_t j = 0; j < nblk; ++j) {
+            float m = -INFINITY;
+            for (int32_t u = 0; u < block_size; ++u) {
+                const int64_t t = (int64_t)j * block_size + u;
+                const float v = t < n_pos ? row[t] : -INFINITY;     /* -inf padding */
+                if (v > m) m = v;
+            }
+            blk[j].v = j == last ? INFINITY : m;
+            blk[j].t = j;
+            keep[j] = 0;
+        }
+        qsort(blk, (size_t)nblk, sizeof(scored_pos), by_score_then_position);
+        const int32_t m = topk_blocks < nblk ? topk_blocks : nblk;
+        for (int32_t j = 0; j < m; ++j)
+            if (blk[j].v > -INFINITY) keep[blk[j].t] = 1;
+        for (int32_t t = 0; t < n_pos; ++t) mask[qi * n_pos + t] = keep[t / block_size];
+    }
+    free(blk);
+    free(keep);
+    return 0;
+}

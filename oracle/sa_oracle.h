@@ -122,6 +122,23 @@ int orc_kv_write(const uint16_t *x, int32_t b, int32_t s, int32_t d, int32_t rd,
                  const int32_t *row0, int32_t cache_rows, uint16_t *cache_bf16,
                  uint8_t *cache_codes, uint8_t *cache_scales, uint16_t *rows_out);
 
+/* ---- indexer ([indexer] Indexer.forward, select_candidate_blocks) ----
+ * q bf16 [b][s][h][d] index queries; k bf16 [b][n_pos][d] index keys; w f32 [b][s][h] head
+ * weights; pos int32 [b][s] absolute query positions; a query at p sees the first
+ * (p+1)/ratio positions. cand (nullable) uint8 [b][s][n_pos]: 1 = candidate.
+ * scores f32 [b][s][n_pos]: sum_h w_h relu(q_h . k_t), -inf where not visible / candidate. */
+int orc_index_scores(const uint16_t *q, const uint16_t *k, const float *w, const int32_t *pos,
+                     const uint8_t *cand, int32_t b, int32_t s, int32_t h, int32_t d,
+                     int32_t n_pos, int32_t ratio, float *scores, int32_t nthreads);
+/* idx int32 [b][s][topk]: the topk best finite scores (ties: lower position first) in
+ * ascending position order, + offset, then -1. */
+int orc_index_topk(const float *scores, int32_t b, int32_t s, int32_t n_pos, int32_t topk,
+                   int32_t offset, int32_t *idx);
+/* mask uint8 [b][s][n_pos] of select_candidate_blocks (ties: lower block first) */
+int orc_candidate_blocks(const float *logits, const int32_t *pos, int32_t b, int32_t s,
+                         int32_t n_pos, int32_t ratio, int32_t topk_blocks, int32_t block_size,
+                         uint8_t *mask);
+
 /* threads an nthreads <= 0 call uses (the OpenMP default), 1 without OpenMP */
 int32_t orc_max_threads(void);
 

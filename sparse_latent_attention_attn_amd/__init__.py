@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "SaError", "lib", "sparse_attn", "sparse_attn_noalloc", "sparse_attn_workspace_bytes", "window_topk_idxs",
-    "quant_kv_fp8", "rope_table", "kv_write", "KvWriteArgs", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
+    "quant_kv_fp8", "rope_table", "kv_write", "KvWriteArgs", "indexer_topk", "candidate_blocks",
+    "IndexerArgs", "CandidateArgs", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +72,33 @@ class KvWriteArgs(C.Structure):
     ]
 
 
+class IndexerArgs(C.Structure):
+    """Mirror of sa_indexer_args in include/sa.h (field order and types must match)."""
+    _fields_ = [
+        ("b", C.c_int32), ("s", C.c_int32), ("h", C.c_int32), ("d", C.c_int32),
+        ("n_pos", C.c_int32), ("ratio", C.c_int32),
+        ("q", C.c_void_p), ("q_seq_stride", C.c_int64),
+        ("k", C.c_void_p), ("k_seq_stride", C.c_int64),
+        ("w", C.c_void_p), ("w_seq_stride", C.c_int64),
+        ("pos", C.c_void_p), ("pos_seq_stride", C.c_int64),
+        ("cand", C.c_void_p), ("cand_seq_stride", C.c_int64),
+        ("scores", C.c_void_p), ("scores_seq_stride", C.c_int64),
+        ("topk", C.c_int32), ("offset", C.c_int32),
+        ("idx", C.c_void_p), ("idx_seq_stride", C.c_int64), ("idx_row_stride", C.c_int64),
+    ]
+
+
+class CandidateArgs(C.Structure):
+    """Mirror of sa_candidate_args in include/sa.h."""
+    _fields_ = [
+        ("b", C.c_int32), ("s", C.c_int32), ("n_pos", C.c_int32), ("ratio", C.c_int32),
+        ("topk_blocks", C.c_int32), ("block_size", C.c_int32),
+        ("logits", C.c_void_p), ("logits_seq_stride", C.c_int64),
+        ("pos", C.c_void_p), ("pos_seq_stride", C.c_int64),
+        ("mask", C.c_void_p), ("mask_seq_stride", C.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -97,6 +125,10 @@ def lib():
         L.sa_window_topk_idxs.argtypes = [I32, I32, I32, P, P, I64, I64, C.POINTER(I32), P]
         L.sa_rope_table.restype = C.c_int
         L.sa_rope_table.argtypes = [I32, I32, I32, C.c_float, C.c_float, C.c_float, C.c_float, P, P]
+        L.sa_indexer_topk.restype = C.c_int
+        L.sa_indexer_topk.argtypes = [C.POINTER(IndexerArgs), P]
+        L.sa_candidate_blocks.restype = C.c_int
+        L.sa_candidate_blocks.argtypes = [C.POINTER(CandidateArgs), P]
         L.sa_kv_write.restype = C.c_int
         L.sa_kv_write.argtypes = [C.POINTER(KvWriteArgs), P]
         L.sa_quant_kv_fp8.restype = C.c_int
@@ -325,6 +357,73 @@ def kv_write(x, pos, cache, *, rope=None, window=0, row0=None, cache_scale=None,
         a.flags, a.err_word = FLAG_CHECK_IDX, _ptr(err_word)
     _check("sa_kv_write", lib().sa_kv_write(C.byref(a), C.c_void_p(_stream(dev))))
     return rows_out
+
+
+def indexer_topk(q, k, w, pos, ratio: int, *, topk: int | None = None, offset: int = 0,
+                 cand=None, scores=None, idx=None):
+    """The indexer (sa_indexer_topk in include/sa.h). q bf16 [b][s][h][d], k bf16
+    [b][n_pos][d], w f32 [b][s][h], pos int32 [b][s], cand uint8 [b][s][n_pos] or None.
+    Returns (scores f32 [b][s][n_pos], idx int32 [b][s][>= topk] or None); with topk None
+    only the scores are computed. idx may be a view into a larger list buffer (its first
+    topk columns are written)."""
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    _need(k, torch.bfloat16, "k", dev)
+    _need(w, torch.float32, "w", dev)
+    _need(pos, torch.int32, "pos", dev)
+    if q.dim() != 4 or k.dim() != 3 or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[3] \
+            or w.shape != q.shape[:3] or pos.shape != q.shape[:2]:
+        raise ValueError("shapes: q [b][s][h][d], k [b][n_pos][d], w [b][s][h], pos [b][s]")
+    b, s, h, d = q.shape
+    n_pos = k.shape[1]
+    if scores is None:
+        scores = torch.empty(b, s, n_pos, dtype=torch.float32, device=dev)
+    _need(scores, torch.float32, "scores", dev)
+    a = IndexerArgs()
+    a.b, a.s, a.h, a.d, a.n_pos, a.ratio = b, s, h, d, n_pos, ratio
+    a.q, a.q_seq_stride = _ptr(q), _seq_major(q, "q", 3)
+    a.k, a.k_seq_stride = _ptr(k), _seq_major(k, "k", 2)
+    a.w, a.w_seq_stride = _ptr(w), _seq_major(w, "w", 2)
+    a.pos, a.pos_seq_stride = _ptr(pos), _seq_major(pos, "pos", 1)
+    if cand is not None:
+        _need(cand, torch.uint8, "cand", dev)
+        if cand.shape != (b, s, n_pos):
+            raise ValueError("cand must be [b][s][n_pos]")
+        a.cand, a.cand_seq_stride = _ptr(cand), _seq_major(cand, "cand", 2)
+    if scores.shape != (b, s, n_pos):
+        raise ValueError("scores must be [b][s][n_pos]")
+    a.scores, a.scores_seq_stride = _ptr(scores), _seq_major(scores, "scores", 2)
+    if topk is not None:
+        if idx is None:
+            idx = torch.empty(b, s, topk, dtype=torch.int32, device=dev)
+        _need(idx, torch.int32, "idx", dev)
+        if idx.dim() != 3 or idx.shape[:2] != (b, s) or idx.shape[2] < topk or idx.stride(2) != 1:
+            raise ValueError("idx must be [b][s][>= topk] with unit column stride")
+        a.topk, a.offset = topk, offset
+        a.idx, a.idx_seq_stride, a.idx_row_stride = _ptr(idx), idx.stride(0), idx.stride(1)
+    _check("sa_indexer_topk", lib().sa_indexer_topk(C.byref(a), C.c_void_p(_stream(dev))))
+    return scores, idx
+
+
+def candidate_blocks(logits, pos, ratio: int, topk_blocks: int, block_size: int, *, mask=None):
+    """select_candidate_blocks (sa_candidate_blocks in include/sa.h): logits f32
+    [b][s][n_pos], pos int32 [b][s]; returns the uint8 mask [b][s][n_pos]."""
+    dev = logits.device
+    _need(logits, torch.float32, "logits", dev)
+    _need(pos, torch.int32, "pos", dev)
+    if logits.dim() != 3 or pos.shape != logits.shape[:2]:
+        raise ValueError("shapes: logits [b][s][n_pos], pos [b][s]")
+    b, s, n_pos = logits.shape
+    if mask is None:
+        mask = torch.empty(b, s, n_pos, dtype=torch.uint8, device=dev)
+    _need(mask, torch.uint8, "mask", dev)
+    a = CandidateArgs()
+    a.b, a.s, a.n_pos, a.ratio, a.topk_blocks, a.block_size = b, s, n_pos, ratio, topk_blocks, block_size
+    a.logits, a.logits_seq_stride = _ptr(logits), _seq_major(logits, "logits", 2)
+    a.pos, a.pos_seq_stride = _ptr(pos), _seq_major(pos, "pos", 1)
+    a.mask, a.mask_seq_stride = _ptr(mask), _seq_major(mask, "mask", 2)
+    _check("sa_candidate_blocks", lib().sa_candidate_blocks(C.byref(a), C.c_void_p(_stream(dev))))
+    return mask
 
 
 def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda", *,

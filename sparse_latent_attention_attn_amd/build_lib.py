@@ -32,6 +32,7 @@ SOURCES = {
     "attn_fwd_wide.hip": [],
     "aux_kernels.hip": VGPR_ACC,
     "noalloc.hip": [],
+    "indexer.hip": VGPR_ACC,
 }
 
 _NOISE = ("is not a recognized feature for this target", "(ignoring feature)")

@@ -321,3 +321,60 @@ SA_EXPORT int sa_kv_write(const sa_kv_write_args* a, void* stream) {
     const hipError_t e = sa::launch_kv_write(p, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }
+
+SA_EXPORT int sa_indexer_topk(const sa_indexer_args* a, void* stream) {
+    if (!a) return SA_ERR_INVALID;
+    if (a->b < 1 || a->s < 1 || a->n_pos < 1 || a->ratio < 1 || a->h < 1) return SA_ERR_INVALID;
+    if (a->d != 64 && a->d != 128 && a->d != 256) return SA_ERR_UNSUPPORTED;
+    if (a->h != 16 && a->h != 32 && a->h != 64) return SA_ERR_UNSUPPORTED;
+    if (a->h == 64 && a->d > 128) return SA_ERR_UNSUPPORTED;
+    if (!a->q || !a->k || !a->w || !a->pos || !a->scores) return SA_ERR_INVALID;
+    if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->w, 4) || !aligned(a->pos, 4) ||
+        !aligned(a->scores, 4) || (a->idx && !aligned(a->idx, 4)))
+        return SA_ERR_INVALID;
+    if (a->q_seq_stride % 8 || a->k_seq_stride % 8) return SA_ERR_INVALID;
+    const int64_t s_np = (int64_t)a->s * a->n_pos;
+    if (a->b > 1) {
+        if (a->q_seq_stride < (int64_t)a->s * a->h * a->d || a->k_seq_stride < (int64_t)a->n_pos * a->d ||
+            a->w_seq_stride < (int64_t)a->s * a->h || a->pos_seq_stride < a->s || a->scores_seq_stride < s_np ||
+            (a->cand && a->cand_seq_stride < s_np))
+            return SA_ERR_INVALID;
+    }
+    if (a->idx) {
+        if (a->topk < 1 || a->idx_row_stride < a->topk) return SA_ERR_INVALID;
+        if (a->b > 1 && a->idx_seq_stride < (int64_t)(a->s - 1) * a->idx_row_stride + a->topk) return SA_ERR_INVALID;
+        if (a->n_pos > 32768) return SA_ERR_UNSUPPORTED;
+    }
+    sa::IdxParams p{};
+    p.b = a->b; p.s = a->s; p.h = a->h; p.d = a->d; p.n_pos = a->n_pos; p.ratio = a->ratio;
+    p.q = (const uint16_t*)a->q; p.q_seq_stride = a->q_seq_stride;
+    p.k = (const uint16_t*)a->k; p.k_seq_stride = a->k_seq_stride;
+    p.w = a->w; p.w_seq_stride = a->w_seq_stride;
+    p.pos = a->pos; p.pos_seq_stride = a->pos_seq_stride;
+    p.cand = a->cand; p.cand_seq_stride = a->cand_seq_stride;
+    p.scores = a->scores; p.scores_seq_stride = a->scores_seq_stride;
+    p.topk = a->topk; p.offset = a->offset;
+    p.idx = a->idx; p.idx_seq_stride = a->idx_seq_stride; p.idx_row_stride = a->idx_row_stride;
+    hipError_t e = sa::launch_index_scores(p, (hipStream_t)stream);
+    if (e == hipSuccess && a->idx) e = sa::launch_index_topk(p, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}
+
+SA_EXPORT int sa_candidate_blocks(const sa_candidate_args* a, void* stream) {
+    if (!a) return SA_ERR_INVALID;
+    if (a->b < 1 || a->s < 1 || a->n_pos < 1 || a->ratio < 1 || a->topk_blocks < 1 || a->block_size < 1)
+        return SA_ERR_INVALID;
+    if (!a->logits || !a->pos || !a->mask || !aligned(a->logits, 4) || !aligned(a->pos, 4)) return SA_ERR_INVALID;
+    const int64_t s_np = (int64_t)a->s * a->n_pos;
+    if (a->b > 1 && (a->logits_seq_stride < s_np || a->mask_seq_stride < s_np || a->pos_seq_stride < a->s))
+        return SA_ERR_INVALID;
+    if ((a->n_pos + (int64_t)a->block_size - 1) / a->block_size > 32768) return SA_ERR_UNSUPPORTED;
+    sa::CandParams p{};
+    p.b = a->b; p.s = a->s; p.n_pos = a->n_pos; p.ratio = a->ratio;
+    p.topk_blocks = a->topk_blocks; p.block_size = a->block_size;
+    p.logits = a->logits; p.logits_seq_stride = a->logits_seq_stride;
+    p.pos = a->pos; p.pos_seq_stride = a->pos_seq_stride;
+    p.mask = a->mask; p.mask_seq_stride = a->mask_seq_stride;
+    const hipError_t e = sa::launch_candidate_blocks(p, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}

@@ -54,6 +54,27 @@ struct KvWriteParams {
     int32_t* err_word;
 };
 
+// One indexer launch (sa_indexer_topk): scores, then the top-k lists.
+struct IdxParams {
+    int32_t b, s, h, d, n_pos, ratio;
+    const uint16_t* q;       int64_t q_seq_stride;        // elements
+    const uint16_t* k;       int64_t k_seq_stride;
+    const float* w;          int64_t w_seq_stride;
+    const int32_t* pos;      int64_t pos_seq_stride;
+    const uint8_t* cand;     int64_t cand_seq_stride;
+    float* scores;           int64_t scores_seq_stride;
+    int32_t topk, offset;
+    int32_t* idx;            int64_t idx_seq_stride, idx_row_stride;
+};
+
+// One sa_candidate_blocks launch.
+struct CandParams {
+    int32_t b, s, n_pos, ratio, topk_blocks, block_size;
+    const float* logits;     int64_t logits_seq_stride;
+    const int32_t* pos;      int64_t pos_seq_stride;
+    uint8_t* mask;           int64_t mask_seq_stride;
+};
+
 // Split plan shared by sa_sparse_attn and sa_sparse_attn_workspace.
 struct Plan {
     int nw;             // waves per workgroup
@@ -75,6 +96,9 @@ hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, cons
                               hipStream_t st);
 hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int32_t yarn, int32_t low,
                              int32_t high, float factor, float* cs, hipStream_t st);
+hipError_t launch_index_scores(const IdxParams& p, hipStream_t st);
+hipError_t launch_index_topk(const IdxParams& p, hipStream_t st);
+hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
 hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
                             uint8_t* scales, uint16_t* rt, hipStream_t st);

@@ -157,3 +157,147 @@ def test_kv_write_linear_store_and_invalid_rows(orc):
     assert np.array_equal(cache[1, 7], rows[1, 0]) and np.array_equal(cache[1, 9], rows[1, 2])
     assert np.all(cache[1, 8] == 0x7777)                                 # position 99: nothing
     assert np.all(cache[1, :7] == 0x7777)
+
+
+# ------------------------------------------------------------------ indexer (compressed top-k)
+def _index_inputs(seed, b, s, h, d, n_pos, integer=False):
+    g = torch.Generator().manual_seed(seed)
+    if integer:
+        q = torch.randint(-3, 4, (b, s, h, d), generator=g).float()
+        k = torch.randint(-3, 4, (b, n_pos, d), generator=g).float()
+        w = 2.0 ** torch.randint(-2, 2, (b, s, h), generator=g).float()
+    else:
+        q = torch.randn(b, s, h, d, generator=g)
+        k = torch.randn(b, n_pos, d, generator=g)
+        w = torch.randn(b, s, h, generator=g) * (d ** -0.5 * h ** -0.5)
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    return (qb.view(torch.int16).numpy().view(np.uint16), kb.view(torch.int16).numpy().view(np.uint16),
+            w.numpy().astype(np.float32), qb.double(), kb.double(), w.double())
+
+
+def test_index_scores_vs_einsum(orc):
+    """The indexer's score as torch evaluates the page's einsum, in f64: relu(q . k) times
+    the head weights, summed over heads; -inf beyond each query's (pos+1)//ratio visible
+    positions and outside the candidate mask."""
+    b, s, h, d, n_pos, ratio = 2, 7, 8, 64, 40, 4
+    q, k, w, qd, kd, wd = _index_inputs(1, b, s, h, d, n_pos)
+    pos = np.array([[0, 3, 4, 50, 100, 159, 200], [7, 8, 9, 10, 11, 12, 300]], np.int32)
+    cand = (np.random.default_rng(2).random((b, s, n_pos)) < 0.7).astype(np.uint8)
+    got = orc.index_scores(q, k, w, pos, ratio, cand)
+    ref = (torch.einsum("bshd,btd->bsht", qd, kd).relu() * wd[..., None]).sum(2).numpy()
+    vis = np.minimum((pos + 1) // ratio, n_pos)
+    t = np.arange(n_pos)
+    live = (t[None, None, :] < vis[..., None]) & (cand == 1)
+    assert np.all(np.isneginf(got[~live]))
+    assert np.allclose(got[live], ref[live], rtol=1e-5, atol=1e-6)
+
+
+def _rank_select(scores, topk):
+    """Brute force by ranks: a finite position is chosen when fewer than topk positions beat
+    it (a higher score, or the same score at a lower position)."""
+    n = scores.size
+    chosen = []
+    for t in range(n):
+        if not np.isfinite(scores[t]):
+            continue
+        beat = sum(1 for u in range(n) if np.isfinite(scores[u]) and
+                   (scores[u] > scores[t] or (scores[u] == scores[t] and u < t)))
+        if beat < topk:
+            chosen.append(t)
+    return chosen
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_index_topk_brute_force(orc, integer):
+    """Top-k, re-sorted by position, shifted by the offset, -1 padded (Indexer.forward's last
+    lines), against rank counting; integer scores make ties common, which go to the lower
+    position."""
+    b, s, h, d, n_pos, ratio, topk, off = 2, 9, 4, 32, 24, 2, 7, 128
+    q, k, w, *_ = _index_inputs(3, b, s, h, d, n_pos, integer=integer)
+    pos = np.array([[0, 1, 2, 5, 9, 13, 20, 40, 60]] * b, np.int32)
+    sc = orc.index_scores(q, k, w, pos, ratio)
+    if integer:
+        assert len(np.unique(sc[np.isfinite(sc)])) < np.isfinite(sc).sum()   # ties present
+    idx = orc.index_topk(sc, topk, off)
+    for bi in range(b):
+        for si in range(s):
+            want = _rank_select(sc[bi, si], topk)
+            row = idx[bi, si]
+            assert row[: len(want)].tolist() == [t + off for t in want]
+            assert np.all(row[len(want):] == -1)
+
+
+def test_index_topk_lists_every_visible_position_when_few(orc):
+    """With at most topk visible positions the list is all of them in order: offset ..
+    offset + (p+1)//ratio - 1, then -1 (closed form of the causal prefill)."""
+    b, s, h, d, n_pos, ratio, topk = 1, 64, 4, 32, 16, 4, 16
+    q, k, w, *_ = _index_inputs(4, b, s, h, d, n_pos)
+    pos = np.arange(s, dtype=np.int32)[None]
+    idx = orc.index_topk(orc.index_scores(q, k, w, pos, ratio), topk, 128)
+    for t in range(s):
+        v = min((t + 1) // ratio, n_pos)
+        assert idx[0, t].tolist() == list(range(128, 128 + v)) + [-1] * (topk - v)
+
+
+def _blocks_brute(row, length, topk_blocks, bs):
+    n = row.size
+    nblk = -(-n // bs)
+    last = (length - 1) // bs                                     # Python floor division
+    sc = []
+    for j in range(nblk):
+        vals = [row[t] if t < n else -np.inf for t in range(j * bs, (j + 1) * bs)]
+        sc.append(np.inf if j == last else max(vals))
+    keep = []
+    for j in range(nblk):
+        beat = sum(1 for u in range(nblk) if sc[u] > sc[j] or (sc[u] == sc[j] and u < j))
+        keep.append(beat < min(topk_blocks, nblk) and sc[j] > -np.inf)
+    return np.repeat(np.array(keep, np.uint8), bs)[:n]
+
+
+@pytest.mark.parametrize("topk_blocks", [1, 3, 6, 50])
+def test_candidate_blocks_brute_force(orc, topk_blocks):
+    """select_candidate_blocks against rank counting over block maxima, with the newest
+    partly filled block pinned; blocks with no finite logit are never kept."""
+    b, s, h, d, n_pos, ratio, bs = 1, 12, 4, 32, 45, 2, 8
+    q, k, w, *_ = _index_inputs(5, b, s, h, d, n_pos, integer=True)
+    pos = np.array([[0, 1, 2, 9, 16, 17, 30, 47, 60, 70, 89, 200]], np.int32)
+    logits = orc.index_scores(q, k, w, pos, ratio)
+    mask = orc.candidate_blocks(logits, pos, ratio, topk_blocks, bs)
+    for si in range(s):
+        length = (int(pos[0, si]) + 1) // ratio
+        assert np.array_equal(mask[0, si], _blocks_brute(logits[0, si], length, topk_blocks, bs)), si
+        if length == 0:
+            assert not mask[0, si].any()
+        elif length <= n_pos:
+            assert mask[0, si, length - 1] == 1                  # the pinned block
+
+
+def test_candidate_blocks_keep_every_reachable_block_when_few(orc):
+    """With at least as many picks as blocks (the config's 2048 blocks of 8 at 16384
+    positions), every block holding a visible position is kept and nothing else."""
+    b, s, h, d, n_pos, ratio, bs = 1, 5, 4, 32, 64, 4, 8
+    q, k, w, *_ = _index_inputs(6, b, s, h, d, n_pos)
+    pos = np.array([[3, 40, 100, 255, 1000]], np.int32)
+    mask = orc.candidate_blocks(orc.index_scores(q, k, w, pos, ratio), pos, ratio, 8, bs)
+    for si in range(s):
+        v = min((int(pos[0, si]) + 1) // ratio, n_pos)
+        want = np.zeros(n_pos, np.uint8)
+        want[: -(-v // bs) * bs] = 1
+        assert np.array_equal(mask[0, si], want[:n_pos])
+
+
+def test_two_level_selection_stays_inside_the_candidates(orc):
+    """Level two masks its own scores to the level-one candidates: every listed position is
+    a candidate and visible."""
+    b, s, h, d, n_pos, ratio, bs = 2, 6, 8, 64, 96, 2, 8
+    q, k, w, *_ = _index_inputs(7, b, s, h, d, n_pos)
+    q2, _, w2, *_ = _index_inputs(8, b, s, h, d, n_pos)
+    pos = np.array([[10, 50, 90, 120, 150, 191]] * b, np.int32)
+    cand = orc.candidate_blocks(orc.index_scores(q, k, w, pos, ratio), pos, ratio, 3, bs)
+    idx = orc.index_topk(orc.index_scores(q2, k, w2, pos, ratio, cand), 10, 0)
+    for bi in range(b):
+        for si in range(s):
+            sel = idx[bi, si][idx[bi, si] >= 0]
+            vis = (pos[bi, si] + 1) // ratio
+            assert sel.size == min(10, int(cand[bi, si, :vis].sum()))
+            assert np.all(cand[bi, si, sel] == 1) and np.all(sel < (pos[bi, si] + 1) // ratio)
