@@ -634,6 +634,71 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool):
     return rec
 
 
+PROJ = {   # name: (tokens, weight storage)
+    "wo_proj_decode": (64, "bf16"),         # the 64 decode queries of the window + compressed decode
+    "wo_proj_decode_fp8": (64, "fp8"),
+    "wo_proj_prefill": (8192, "bf16"),      # the long prefill's 8192 queries
+}
+
+
+def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool):
+    """The grouped output projection (sa_grouped_proj) at the model config's 8 groups of
+    o_lora_rank 1024 on 128 heads of 512 (k 8192 per group). Decode streams the weights once
+    (HBM-bound); the prefill is a dense bf16 contraction (MFMA-bound)."""
+    m, wfmt = PROJ[name]
+    g, r, kg = 8, 1024, 8192
+    gen = torch.Generator().manual_seed(51)
+    o0 = torch.randn(m, g * kg, generator=gen).to(torch.bfloat16)
+    w0 = (torch.randn(g, r, kg, generator=gen) * kg ** -0.5).to(torch.bfloat16)
+    flops = 2.0 * m * g * r * kg
+    w_bytes = g * r * kg * (2 if wfmt == "bf16" else 1) + (g * r * kg // 32 if wfmt == "fp8" else 0)
+    alg_bytes = w_bytes + m * g * kg * 2 + m * g * r * 2
+    nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / alg_bytes)))
+    wd = w0.to(dev)
+    wsc = None
+    if wfmt == "fp8":
+        wd, wsc = sa.quant_kv_fp8(wd, want=("codes", "scales"))
+    sets = [dict(o=o0.to(dev), w=wd if i == 0 else wd.clone(), ws=None if wsc is None else (wsc if i == 0 else wsc.clone()),
+                 out=torch.empty(m, g, r, dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
+    fns = [(lambda x=x: sa.grouped_proj(x["o"], x["w"], w_scale=x["ws"], out=x["out"])) for x in sets]
+    ms_step = time_graph_steps(fns, steps, warmup)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(20, 5 * steps)))
+    if m <= 64:
+        achieved = alg_bytes / (k_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        value, unit, metric = alg_bytes / (ms_step * 1e-3) / 1e9, "GB/s", "grouped wo_a GB/s (decode)"
+    else:
+        achieved = flops / (k_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+        value, unit, metric = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", "grouped wo_a TFLOP/s (prefill)"
+    roof.update({"traffic": None, "kernel": "proj_skinny_kernel" if m <= 64 else "proj_tiled_kernel",
+                 "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
+                 "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops})
+    rec = {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step, "steps": steps,
+           "dtype": "bf16 (f32 accumulation)" if wfmt == "bf16" else "fp8-e4m3 weights, bf16 compute",
+           "config": {"workload": name, "tokens": m, "groups": g, "rank": r, "k_per_group": kg,
+                      "weights": wfmt},
+           "roofline": roof, "cpu_baseline": None}
+    if cpu:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+        from sa_harness import u16
+        ms = 2 if m > 64 else 8
+        oq, wq = u16(o0[:ms]).reshape(ms, g, kg), u16(w0)
+        threads = oracle.max_threads()
+        per, reps, dt = _oracle_seconds(lambda: oracle.grouped_proj(oq, wq, nthreads=threads), 2.0)
+        per_step = per * m / ms
+        val = (alg_bytes / per_step / 1e9, "GB/s") if m <= 64 else (flops / per_step / 1e12, "TFLOP/s")
+        rec["cpu_baseline"] = {"value": val[0], "unit": val[1], "cores": threads, "kind": "oracle",
+                               "sample": f"{ms} of {m} tokens (bf16 weights) x {reps} run(s), {dt:.1f} s wall, "
+                                         f"scaled to one step"}
+    del sets, fns
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -713,6 +778,12 @@ def main():
                   f"{r['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {r['roofline']['frac']:.3f} of "
                   f"{r['roofline']['bound']}; candidate blocks {r['candidate_blocks']['kernel_ms_mean'] * 1e3:.2f} us "
                   f"({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
+        for name in PROJ:
+            r = measure_proj(name, dev, args.steps, args.warmup, cpu)
+            records.append(r)
+            print(f"[bench] {name}: {r['value']:.4g} {r['unit']}, kernel "
+                  f"{r['roofline']['kernel_ms_mean'] * 1e3:.2f} us, {r['roofline']['frac']:.3f} of "
+                  f"{r['roofline']['bound']} ({time.perf_counter() - t_start:.0f} s)", file=sys.stderr, flush=True)
         for name in KV_WRITE:
             r = measure_kv_write(name, dev, args.steps, args.warmup, cpu)
             records.append(r)

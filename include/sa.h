@@ -253,6 +253,33 @@ typedef struct sa_candidate_args {
 
 int sa_candidate_blocks(const sa_candidate_args *a, void *stream);
 
+/* The grouped output projection, the step after sparse_attn and its inverse RoPE
+ * (attention output page, Attention.forward: the output viewed as [tokens][o_groups]
+ * [heads/o_groups * head_dim] is multiplied group by group with wo_a viewed as
+ * [o_groups][o_lora_rank][heads/o_groups * head_dim], the einsum "bsgd,grd->bsgr"; wo_a is
+ * block-diagonal over groups). For token t, group gg and row n < r:
+ *   out[t][gg][n] = sum over k < kg of o[t][gg][k] * W[gg][n][k]
+ * with f32 accumulation, rounded to bf16 (the attention API docs' precision paragraph: a
+ * bf16 GEMM). W is bf16, or (w_format SA_KV_FP8_E4M3_B32) e4m3 codes with e8m0 scale bytes
+ * per 32 consecutive k (sa_quant_kv_fp8's form, rows of kg), whose values are exact bf16
+ * values: the result is the bf16 product with the decoded weights, at half the weight
+ * bytes (the page's note on an fp8 grouped GEMM). Supported: kg a multiple of 64 and r a
+ * multiple of 128, or m <= 64 with r a multiple of 16 and kg a multiple of 512. Device
+ * pointers, caller-owned, 16-byte aligned (w_scale: any); strides in elements. */
+typedef struct sa_grouped_proj_args {
+    int32_t m;              /* tokens */
+    int32_t g;              /* groups (o_groups) */
+    int32_t r;              /* rows of W per group (o_lora_rank) */
+    int32_t kg;             /* k per group: heads per group * head_dim */
+    const void *o;          int64_t o_stride;            /* bf16 [m][>= g * kg] */
+    int32_t w_format;                                    /* SA_KV_BF16 or SA_KV_FP8_E4M3_B32 */
+    const void *w;                                       /* bf16 or e4m3 [g][r][kg] */
+    const uint8_t *w_scale;                              /* e8m0 [g][r][kg / 32] (fp8 only) */
+    void *out;              int64_t out_stride;          /* bf16 [m][>= g * r] */
+} sa_grouped_proj_args;
+
+int sa_grouped_proj(const sa_grouped_proj_args *a, void *stream);
+
 /* The (cos, sin) table that the inverse-RoPE epilogue reads (rope_cos_sin above):
  * precompute_freqs_cis of Attention.__init__ (atlas.klimoza.dev/.../attention/output,
  * precompute_freqs_cis; attention API docs, "freqs_cis"), evaluated on the device with the

@@ -84,6 +84,7 @@ def lib():
             "orc_index_scores": (C.c_int, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P, I32]),
             "orc_index_topk": (C.c_int, [P, I32, I32, I32, I32, I32, P]),
             "orc_candidate_blocks": (C.c_int, [P, P, I32, I32, I32, I32, I32, I32, P]),
+            "orc_grouped_proj": (C.c_int, [P, I64, P, I32, I32, I32, I32, P, I32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -339,4 +340,17 @@ def candidate_blocks(logits, pos, ratio: int, topk_blocks: int, block_size: int)
     if lib().orc_candidate_blocks(_ptr(logits), _ptr(pos), b, s, n_pos, ratio, topk_blocks,
                                   block_size, _ptr(out)):
         raise ValueError("orc_candidate_blocks rejected its arguments")
+    return out
+
+
+# ---------------------------------------------------------------- grouped output projection
+def grouped_proj(o, w, nthreads: int = 0) -> np.ndarray:
+    """o: bf16 (u16) [m][g][kg]; w: bf16 (u16) [g][r][kg] -> bf16 (u16) [m][g][r]."""
+    o, w = _u16(o), _u16(w)
+    m, g, kg = o.shape
+    r = w.shape[1]
+    assert w.shape == (g, r, kg)
+    out = np.empty((m, g, r), np.uint16)
+    if lib().orc_grouped_proj(_ptr(o), g * kg, _ptr(w), m, g, r, kg, _ptr(out), nthreads):
+        raise ValueError("orc_grouped_proj rejected its arguments")
     return out

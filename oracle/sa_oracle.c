@@ -724,3 +724,34 @@ int orc_candidate_blocks(const float *logits, const int32_t *pos, int32_t b, int
     free(keep);
     return 0;
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Grouped output projection. [attn-fwd] Attention.forward: the attention output is      */
+/* viewed as [tokens][groups][heads_per_group * head_dim] and multiplied, group by group, */
+/* with wo_a viewed as [groups][o_lora_rank][heads_per_group * head_dim] (einsum          */
+/* "bsgd,grd->bsgr"; wo_a is block-diagonal over groups). [attn-docs] precision           */
+/* paragraph: a bf16 GEMM, f32 accumulation, bf16 result (round to nearest even).        */
+/* o: bf16 rows of m tokens, token stride o_stride (elements) >= g * kg; w: bf16          */
+/* [g][r][kg]; out: bf16 [m][g][r].                                                       */
+/* ------------------------------------------------------------------------------------ */
+int orc_grouped_proj(const uint16_t *o, int64_t o_stride, const uint16_t *w, int32_t m,
+                     int32_t g, int32_t r, int32_t kg, uint16_t *out, int32_t nthreads)
+{
+    if (!o || !w || !out || m < 1 || g < 1 || r < 1 || kg < 1 || o_stride < (int64_t)g * kg) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t t = 0; t < m; ++t)
+        for (int32_t gg = 0; gg < g; ++gg) {
+            const uint16_t *a = o + t * o_stride + (int64_t)gg * kg;
+            for (int32_t rr = 0; rr < r; ++rr) {
+                const uint16_t *wr = w + ((int64_t)gg * r + rr) * kg;
+                float acc = 0.0f;
+                for (int32_t k = 0; k < kg; ++k) acc += orc_bf16_to_f32(a[k]) * orc_bf16_to_f32(wr[k]);
+                out[(t * g + gg) * (int64_t)r + rr] = orc_f32_to_bf16(acc);
+            }
+        }
+    (void)nthreads;
+    return 0;
+}

@@ -139,6 +139,12 @@ int orc_candidate_blocks(const float *logits, const int32_t *pos, int32_t b, int
                          int32_t n_pos, int32_t ratio, int32_t topk_blocks, int32_t block_size,
                          uint8_t *mask);
 
+/* ---- grouped output projection ([attn-fwd] Attention.forward, the wo_a einsum):
+ * out bf16 [m][g][r] = per group gg, o[t][gg][:] . w[gg][rr][:] in f32, rounded to bf16.
+ * o: bf16 tokens of g * kg elements at stride o_stride; w: bf16 [g][r][kg]. */
+int orc_grouped_proj(const uint16_t *o, int64_t o_stride, const uint16_t *w, int32_t m,
+                     int32_t g, int32_t r, int32_t kg, uint16_t *out, int32_t nthreads);
+
 /* threads an nthreads <= 0 call uses (the OpenMP default), 1 without OpenMP */
 int32_t orc_max_threads(void);
 

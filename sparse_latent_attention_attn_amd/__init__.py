@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "SaError", "lib", "sparse_attn", "sparse_attn_noalloc", "sparse_attn_workspace_bytes", "window_topk_idxs",
     "quant_kv_fp8", "rope_table", "kv_write", "KvWriteArgs", "indexer_topk", "candidate_blocks",
-    "IndexerArgs", "CandidateArgs", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
+    "IndexerArgs", "CandidateArgs", "grouped_proj", "GroupedProjArgs", "KV_BF16", "KV_FP8", "FLAG_CHECK_IDX", "AttnArgs",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -99,6 +99,16 @@ class CandidateArgs(C.Structure):
     ]
 
 
+class GroupedProjArgs(C.Structure):
+    """Mirror of sa_grouped_proj_args in include/sa.h."""
+    _fields_ = [
+        ("m", C.c_int32), ("g", C.c_int32), ("r", C.c_int32), ("kg", C.c_int32),
+        ("o", C.c_void_p), ("o_stride", C.c_int64),
+        ("w_format", C.c_int32), ("w", C.c_void_p), ("w_scale", C.c_void_p),
+        ("out", C.c_void_p), ("out_stride", C.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -129,6 +139,8 @@ def lib():
         L.sa_indexer_topk.argtypes = [C.POINTER(IndexerArgs), P]
         L.sa_candidate_blocks.restype = C.c_int
         L.sa_candidate_blocks.argtypes = [C.POINTER(CandidateArgs), P]
+        L.sa_grouped_proj.restype = C.c_int
+        L.sa_grouped_proj.argtypes = [C.POINTER(GroupedProjArgs), P]
         L.sa_kv_write.restype = C.c_int
         L.sa_kv_write.argtypes = [C.POINTER(KvWriteArgs), P]
         L.sa_quant_kv_fp8.restype = C.c_int
@@ -424,6 +436,45 @@ def candidate_blocks(logits, pos, ratio: int, topk_blocks: int, block_size: int,
     a.mask, a.mask_seq_stride = _ptr(mask), _seq_major(mask, "mask", 2)
     _check("sa_candidate_blocks", lib().sa_candidate_blocks(C.byref(a), C.c_void_p(_stream(dev))))
     return mask
+
+
+def grouped_proj(o, w, *, w_scale=None, out=None):
+    """The grouped output projection (sa_grouped_proj in include/sa.h). o: bf16 holding m
+    tokens of g * kg elements (e.g. sparse_attn's output [b][s][h][d]; viewed as [m][g * kg]
+    without a copy); w: bf16 [g][r][kg], or uint8 e4m3 codes [g][r][kg] with w_scale uint8
+    [g][r][kg/32]. Returns out, bf16 [m][g][r]."""
+    dev = o.device
+    _need(o, torch.bfloat16, "o", dev)
+    if w.dim() != 3:
+        raise ValueError("w must be [g][r][kg]")
+    g, r, kg = w.shape
+    if o.numel() % (g * kg) != 0:
+        raise ValueError("o must hold whole tokens of g * kg elements")
+    tok = o.view(-1, g * kg)
+    m = tok.shape[0]
+    if out is None:
+        out = torch.empty(m, g, r, dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", dev)
+    if tuple(out.shape) != (m, g, r) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [m][g][r]")
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    a = GroupedProjArgs()
+    a.m, a.g, a.r, a.kg = m, g, r, kg
+    a.o, a.o_stride = _ptr(tok), tok.stride(0)
+    if w.dtype == torch.bfloat16:
+        _need(w, torch.bfloat16, "w", dev)
+        a.w_format = KV_BF16
+    else:
+        _need(w, torch.uint8, "w", dev)
+        if w_scale is None:
+            raise ValueError("fp8 weights need w_scale")
+        _need(w_scale, torch.uint8, "w_scale", dev)
+        a.w_format, a.w_scale = KV_FP8, _ptr(w_scale)
+    a.w = _ptr(w)
+    a.out, a.out_stride = _ptr(out), g * r
+    _check("sa_grouped_proj", lib().sa_grouped_proj(C.byref(a), C.c_void_p(_stream(dev))))
+    return out
 
 
 def rope_table(rope_dim: int, max_pos: int, base: float = 10000.0, device="cuda", *,

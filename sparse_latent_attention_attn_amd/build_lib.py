@@ -33,6 +33,7 @@ SOURCES = {
     "aux_kernels.hip": VGPR_ACC,
     "noalloc.hip": [],
     "indexer.hip": VGPR_ACC,
+    "wo_proj.hip": [],
 }
 
 _NOISE = ("is not a recognized feature for this target", "(ignoring feature)")

@@ -378,3 +378,30 @@ SA_EXPORT int sa_candidate_blocks(const sa_candidate_args* a, void* stream) {
     const hipError_t e = sa::launch_candidate_blocks(p, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
 }
+
+SA_EXPORT int sa_grouped_proj(const sa_grouped_proj_args* a, void* stream) {
+    if (!a) return SA_ERR_INVALID;
+    if (a->m < 1 || a->g < 1 || a->r < 1 || a->kg < 1) return SA_ERR_INVALID;
+    if (a->w_format != SA_KV_BF16 && a->w_format != SA_KV_FP8_E4M3_B32) return SA_ERR_INVALID;
+    const bool fp8 = a->w_format == SA_KV_FP8_E4M3_B32;
+    if (!a->o || !a->w || !a->out || (fp8 && !a->w_scale)) return SA_ERR_INVALID;
+    if (!aligned(a->o, 16) || !aligned(a->w, 16) || !aligned(a->out, 16)) return SA_ERR_INVALID;
+    if (a->o_stride < (int64_t)a->g * a->kg || a->out_stride < (int64_t)a->g * a->r || a->o_stride % 8 ||
+        a->out_stride % 8)
+        return SA_ERR_INVALID;
+    const bool skinny = a->m <= 64 && a->r % 16 == 0 && a->kg % 512 == 0;
+    if (!skinny && (a->r % 128 != 0 || a->kg % 64 != 0)) return SA_ERR_UNSUPPORTED;
+    if ((int64_t)a->g * a->r * a->kg > ((int64_t)1 << 40)) return SA_ERR_UNSUPPORTED;
+    sa::ProjParams p{};
+    p.m = a->m; p.g = a->g; p.r = a->r; p.kg = a->kg;
+    p.o = (const uint16_t*)a->o; p.o_stride = a->o_stride;
+    if (fp8) {
+        p.wq = (const uint8_t*)a->w;
+        p.ws = a->w_scale;
+    } else {
+        p.w = (const uint16_t*)a->w;
+    }
+    p.out = (uint16_t*)a->out; p.out_stride = a->out_stride;
+    const hipError_t e = sa::launch_grouped_proj(p, (hipStream_t)stream);
+    return e == hipSuccess ? SA_OK : (e == hipErrorInvalidValue ? SA_ERR_UNSUPPORTED : SA_ERR_HIP);
+}

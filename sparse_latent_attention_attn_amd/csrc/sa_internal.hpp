@@ -75,6 +75,15 @@ struct CandParams {
     uint8_t* mask;           int64_t mask_seq_stride;
 };
 
+// One grouped output projection (sa_grouped_proj): out[t][gg][:] = o[t][gg][:] . W[gg]^T.
+struct ProjParams {
+    int32_t m, g, r, kg;                 // tokens, groups, rows of W per group, K per group
+    const uint16_t* o;       int64_t o_stride;       // bf16 tokens, stride in elements
+    const uint16_t* w;                              // bf16 [g][r][kg], or null with fp8
+    const uint8_t* wq;       const uint8_t* ws;     // e4m3 [g][r][kg] + e8m0 [g][r][kg/32]
+    uint16_t* out;           int64_t out_stride;     // bf16 [m][g][r], stride in elements
+};
+
 // Split plan shared by sa_sparse_attn and sa_sparse_attn_workspace.
 struct Plan {
     int nw;             // waves per workgroup
@@ -99,6 +108,7 @@ hipError_t launch_rope_table(int32_t rope_dim, int32_t max_pos, float base, int3
 hipError_t launch_index_scores(const IdxParams& p, hipStream_t st);
 hipError_t launch_index_topk(const IdxParams& p, hipStream_t st);
 hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st);
+hipError_t launch_grouped_proj(const ProjParams& p, hipStream_t st);
 hipError_t launch_kv_write(const KvWriteParams& p, hipStream_t st);
 hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
                             uint8_t* scales, uint16_t* rt, hipStream_t st);

@@ -159,3 +159,21 @@ def test_kv_write_rejects_before_any_hip_call(sa, field, value, status):
 def test_kv_write_linear_needs_row0(sa):
     assert sa.lib().sa_kv_write(C.byref(_kv_args(sa, window=0)), None) == -1
     assert sa.lib().sa_kv_write(None, None) == -1
+
+
+def test_grouped_proj_validation(sa):
+    L = sa.lib()
+
+    def args(**kw):
+        a = sa.GroupedProjArgs()
+        a.m, a.g, a.r, a.kg = 300, 2, 256, 512
+        a.o = a.w = a.out = 0x10000
+        a.o_stride, a.out_stride = 1024, 512
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    for kw, st in (({"m": 0}, -1), ({"w_format": 5}, -1), ({"o": 0}, -1), ({"w_format": 1}, -1),
+                   ({"o_stride": 1000}, -1), ({"out_stride": 100}, -1), ({"r": 200}, -2),
+                   ({"kg": 96, "o_stride": 192}, -2), ({"o": 0x10008}, -1)):
+        assert L.sa_grouped_proj(C.byref(args(**kw)), None) == st, kw
+    assert L.sa_grouped_proj(None, None) == -1

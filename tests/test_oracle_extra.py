@@ -301,3 +301,41 @@ def test_two_level_selection_stays_inside_the_candidates(orc):
             vis = (pos[bi, si] + 1) // ratio
             assert sel.size == min(10, int(cand[bi, si, :vis].sum()))
             assert np.all(cand[bi, si, sel] == 1) and np.all(sel < (pos[bi, si] + 1) // ratio)
+
+
+# ------------------------------------------------------------------ grouped output projection
+def _proj_inputs(seed, m, g, r, kg, integer=False):
+    gen = torch.Generator().manual_seed(seed)
+    if integer:
+        o = torch.randint(-4, 5, (m, g, kg), generator=gen).float()
+        w = torch.randint(-4, 5, (g, r, kg), generator=gen).float()
+    else:
+        o = torch.randn(m, g, kg, generator=gen)
+        w = torch.randn(g, r, kg, generator=gen) * kg ** -0.5
+    return o.to(torch.bfloat16), w.to(torch.bfloat16)
+
+
+def test_grouped_proj_vs_einsum(orc):
+    """The page's einsum "bsgd,grd->bsgr" evaluated by torch in f64, then rounded to bf16:
+    the f32 oracle differs by at most one bf16 rounding step."""
+    o, w = _proj_inputs(1, 7, 4, 24, 96)
+    got = _f32(orc.grouped_proj(o.view(torch.int16).numpy().view(np.uint16), w.view(torch.int16).numpy().view(np.uint16)))
+    ref = torch.einsum("mgd,grd->mgr", o.double(), w.double())
+    refb = ref.to(torch.bfloat16).double()
+    assert np.all(np.abs(got - refb.numpy()) <= np.abs(ref.numpy()) * 2 ** -8 + 1e-6)
+    assert (got == refb.numpy()).mean() > 0.97
+
+
+def test_grouped_proj_exact_and_block_diagonal(orc):
+    """Small integers: every partial sum is exact, so the oracle equals the exact einsum;
+    changing one group's input changes only that group's output (block-diagonal wo_a)."""
+    o, w = _proj_inputs(2, 5, 3, 16, 64, integer=True)
+    ou = lambda t: t.view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    got = orc.grouped_proj(ou(o), ou(w))
+    ref = torch.einsum("mgd,grd->mgr", o.double(), w.double()).to(torch.bfloat16)
+    assert np.array_equal(got, ou(ref))
+    o2 = o.clone()
+    o2[:, 1] = -o2[:, 1]
+    got2 = orc.grouped_proj(ou(o2), ou(w))
+    assert np.array_equal(got2[:, [0, 2]], got[:, [0, 2]])
+    assert np.array_equal(_f32(got2[:, 1]), -_f32(got[:, 1]))
