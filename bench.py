@@ -1,7 +1,9 @@
 """Benchmark of the sparse latent attention hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: the window index lists
-(sa_window_topk_idxs) followed by sparse_attn with the inverse-RoPE epilogue. Inputs are
+A step is one pass of the whole path over one batch: sparse_attn with its window index
+lists generated inside the kernel from the query positions (the fused form of
+sa_window_topk_idxs; --explicit-window launches that first and reads the whole list), the
+compressed columns read from the index lists, and the inverse-RoPE epilogue. Inputs are
 seeded and synthetic and already resident in HBM.
 
 The default run reports the long-context prefill with compression (1 sequence of 8192
@@ -54,6 +56,10 @@ BF16_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4
 MALL_BYTES = 256 << 20
 
 DECODE = {"decode_window", "decode_compress"}
+# The window lists are generated inside sparse_attn from the query positions (its fused
+# window mode), so a step is one kernel; --explicit-window runs sa_window_topk_idxs first
+# and has sparse_attn read the whole list from idx.
+FUSED_WINDOW = True
 # the roofline that bounds each workload's kernel (arithmetic intensity against the ridge
 # of 2516.6 TFLOP/s / 8 TB/s = 315 flop/B): the window-only prefill does 126 flop/B
 HBM_BOUND = {"decode_window", "decode_compress", "prefill_window"}
@@ -80,7 +86,8 @@ def algorithmic(w: W.Workload, idx: np.ndarray, kv_format: str, epilogue: bool =
     kv_bytes = distinct * row_bytes
     nq = w.b * w.s
     qo_bytes = 2 * nq * w.h * w.d * 2
-    idx_bytes = nq * w.topk * 4
+    # with fused window lists only the compressed columns of idx are read
+    idx_bytes = nq * (w.topk - (w.win_cols if FUSED_WINDOW else 0)) * 4
     small = w.h * 4 + (nq * 4 + nq * (w.rd // 2) * 8 if epilogue else 0)   # sink, positions, rope rows
     attn_bytes = kv_bytes + qo_bytes + idx_bytes + small
     flops = 4.0 * w.h * w.d * valid_pairs
@@ -105,12 +112,15 @@ class Step:
                             out=self.idx_view)
 
     def attend(self):
-        sa.sparse_attn(self.q, self.kv, self.sink, self.idx, self.w.scale, out=self.out,
+        w = self.w
+        fused = (w.window, "chunk" if w.win_start_pos is None else "ring", self.pos) if FUSED_WINDOW else None
+        sa.sparse_attn(self.q, self.kv, self.sink, self.idx, w.scale, out=self.out,
                        kv_scale=self.kv_scale, rope=(self.table, self.pos) if self.epilogue else None,
-                       workspace=self.ws)
+                       workspace=self.ws, window=fused)
 
     def run(self):
-        self.window()
+        if not FUSED_WINDOW:
+            self.window()
         self.attend()
 
 
@@ -133,7 +143,8 @@ def make_sets(w: W.Workload, kv_format: str, touched_bytes: int, dev, epilogue: 
     sp0 = None if w.win_start_pos is None else w.win_start_pos.to(dev)
     table = sa.rope_table(w.rd, w.max_pos, w.rope_base, dev)
     probe = sa.make_args(q0, kv0, sink, idx0, w.scale, torch.empty_like(q0), kv_scale=scales0,
-                         rope=(table, pos0))
+                         rope=(table, pos0),
+                         window=(w.window, "chunk" if w.win_start_pos is None else "ring", pos0) if FUSED_WINDOW else None)
     ws_bytes = sa.sparse_attn_workspace_bytes(probe)
     nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / max(touched_bytes, 1))))
     sets = []
@@ -420,6 +431,7 @@ def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool
         "config": {"workload": w.name, "sequences": w.b, "queries_per_sequence": w.s, "heads": w.h,
                    "head_dim": w.d, "rope_dim": w.rd, "topk": w.topk, "kv_rows_per_sequence": w.kv_rows,
                    "kv_storage": kv, "epilogue": "inverse RoPE" if epilogue else "none",
+                   "window_lists": "generated inside sparse_attn" if FUSED_WINDOW else "sa_window_topk_idxs",
                    "kv_bytes_per_step": alg["kv_bytes"], "distinct_kv_rows": alg["distinct_rows"],
                    "valid_pairs": alg["valid_pairs"]},
         "roofline": roof,
@@ -708,6 +720,9 @@ def main():
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="storage of a single --workload (the default run times both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--explicit-window", action="store_true",
+                    help="run sa_window_topk_idxs before sparse_attn in every step instead of "
+                         "generating the window lists inside sparse_attn")
     ap.add_argument("--no-epilogue", action="store_true",
                     help="time sparse_attn without the inverse-RoPE epilogue (plain bf16 output)")
     ap.add_argument("--profile-calls", type=int, default=0,
@@ -733,6 +748,8 @@ def main():
     torch.cuda.set_device(dev)
     sa.lib()
     epilogue = not args.no_epilogue
+    global FUSED_WINDOW
+    FUSED_WINDOW = not args.explicit_window
 
     if args.profile_calls:
         if args.workload == "all":

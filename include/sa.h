@@ -30,7 +30,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 /* status codes */
 enum {
@@ -108,7 +108,24 @@ typedef struct sa_attn_args {
     int32_t *err_word;                                   /* device int32, with
                                                             SA_FLAG_CHECK_IDX only; the caller
                                                             clears it beforehand */
+
+    /* optional fused window lists: with window > 0 the first `win` columns of every index
+       list are the window lists of sa_window_topk_idxs (attention API docs,
+       "window_topk_idxs" and the ring-cache paragraph), generated inside the kernel from
+       the query's position p = pos[n][t] instead of read from idx (whose first `win`
+       columns are then never read; the caller need not fill them):
+         SA_WINDOW_RING:  the decode list of a ring of `window` slots at position p, oldest
+                          first: (p + 1 + j) mod window when p >= window - 1, else j for
+                          j <= p and -1 beyond (a negative p lists nothing); win = window;
+         SA_WINDOW_CHUNK: the prefill list into the chunk itself for the query at p: rows
+                          max(0, p - window + 1) + j while <= p, then -1;
+                          win = min(s, window).
+       win <= topk; pos is then required (also without the epilogue). window = 0: off. */
+    int32_t window;
+    int32_t window_mode;                                 /* SA_WINDOW_RING or SA_WINDOW_CHUNK */
 } sa_attn_args;
+
+enum { SA_WINDOW_RING = 1, SA_WINDOW_CHUNK = 2 };
 
 /* sparse_attn: out[n][t][hh][:] for every sequence n, query t and head hh, as described at
  * the top of this file, followed by the optional inverse-RoPE epilogue. Queries whose

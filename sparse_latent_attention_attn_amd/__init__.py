@@ -26,6 +26,7 @@ SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_HIP, SA_ERR_WORKSPACE, SA_ERR_
 NOALLOC_SCRATCH_BYTES = 64 << 20
 KV_BF16, KV_FP8 = 0, 1
 FLAG_CHECK_IDX = 1
+WINDOW_RING, WINDOW_CHUNK = 1, 2
 
 
 class SaError(RuntimeError):
@@ -53,6 +54,7 @@ class AttnArgs(C.Structure):
         ("pos", C.c_void_p), ("pos_seq_stride", C.c_int64),
         ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
         ("flags", C.c_uint32), ("err_word", C.c_void_p),
+        ("window", C.c_int32), ("window_mode", C.c_int32),
     ]
 
 
@@ -145,7 +147,7 @@ def lib():
         L.sa_kv_write.argtypes = [C.POINTER(KvWriteArgs), P]
         L.sa_quant_kv_fp8.restype = C.c_int
         L.sa_quant_kv_fp8.argtypes = [P, I64, I32, P, P, P, P]
-        if L.sa_abi_version() != 1:
+        if L.sa_abi_version() != 2:
             raise RuntimeError("libsa.so ABI version mismatch")
         _lib = L
     return _lib
@@ -184,10 +186,12 @@ def _seq_major(t, name, inner_ndim):
 
 
 def make_args(q, kv, sink, idx, scale, out, *, kv_scale=None, rope=None, workspace=None,
-              err_word=None, check_idx=False) -> AttnArgs:
+              err_word=None, check_idx=False, window=None) -> AttnArgs:
     """Build sa_attn_args from tensors. q [b][s][h][d] bf16, kv [b][R][d] bf16 or uint8
     (fp8 codes, with kv_scale uint8 [b][R][d/32]), sink f32 [h], idx int32 [b][s][topk],
-    out like q. rope = (cos_sin f32 [max_pos][rd/2][2], pos int32 [b][s]) or None."""
+    out like q. rope = (cos_sin f32 [max_pos][rd/2][2], pos int32 [b][s]) or None.
+    window = (W, "ring" | "chunk", pos int32 [b][s]) fuses the window lists: the first
+    W (ring) or min(s, W) (chunk) columns are generated from the positions."""
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
     _need(out, torch.bfloat16, "out", dev)
@@ -236,6 +240,15 @@ def make_args(q, kv, sink, idx, scale, out, *, kv_scale=None, rope=None, workspa
             raise ValueError("check_idx needs err_word")
         _need(err_word, torch.int32, "err_word", dev)
         a.flags, a.err_word = FLAG_CHECK_IDX, _ptr(err_word)
+    if window is not None:
+        wn, mode, wpos = window
+        _need(wpos, torch.int32, "window pos", dev)
+        if wpos.shape != (b, s):
+            raise ValueError("window positions must be [b][s]")
+        if rope is not None and wpos.data_ptr() != rope[1].data_ptr():
+            raise ValueError("the fused window lists and the epilogue read the same positions")
+        a.window, a.window_mode = wn, {"ring": WINDOW_RING, "chunk": WINDOW_CHUNK}[mode]
+        a.pos, a.pos_seq_stride = _ptr(wpos), _seq_major(wpos, "pos", 1)
     return a
 
 
@@ -246,13 +259,14 @@ def sparse_attn_workspace_bytes(args: AttnArgs) -> int:
 
 
 def sparse_attn(q, kv, sink, idx, scale, *, out=None, kv_scale=None, rope=None,
-                workspace=None, err_word=None, check_idx=False):
+                workspace=None, err_word=None, check_idx=False, window=None):
     """sparse_attn on the GPU (see include/sa.h). Returns out (bf16, like q). A workspace
-    is allocated with torch when none is given and the plan needs one."""
+    is allocated with torch when none is given and the plan needs one. window: see
+    make_args."""
     if out is None:
         out = torch.empty_like(q)
     a = make_args(q, kv, sink, idx, scale, out, kv_scale=kv_scale, rope=rope,
-                  err_word=err_word, check_idx=check_idx)
+                  err_word=err_word, check_idx=check_idx, window=window)
     need = sparse_attn_workspace_bytes(a)
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:

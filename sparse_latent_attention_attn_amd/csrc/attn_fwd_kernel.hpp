@@ -344,7 +344,7 @@ __device__ __forceinline__ u32x2 epilogue4(float a0, float a1, float a2, float a
 // for all of them), which would hold back every load issued after that wait by one memory
 // round trip.
 __device__ __forceinline__ int rope_pos(const KParams& p, int seq, int t) {
-    if (p.rope_dim == 0) return 0;
+    if (p.rope_dim == 0 && p.window == 0) return 0;
     int zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
     return p.pos[(int64_t)seq * p.pos_seq_stride + t + zero];
@@ -360,6 +360,26 @@ __device__ __forceinline__ const float* rope_ptr(const KParams& p, int pos, bool
 __device__ __forceinline__ const float* rope_row(const KParams& p, int seq, int t, bool report) {
     return rope_ptr(p, rope_pos(p, seq, t), report);
 }
+
+// The fused window list of a query at position pos (the window_topk_idxs lists): ring
+// (decode): the slots of a ring of `window` rows oldest first; chunk (prefill from 0): the
+// chunk rows max(0, pos - window + 1) .. pos; -1 where the list holds nothing. The one
+// division is done once per query (`first`: the slot of the oldest token of a full ring, or
+// the chunk's first row); an entry is then an add and a compare.
+struct WindowList {
+    int pos, window, first;
+    bool full;
+    __device__ __forceinline__ WindowList(const KParams& p, int pos_) : pos(pos_), window(p.window) {
+        const bool ring = p.window_mode == 1;
+        full = ring && pos >= window - 1;
+        first = ring ? (full ? (pos + 1) % window : 0) : max(0, pos - window + 1);
+    }
+    // entry j; a negative position lists nothing (first + j > pos)
+    __device__ __forceinline__ int operator()(int j) const {
+        const int v = first + j;
+        return full ? (v >= window ? v - window : v) : (v <= pos ? v : -1);
+    }
+};
 
 // Work item of block b (items are query-major: item = query * per_q + j). Workgroups are
 // dealt to the 8 XCDs round-robin: block b runs on XCD b % 8, as the (b / 8)-th workgroup
@@ -499,9 +519,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     int err = 0;
     int last = -1;
     int stage_v[kStageUnroll];
-    if (ncols > 0) {
+    // with fused window lists, columns below win_cols are generated from the position and
+    // idx is read only from there on (its loads are clamped to that range)
+    const int gen_end = min(ncols, max(0, p.win_cols - col_begin));      // generated columns
+    const bool any_loaded = gen_end < ncols;
+    if (any_loaded) {
 #pragma unroll
-        for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[min(tid + u * NW * kWave, ncols - 1)];
+        for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[max(gen_end, min(tid + u * NW * kWave, ncols - 1))];
+    } else {
+#pragma unroll
+        for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = -1;
     }
     // Q as the B operand of the 16x16x32 product: lane holds head l16 of each block,
     // d = 32*kk + 8*qc + 0..7. Padding heads (past h) repeat the last head: they are never
@@ -517,18 +544,30 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         sink_raw[hb] = p.sink[hq];
     }
     for (int c0 = 0; c0 < ncols_pad; c0 += kStageUnroll * NW * kWave) {
-        if (c0 > 0) {
+        if (c0 > 0 && any_loaded) {
 #pragma unroll
-            for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[min(c0 + tid + u * NW * kWave, ncols - 1)];
+            for (int u = 0; u < kStageUnroll; ++u) stage_v[u] = cols[max(gen_end, min(c0 + tid + u * NW * kWave, ncols - 1))];
         }
 #pragma unroll
         for (int u = 0; u < kStageUnroll; ++u) {
             const int c = c0 + tid + u * NW * kWave;
-            int row = c < ncols ? stage_v[u] : -1;
+            int row = c < ncols && c >= gen_end ? stage_v[u] : -1;
             if (row >= p.kv_rows) { err = 1; row = -1; }
             row = row < 0 ? -1 : row;
-            if (c < ncols_pad) istage[c] = row;
+            if (c < ncols_pad && c >= gen_end) istage[c] = row;
             if (row >= 0) last = c;
+        }
+    }
+    if (gen_end > 0) {
+        // the fused window columns, generated from the position (a short loop of its own, so
+        // that the unrolled staging above stays as compact as without them)
+        const WindowList win_list(p, pos);
+#pragma unroll 1
+        for (int c = tid; c < gen_end; c += NW * kWave) {
+            int row = win_list(col_begin + c);
+            if (row >= p.kv_rows) { err = 1; row = -1; }
+            istage[c] = row;
+            if (row >= 0) last = max(last, c);
         }
     }
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));

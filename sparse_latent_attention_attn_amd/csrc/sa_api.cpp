@@ -57,6 +57,13 @@ int check_shape(const sa_attn_args* a) {
     if (a->q_seq_stride % 8 || a->out_seq_stride % 8) return SA_ERR_INVALID;
     if (a->kv_format == SA_KV_BF16 ? (a->kv_seq_stride % 8) : (a->kv_seq_stride % 16)) return SA_ERR_INVALID;
     if (!std::isfinite(a->scale)) return SA_ERR_INVALID;
+    if (a->window < 0) return SA_ERR_INVALID;
+    if (a->window > 0) {
+        if (a->window_mode != SA_WINDOW_RING && a->window_mode != SA_WINDOW_CHUNK) return SA_ERR_INVALID;
+        const int64_t win = a->window_mode == SA_WINDOW_RING ? a->window : std::min<int64_t>(a->s, a->window);
+        if (win > a->topk) return SA_ERR_INVALID;
+        if (a->b > 1 && a->pos_seq_stride < a->s) return SA_ERR_INVALID;
+    }
     // one sequence's kv rows are addressed with 32-bit byte offsets
     const int64_t row_bytes = a->kv_format == SA_KV_BF16 ? 2 * (int64_t)a->d : a->d;
     if ((int64_t)a->kv_rows * row_bytes > INT32_MAX) return SA_ERR_UNSUPPORTED;
@@ -73,6 +80,7 @@ int check_pointers(const sa_attn_args* a) {
         if (!a->rope_cos_sin || !a->pos || a->max_pos < 1 || !aligned(a->rope_cos_sin, 8)) return SA_ERR_INVALID;
     }
     if ((a->flags & SA_FLAG_CHECK_IDX) && !a->err_word) return SA_ERR_INVALID;
+    if (a->window > 0 && (!a->pos || !aligned(a->pos, 4))) return SA_ERR_INVALID;
     return SA_OK;
 }
 
@@ -213,6 +221,11 @@ int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParam
         p.ws_ml = p.ws_o + slots * a->d;
     }
     p.flags = a->flags; p.err_word = a->err_word;
+    if (a->window > 0) {
+        p.window = a->window;
+        p.window_mode = a->window_mode;
+        p.win_cols = a->window_mode == SA_WINDOW_RING ? a->window : std::min(a->s, a->window);
+    }
     return SA_OK;
 }
 

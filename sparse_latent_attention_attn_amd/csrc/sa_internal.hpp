@@ -34,6 +34,7 @@ struct KParams {
     int32_t splits, cols_per_split, head_blocks, h_pad;
     uint32_t flags;
     int32_t* err_word;
+    int32_t window, window_mode, win_cols;                  // fused window lists (0: off)
 };
 
 // One sa_kv_write launch (pointers already offset to element 0; strides in elements of the

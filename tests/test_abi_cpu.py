@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(sa):
     L = sa.lib()
     for n in _declared_functions():
         assert hasattr(L, n), n
-    assert L.sa_abi_version() == 1
+    assert L.sa_abi_version() == 2
     assert L.sa_status_string(0) == b"ok"
     assert b"invalid" in L.sa_status_string(-1)
 
@@ -177,3 +177,11 @@ def test_grouped_proj_validation(sa):
                    ({"kg": 96, "o_stride": 192}, -2), ({"o": 0x10008}, -1)):
         assert L.sa_grouped_proj(C.byref(args(**kw)), None) == st, kw
     assert L.sa_grouped_proj(None, None) == -1
+
+
+def test_fused_window_validation(sa):
+    for kw in ({"window": -1}, {"window": 8, "window_mode": 3}, {"window": 8, "window_mode": 1},
+               {"window": 9, "window_mode": 1, "pos": 0x10000}, {"window": 4, "window_mode": 1, "pos": 0x10002}):
+        # topk is 8: a ring of 9 slots does not fit, and a window needs 4-byte aligned positions
+        a = _args(sa, **kw)
+        assert sa.lib().sa_sparse_attn(C.byref(a), None) == -1, kw

@@ -641,3 +641,61 @@ def test_fp8_storage_other_head_dims(sa, seed, b, s, h, d, rows, topk, hole, dup
     core = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
     ref = oracle.apply_rotary(core, rd, oracle.freqs_cis(rd, 3000, 10000.0), pos.view(-1).numpy(), inverse=True)
     assert_close(u16(out).reshape(-1, h, d), ref, f"fp8 d={d}")
+
+
+# ------------------------------------------------------------------ fused window lists
+def _fused_case(w, fmt):
+    """(explicit output, fused output, idx with the window columns poisoned)."""
+    import sparse_latent_attention_attn_amd as sa
+    q, kv, kv_scale, sink, idx = gpu_inputs(w, fmt)
+    pos = w.pos.cuda()
+    table = sa.rope_table(w.rd, w.max_pos, w.rope_base, "cuda")
+    ref = sa.sparse_attn(q, kv, sink, idx, w.scale, kv_scale=kv_scale, rope=(table, pos))
+    poisoned = idx.clone()
+    poisoned[..., :w.win_cols] = 10 ** 9                   # never read in the fused mode
+    mode = "chunk" if w.win_start_pos is None else "ring"
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = sa.sparse_attn(q, kv, sink, poisoned, w.scale, kv_scale=kv_scale, rope=(table, pos),
+                         window=(w.window, mode, pos), err_word=err, check_idx=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "a window column was read from idx"
+    return ref, got
+
+
+@pytest.mark.parametrize("name", ["decode_window", "prefill_window", "decode_compress", "prefill_compress"])
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_fused_window_lists_equal_explicit_lists(sa, name, size):
+    """The window lists generated inside sparse_attn from the positions (ring lists for the
+    decode workloads and the long prefill's per-query lists, chunk lists for the window-only
+    prefill) give the same output, bit for bit, as the lists of sa_window_topk_idxs."""
+    _say("fused window", name, size)
+    w = W.small_variant(name) if size == "small" else W.make(name)
+    for fmt in (("bf16", "fp8") if size == "small" else ("bf16",)):
+        ref, got = _fused_case(w, fmt)
+        assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), f"{name} {fmt}"
+
+
+def test_fused_window_across_splits_and_against_oracle(sa):
+    """A 300-slot ring list inside 4500-column lists (split plans: the generated columns run
+    into the second split), d = 256, and a chunk list at d = 64, against the oracle."""
+    for d, window, mode, topk, rows in ((256, 300, "ring", 4500, 6000), (64, 40, "chunk", 40, 90)):
+        _say("fused window splits", d, window, mode)
+        b, s, h = (2, 1, 32) if mode == "ring" else (1, 90, 16)
+        q, kv, sink, idx = W.rand_problem(140 + d, b, s, h, d, rows, topk, 0.05, False)
+        if mode == "ring":
+            pos = torch.tensor([[70000], [123]], dtype=torch.int32)
+            win = oracle.window_topk_idxs(window, 1, pos.view(-1).numpy())
+        else:
+            pos = torch.arange(s, dtype=torch.int32).view(1, s)
+            win = oracle.window_topk_idxs(window, s)
+        ncol = win.shape[-1]
+        full = idx.clone()
+        full[..., :ncol] = torch.from_numpy(win.reshape(b, s, ncol))
+        rd = d // 4
+        table = sa.rope_table(rd, 70001, 10000.0, "cuda")
+        posd = pos.cuda()
+        out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), float(np.float32(d ** -0.5)),
+                             rope=(table, posd), window=(window, mode, posd))
+        core = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), full.numpy(), float(np.float32(d ** -0.5)))
+        ref = oracle.apply_rotary(core, rd, oracle.freqs_cis(rd, 70001, 10000.0), pos.view(-1).numpy(), inverse=True)
+        assert_close(u16(out).reshape(-1, h, d), ref, f"fused {mode}")
