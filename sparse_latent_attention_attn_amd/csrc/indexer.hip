@@ -125,43 +125,72 @@ __device__ __forceinline__ uint32_t score_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix count of `bit` over the workgroup's threads in thread order, and the
-// total; `tot` is 4 words of LDS. Contains one barrier before the totals are read and one
-// after, so consecutive calls can reuse `tot`.
-__device__ __forceinline__ int block_excl_count(bool bit, SA_LDS int* tot, int& total) {
+// Exclusive prefix sum of v over the workgroup's threads in thread order, and the total
+// (NT threads); `tot` holds NT / 64 words of LDS. One barrier before the totals are read and
+// one after, so consecutive calls can reuse `tot`.
+template <int NT>
+__device__ __forceinline__ int block_excl_sum(int v, SA_LDS int* tot, int& total) {
+    constexpr int NWV = NT / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const uint64_t m = __ballot(bit);
-    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-    if (lane == 0) tot[wid] = __builtin_popcountll(m);
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        incl += lane >= o ? u : 0;
+    }
+    if (lane == 63) tot[wid] = incl;
     __syncthreads();
     int before = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
         const int c = tot[w];
         before += w < wid ? c : 0;
         total += c;
     }
     __syncthreads();
-    return before + below;
+    return before + incl - v;
 }
 
-// The keep flags of the k largest keys among keys[0 .. n) in LDS (k >= 1, at most the number
-// of non-zero keys): keys greater than the k-th largest, and as many keys equal to it as are
-// still needed, the lowest positions first. Writes the threshold key and that number of ties.
-// 256 threads; hist: 256 words of LDS; misc: 8 words.
+// The k-th largest key among keys[0 .. n) in LDS (k >= 1, at most the number of non-zero
+// keys) by a 4-pass radix select (8 bits per pass, most significant first), and how many
+// keys equal to it are among the k largest (the rest of the k are greater). NT threads;
+// hist: 256 words of LDS; misc: 8 words.
+template <int NT>
 __device__ void radix_threshold(SA_LDS const uint32_t* keys, int n, int k, SA_LDS uint32_t* hist,
                                 SA_LDS int* misc, uint32_t& thr, int& ties) {
     const int tid = threadIdx.x, lane = tid & 63;
     uint32_t prefix = 0, mask = 0;
     int rem = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;
+        for (int i = tid; i < 256; i += NT) hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += 256) {
-            const uint32_t u = keys[i];
-            if ((u & mask) == prefix)
-                __hip_atomic_fetch_add(&hist[(u >> shift) & 255u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (shift == 24 && NT <= 256) {
+            // the first digit (sign and high exponent bits) takes few values, so same-address
+            // atomics would serialise: equal digits of a wave are counted first and added once
+            // (measured on the 256-thread lists of the long prefill; the 1024-thread ones of
+            // decode ran faster with plain atomics)
+            for (int i0 = 0; i0 < n; i0 += NT) {
+                const int i = i0 + tid;
+                const bool act = i < n;
+                const uint32_t dig = act ? keys[i] >> 24 : 0u;
+                uint64_t todo = __ballot(act);
+                while (todo) {
+                    const int leader = __builtin_ctzll(todo);
+                    const uint32_t d = __shfl(dig, leader, 64);
+                    const uint64_t same = __ballot(act && dig == d);
+                    if (lane == leader)
+                        __hip_atomic_fetch_add(&hist[d], (uint32_t)__builtin_popcountll(same), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                    todo &= ~same;
+                }
+            }
+        } else {
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t u = keys[i];
+                if ((u & mask) == prefix)
+                    __hip_atomic_fetch_add(&hist[(u >> shift) & 255u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
         __syncthreads();
         if (tid < 64) {
@@ -200,54 +229,88 @@ __device__ void radix_threshold(SA_LDS const uint32_t* keys, int n, int k, SA_LD
     ties = rem;
 }
 
+// keys[i] = score_key(src[i]) for i < n, with 8 loads in flight per thread (a loop of single
+// loads would wait one memory round trip per iteration).
+template <int NT>
+__device__ __forceinline__ void load_keys(const float* src, int n, SA_LDS uint32_t* keys) {
+    for (int i0 = 0; i0 < n; i0 += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT + (int)threadIdx.x;
+            v[u] = i < n ? src[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT + (int)threadIdx.x;
+            if (i < n) keys[i] = score_key(v[u]);
+        }
+    }
+}
+
 // Number of non-zero keys among keys[0 .. n) (the selectable ones), in every thread.
+template <int NT>
 __device__ __forceinline__ int count_selectable(SA_LDS const uint32_t* keys, int n, SA_LDS int* tot) {
     int c = 0;
-    for (int i = threadIdx.x; i < n; i += 256) c += keys[i] != 0u;
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-    if ((threadIdx.x & 63) == 0) tot[threadIdx.x >> 6] = c;
-    __syncthreads();
-    const int total = tot[0] + tot[1] + tot[2] + tot[3];
-    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NT) c += keys[i] != 0u;
+    int total;
+    block_excl_sum<NT>(c, tot, total);
     return total;
+}
+
+// The ordered selection: every thread owns the run of `per` consecutive entries
+// [tid * per, ...); among equal keys at the threshold the lowest positions are taken first.
+// Calls take(i, rank) for every selected entry i with its rank among the selected (in
+// position order). Two block scans in all.
+template <int NT, typename Take>
+__device__ __forceinline__ void select_in_order(SA_LDS const uint32_t* keys, int n, uint32_t thr, int ties,
+                                                SA_LDS int* tot, Take take) {
+    const int per = (n + NT - 1) / NT;
+    const int i0 = min(n, (int)threadIdx.x * per), i1 = min(n, i0 + per);
+    int eq = 0;
+    for (int i = i0; i < i1; ++i) eq += keys[i] == thr;
+    int eq_total;
+    int tie_rank = block_excl_sum<NT>(eq, tot, eq_total);
+    int cnt = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t u = keys[i];
+        if (u > thr || (u == thr && tie_rank++ < ties)) ++cnt;
+    }
+    int cnt_total;
+    int rank = block_excl_sum<NT>(cnt, tot, cnt_total);
+    tie_rank -= eq;                                              // back to this run's first tie
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t u = keys[i];
+        if (u > thr || (u == thr && tie_rank++ < ties)) take(i, rank++);
+    }
 }
 
 // ------------------------------------------------------------------ top-k lists
 // One workgroup per query: the query's scores become keys in LDS; the k-th largest is found
 // by a 4-pass radix select; one ordered pass then lists the chosen positions in ascending
 // order (which is also the order the page re-sorts them into), shifted by the offset.
-__global__ __launch_bounds__(256) void index_topk_kernel(const IdxParams p) {
+// NT threads: 256 for short lists, 1024 for long ones.
+template <int NT>
+__global__ __launch_bounds__(NT) void index_topk_kernel(const IdxParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint32_t* hist = (SA_LDS uint32_t*)smem_raw;          // 256
-    SA_LDS int* misc = (SA_LDS int*)(hist + 256);                // 8
-    SA_LDS uint32_t* keys = (SA_LDS uint32_t*)(misc + 8);        // n_pos
+    SA_LDS int* misc = (SA_LDS int*)(hist + 256);                // 16
+    SA_LDS uint32_t* keys = (SA_LDS uint32_t*)(misc + 16);       // n_pos
     const int tid = threadIdx.x;
     const int64_t qi = blockIdx.x;
     const int n = (int)(qi / p.s), t = (int)(qi % p.s);
     const float* sc = p.scores + (int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos;
-    for (int i = tid; i < p.n_pos; i += 256) keys[i] = score_key(sc[i]);
+    load_keys<NT>(sc, p.n_pos, keys);
     __syncthreads();
     int32_t* out = p.idx + (int64_t)n * p.idx_seq_stride + (int64_t)t * p.idx_row_stride;
-    const int k = min(p.topk, count_selectable(keys, p.n_pos, misc));
-    int listed = 0;
+    const int k = min(p.topk, count_selectable<NT>(keys, p.n_pos, misc));
     if (k > 0) {
         uint32_t thr;
         int ties;
-        radix_threshold(keys, p.n_pos, k, hist, misc, thr, ties);
-        int tie_base = 0;
-        for (int c = 0; c < p.n_pos; c += 256) {
-            const int i = c + tid;
-            const uint32_t u = i < p.n_pos ? keys[i] : 0u;
-            int eq_total, fl_total;
-            const int tie_rank = tie_base + block_excl_count(u == thr, misc, eq_total);
-            const bool take = u > thr || (u == thr && tie_rank < ties);
-            const int slot = listed + block_excl_count(take, misc, fl_total);
-            if (take) out[slot] = i + p.offset;
-            tie_base += eq_total;
-            listed += fl_total;
-        }
+        radix_threshold<NT>(keys, p.n_pos, k, hist, misc, thr, ties);
+        select_in_order<NT>(keys, p.n_pos, thr, ties, misc, [&](int i, int r) { out[r] = i + p.offset; });
     }
-    for (int j = listed + tid; j < p.topk; j += 256) out[j] = -1;
+    for (int j = k + tid; j < p.topk; j += NT) out[j] = -1;
 }
 
 // ------------------------------------------------------------------ candidate blocks
@@ -256,10 +319,12 @@ __global__ __launch_bounds__(256) void index_topk_kernel(const IdxParams p) {
 // division, pinned to +inf, the min(topk_blocks, blocks) best blocks kept when above -inf
 // (ties: the lower block first), each block's flag repeated over its positions.
 __global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams p) {
+    constexpr int NT = 256;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint32_t* hist = (SA_LDS uint32_t*)smem_raw;
     SA_LDS int* misc = (SA_LDS int*)(hist + 256);
-    SA_LDS uint32_t* keys = (SA_LDS uint32_t*)(misc + 8);        // one per block
+    SA_LDS uint32_t* keys = (SA_LDS uint32_t*)(misc + 16);       // one per block
+    SA_LDS uint8_t* keep = (SA_LDS uint8_t*)(keys + ((p.n_pos + p.block_size - 1) / p.block_size));
     const int tid = threadIdx.x;
     const int64_t qi = blockIdx.x;
     const int n = (int)(qi / p.s), t = (int)(qi % p.s);
@@ -268,31 +333,41 @@ __global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams 
     const int pos = p.pos[(int64_t)n * p.pos_seq_stride + t];
     const int64_t len = pos < 0 ? 0 : ((int64_t)pos + 1) / p.ratio;
     const int64_t last = len > 0 ? (len - 1) / p.block_size : -1;
-    for (int j = tid; j < nblk; j += 256) {
-        float m = -INFINITY;
-        const int t0 = j * p.block_size, t1 = min(p.n_pos, t0 + p.block_size);
-        for (int u = t0; u < t1; ++u) m = fmaxf(m, lg[u]);
-        keys[j] = score_key(j == last ? INFINITY : m);
+    // block maxima as the maxima of the order-preserving keys (-inf padding is key 0), with
+    // 8 logit loads in flight per thread
+    for (int j = tid; j < nblk; j += NT) {
+        keys[j] = 0u;
+        keep[j] = 0;
     }
     __syncthreads();
-    const int k = min(p.topk_blocks, count_selectable(keys, nblk, misc));
-    uint32_t thr = 0xffffffffu;
-    int ties = 0;
-    if (k > 0) radix_threshold(keys, nblk, k, hist, misc, thr, ties);
-    // the keep flags replace the keys (each thread rewrites only the entries it read)
-    int tie_base = 0;
-    for (int c = 0; c < nblk; c += 256) {
-        const int j = c + tid;
-        const uint32_t u = j < nblk ? keys[j] : 0u;
-        int eq_total;
-        const int tie_rank = tie_base + block_excl_count(k > 0 && u == thr, misc, eq_total);
-        const bool keep = k > 0 && (u > thr || (u == thr && tie_rank < ties));
-        if (j < nblk) keys[j] = keep ? 1u : 0u;
-        tie_base += eq_total;
+    for (int i0 = 0; i0 < p.n_pos; i0 += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT + tid;
+            v[u] = i < p.n_pos ? lg[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * NT + tid;
+            const uint32_t key = score_key(v[u]);
+            if (i < p.n_pos && key != 0u)
+                __hip_atomic_fetch_max(&keys[i / p.block_size], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+    __syncthreads();
+    if (tid == 0 && last >= 0 && last < nblk) keys[last] = score_key(INFINITY);
+    __syncthreads();
+    const int k = min(p.topk_blocks, count_selectable<NT>(keys, nblk, misc));
+    if (k > 0) {
+        uint32_t thr;
+        int ties;
+        radix_threshold<NT>(keys, nblk, k, hist, misc, thr, ties);
+        select_in_order<NT>(keys, nblk, thr, ties, misc, [&](int j, int) { keep[j] = 1; });
     }
     __syncthreads();
     uint8_t* mask = p.mask + (int64_t)n * p.mask_seq_stride + (int64_t)t * p.n_pos;
-    for (int u = tid; u < p.n_pos; u += 256) mask[u] = (uint8_t)keys[u / p.block_size];
+    for (int u = tid; u < p.n_pos; u += NT) mask[u] = keep[u / p.block_size];
 }
 
 // ------------------------------------------------------------------ launches
@@ -332,18 +407,22 @@ hipError_t launch_index_scores(const IdxParams& p, hipStream_t st) {
 }
 
 hipError_t launch_index_topk(const IdxParams& p, hipStream_t st) {
-    const size_t lds = (256 + 8) * 4 + (size_t)p.n_pos * 4;
+    const size_t lds = (256 + 16) * 4 + (size_t)p.n_pos * 4;
     const int64_t nq = (int64_t)p.b * p.s;
     if (lds > 160 * 1024 || nq > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute((const void*)index_topk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // long lists get four times the threads: the passes over the keys dominate there
+    const bool wide = p.n_pos > 4096;
+    const void* k = wide ? (const void*)index_topk_kernel<1024> : (const void*)index_topk_kernel<256>;
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_topk_kernel, dim3((unsigned)nq), dim3(256), lds, st, p);
+    if (wide) hipLaunchKernelGGL(index_topk_kernel<1024>, dim3((unsigned)nq), dim3(1024), lds, st, p);
+    else hipLaunchKernelGGL(index_topk_kernel<256>, dim3((unsigned)nq), dim3(256), lds, st, p);
     return hipGetLastError();
 }
 
 hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st) {
     const int nblk = (p.n_pos + p.block_size - 1) / p.block_size;
-    const size_t lds = (256 + 8) * 4 + (size_t)nblk * 4;
+    const size_t lds = (256 + 16) * 4 + (size_t)nblk * 5;
     const int64_t nq = (int64_t)p.b * p.s;
     if (lds > 160 * 1024 || nq > 0x7fffffff) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute((const void*)candidate_blocks_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

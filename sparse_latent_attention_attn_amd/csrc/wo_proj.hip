@@ -12,7 +12,8 @@
 //     64 staged in LDS (double-buffered, 16-byte chunks XOR-swizzled by row), 4 waves of
 //     64 x 128.
 //   * proj_skinny_kernel (decode, at most 64 tokens): the cost is streaming W once, so each
-//     workgroup takes 16 rows of W, its 4 waves split k four ways, and LDS sums the parts.
+//     workgroup takes 32 (or 16) rows of W, its 4 to 16 waves split k, and LDS sums the
+//     parts.
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -40,48 +41,103 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
 }
 
 // ------------------------------------------------------------------ skinny (decode)
-// Grid (r / 16, g, ceil(m / (16 MB))); wave w takes k in [w kg/4, (w+1) kg/4).
-template <bool FP8, int MB>
-__global__ __launch_bounds__(256) void proj_skinny_kernel(const ProjParams p) {
-    __shared__ f32x4 part[3][MB][64];
+// Grid (r / (16 NB)) * g workgroups of KW waves; wave w takes k in
+// [w kg/KW, (w+1) kg/KW) for NB blocks of 16 rows of W and MB blocks of 16 tokens, and LDS
+// sums the KW parts. Each token operand loaded feeds NB matrix instructions (every load
+// passes the texture unit at about 64 bytes per clock per CU, and the tokens are re-read
+// by every workgroup of their group), and the k range of a wave is short (4 rounds of 4
+// k-steps at kg = 8192): the loop is a chain of memory round trips, so more waves with
+// shorter chains keep more bytes in flight.
+template <bool FP8, int MB, int NB, int KW>
+__global__ __launch_bounds__(KW * 64) void proj_skinny_kernel(const ProjParams p) {
+    __shared__ f32x4 part[KW - 1][NB][MB][64];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int l16 = lane & 15, gq = lane >> 4;
-    const int n0 = blockIdx.x * 16, gg = blockIdx.y, m0 = blockIdx.z * 16 * MB;
-    const int kq = p.kg / 4, kbeg = wid * kq;
-    const int64_t wrow = ((int64_t)gg * p.r + n0 + l16) * p.kg;
+    // 1-D grid, group fastest: workgroups are dealt to the 8 XCDs round-robin, so with 8
+    // groups each XCD takes one group and its L2 keeps that group's tokens, which every
+    // workgroup of the group reads in full
+    const int gg = blockIdx.x % p.g, n0 = (blockIdx.x / p.g) * 16 * NB, m0 = blockIdx.y * 16 * MB;
+    const int kq = p.kg / KW, kbeg = wid * kq;
+    int64_t wrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wrow[nb] = ((int64_t)gg * p.r + n0 + 16 * nb + l16) * p.kg;
     const uint16_t* orow[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
         orow[mb] = p.o + (int64_t)min(m0 + 16 * mb + l16, p.m - 1) * p.o_stride + (int64_t)gg * p.kg + 8 * gq;
-    f32x4 acc[MB];
+    f32x4 acc[NB][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kbeg; k0 < kbeg + kq; k0 += 128) {           // kq is a multiple of 128
+        // fp8: the scale bytes of the round's four 32-blocks, one word per row
+        uint32_t sc4[NB];
+        if constexpr (FP8) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sc4[nb] = *(const uint32_t*)(p.ws + (wrow[nb] + k0) / 32);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int k = k0 + 32 * u;
-            const u32x4 a = load_w8<FP8>(p, wrow, k + 8 * gq);
-            u32x4 b[MB];
+            u32x4 a[NB], b[MB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                if constexpr (FP8) {
+                    const u32x2 c = *(const u32x2*)(p.wq + wrow[nb] + k + 8 * gq);
+                    const float sc = bits_f32(((sc4[nb] >> (8 * u)) & 0xffu) << 23);
+                    a[nb][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false));
+                    a[nb][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true));
+                    a[nb][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false));
+                    a[nb][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true));
+                } else {
+                    a[nb] = load_w8<false>(p, wrow[nb], k + 8 * gq);
+                }
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) b[mb] = *(const u32x4*)(orow[mb] + k);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma16(a, b[mb], acc[mb]);
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = mfma16(a[nb], b[mb], acc[nb][mb]);
         }
     }
     if (wid > 0) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) part[wid - 1][mb][lane] = acc[mb];
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) part[wid - 1][nb][mb][lane] = acc[nb][mb];
     }
     __syncthreads();
     if (wid > 0) return;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const f32x4 v = acc[mb] + part[0][mb][lane] + part[1][mb][lane] + part[2][mb][lane];
-        const int t = m0 + 16 * mb + l16;
-        if (t < p.m)
-            *(u32x2*)(p.out + (int64_t)t * p.out_stride + (int64_t)gg * p.r + n0 + 4 * gq) =
-                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    }
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4 v = acc[nb][mb];
+#pragma unroll
+            for (int w = 0; w < KW - 1; ++w) v += part[w][nb][mb][lane];
+            const int t = m0 + 16 * mb + l16;
+            if (t < p.m)
+                *(u32x2*)(p.out + (int64_t)t * p.out_stride + (int64_t)gg * p.r + n0 + 16 * nb + 4 * gq) =
+                    u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+}
+
+template <bool FP8, int NB, int KW>
+static void launch_skinny_mb(const ProjParams& p, hipStream_t st) {
+    const dim3 grid((p.r / (16 * NB)) * p.g, 1, 1), block(KW * 64);
+    if (p.m <= 16) hipLaunchKernelGGL((proj_skinny_kernel<FP8, 1, NB, KW>), grid, block, 0, st, p);
+    else if (p.m <= 32) hipLaunchKernelGGL((proj_skinny_kernel<FP8, 2, NB, KW>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((proj_skinny_kernel<FP8, 4, NB, KW>), grid, block, 0, st, p);
+}
+
+// k split over KW waves: as many as keep a wave's range at 512 or more (a multiple of 128)
+template <bool FP8, int NB>
+static void launch_skinny_nb(const ProjParams& p, hipStream_t st) {
+    if (p.kg % (16 * 512) == 0) launch_skinny_mb<FP8, NB, 16>(p, st);
+    else if (p.kg % (8 * 512) == 0) launch_skinny_mb<FP8, NB, 8>(p, st);
+    else launch_skinny_mb<FP8, NB, 4>(p, st);
 }
 
 // ------------------------------------------------------------------ tiled
@@ -173,10 +229,8 @@ __global__ __launch_bounds__(256) void proj_tiled_kernel(const ProjParams p) {
 template <bool FP8>
 static hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
     if (p.m <= 64 && p.r % 16 == 0 && p.kg % 512 == 0) {
-        const dim3 grid(p.r / 16, p.g, 1);
-        if (p.m <= 16) hipLaunchKernelGGL((proj_skinny_kernel<FP8, 1>), grid, dim3(256), 0, st, p);
-        else if (p.m <= 32) hipLaunchKernelGGL((proj_skinny_kernel<FP8, 2>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((proj_skinny_kernel<FP8, 4>), grid, dim3(256), 0, st, p);
+        if (p.r % 32 == 0) launch_skinny_nb<FP8, 2>(p, st);
+        else launch_skinny_nb<FP8, 1>(p, st);
         return hipGetLastError();
     }
     if (p.r % kProjN != 0 || p.kg % kProjK != 0) return hipErrorInvalidValue;
