@@ -115,6 +115,128 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
     }
 }
 
+// The same scores for many queries of one sequence (prefill): a workgroup of 4 waves takes
+// 8 consecutive queries (2 per wave) and walks their visible positions in tiles of 64 keys,
+// staged in LDS by contiguous 16-byte loads (8 cache lines per load instruction instead of
+// the 16 rows x 64 bytes of an operand-shaped load) and double-buffered; each wave reads its B
+// operands from LDS (rows XOR-swizzled in 16-byte chunks so that the 16 rows of an operand
+// read fall in distinct banks). Every staged key then feeds 8 queries x h heads.
+constexpr int kLdsQueries = 8, kLdsTile = 64;
+
+template <int D, int HB>
+__global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p) {
+    constexpr int KS = D / 32, CH = D / 8;                      // k-steps; 16-byte chunks per row
+    constexpr int kTileBytes = kLdsTile * D * 2;
+    constexpr int kPer = kTileBytes / 16 / 256;                 // staging loads per thread
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTileBytes];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int n = blockIdx.y;
+    const int t0 = blockIdx.x * kLdsQueries + 2 * wid;          // this wave's two queries
+    int vis[2];
+    int vmax_w = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        vis[j] = t0 + j < p.s ? visible_positions(p.pos[(int64_t)n * p.pos_seq_stride + t0 + j], p.ratio, p.n_pos) : 0;
+        vmax_w = max(vmax_w, vis[j]);
+    }
+    // the workgroup's extent: the maximum over its 8 queries (all waves walk the same tiles)
+    __shared__ int vmax_s[4];
+    if (lane == 0) vmax_s[wid] = vmax_w;
+    __syncthreads();
+    const int vmax = max(max(vmax_s[0], vmax_s[1]), max(vmax_s[2], vmax_s[3]));
+    const uint16_t* kseq = p.k + (int64_t)n * p.k_seq_stride;
+    u32x4 qa[2][HB][KS];
+    float wv[2][HB][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = min(t0 + j, p.s - 1);
+        const uint16_t* qq = p.q + (int64_t)n * p.q_seq_stride + (int64_t)t * p.h * D;
+        const float* ww = p.w + (int64_t)n * p.w_seq_stride + (int64_t)t * p.h;
+#pragma unroll
+        for (int mb = 0; mb < HB; ++mb) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                qa[j][mb][kk] = *(const u32x4*)(qq + (int64_t)(16 * mb + l16) * D + 32 * kk + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[j][mb][r] = ww[16 * mb + 4 * g + r];
+        }
+    }
+    // staging: load u of thread tid moves chunk (tid + 256 u) of the tile (row = chunk / CH)
+    u32x4 st[kPer];
+    auto fetch = [&](int tb) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int c = tid + 256 * u, row = c / CH;
+            const int pp = min(tb + row, p.n_pos - 1);
+            st[u] = *(const u32x4*)(kseq + (int64_t)pp * D + 8 * (c % CH));
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int c = tid + 256 * u, row = c / CH, ch = c % CH;
+            *(SA_LDS u32x4*)((SA_LDS uint8_t*)tiles[buf] + row * (D * 2) + ((ch ^ (row & (CH - 1) & 15)) << 4)) = st[u];
+        }
+    };
+    const int ntiles = (vmax + kLdsTile - 1) / kLdsTile;
+    const int nall = (p.n_pos + kLdsTile - 1) / kLdsTile;
+    if (ntiles > 0) {
+        fetch(0);
+        stage(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < nall; ++it) {
+        const int tb = it * kLdsTile;
+        if (it < ntiles) {
+            if (it + 1 < ntiles) fetch(tb + kLdsTile);
+            SA_LDS const uint8_t* tile = (SA_LDS const uint8_t*)tiles[it & 1];
+#pragma unroll
+            for (int nb = 0; nb < kLdsTile / 16; ++nb) {
+                const int row = 16 * nb + l16, pp = tb + row;
+                u32x4 kb[KS];
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk)
+                    kb[kk] = *(SA_LDS const u32x4*)(tile + row * (D * 2) + (((4 * kk + g) ^ (row & (CH - 1) & 15)) << 4));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x4 acc[HB];
+#pragma unroll
+                    for (int mb = 0; mb < HB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+                        for (int mb = 0; mb < HB; ++mb)
+                            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, qa[j][mb][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[mb], 0, 0, 0);
+                    float part = 0.0f;
+#pragma unroll
+                    for (int mb = 0; mb < HB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
+                    part = sum_xor32(sum_xor16(part));
+                    const int t = t0 + j;
+                    if (g == 0 && t < p.s && pp < p.n_pos) {
+                        bool keep = pp < vis[j];
+                        if (keep && p.cand) keep = p.cand[(int64_t)n * p.cand_seq_stride + (int64_t)t * p.n_pos + pp] != 0;
+                        p.scores[(int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos + pp] = keep ? part : -INFINITY;
+                    }
+                }
+            }
+            if (it + 1 < ntiles) stage((it + 1) & 1);
+            __syncthreads();
+        } else {
+            // beyond every query's visible positions: -inf, no keys needed
+            for (int j = 0; j < 2; ++j) {
+                const int t = t0 + j;
+                if (t >= p.s) continue;
+                float* row = p.scores + (int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos;
+                for (int u = lane; u < kLdsTile && tb + u < p.n_pos; u += 64) row[tb + u] = -INFINITY;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ radix select
 // Order-preserving 32-bit key of a score; -inf, NaN (and nothing else) map to 0, so only
 // finite scores (and +inf) are ever selected; -0 counts as +0.
@@ -373,6 +495,14 @@ __global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams 
 // ------------------------------------------------------------------ launches
 template <int D, int HB>
 static hipError_t launch_scores_hb(const IdxParams& p, hipStream_t st) {
+    if constexpr (HB * D <= 256) {
+        if (p.s >= kLdsQueries) {
+            const int64_t gx = (p.s + kLdsQueries - 1) / kLdsQueries;
+            if (gx > 0x7fffffff || p.b > 65535) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((index_scores_lds_kernel<D, HB>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
+            return hipGetLastError();
+        }
+    }
     constexpr int QPW = HB * D <= 256 ? 2 : 1;
     const int qpw = p.s > 1 ? QPW : 1;                      // decode: one query per sequence
     const int64_t waves = (int64_t)p.b * ((p.s + qpw - 1) / qpw);
