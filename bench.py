@@ -290,17 +290,41 @@ def cpu_baseline(w: W.Workload, alg, budget_s: float, rope: bool = True):
 
 # ------------------------------------------------------------------ HBM traffic counters
 CAL_BYTES = 1 << 30              # calibration copy: 1 GiB read, 1 GiB written
-KERNEL_SOURCES = ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "sa_api.cpp", "sa_internal.hpp", "sa_device.hpp"]
+# per family of workloads: the sources its kernels are built from, and the kernel names
+# (substrings) of one call
+FAMILY_SOURCES = {
+    "attn": ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "sa_api.cpp", "sa_internal.hpp",
+             "sa_device.hpp"],
+    "kv_write": ["aux_kernels.hip", "sa_device.hpp"],
+    "indexer": ["indexer.hip", "sa_device.hpp"],
+    "proj": ["wo_proj.hip", "sa_device.hpp"],
+}
+FAMILY_KERNELS = {
+    "attn": ["attn_fwd_kernel", "attn_combine_kernel"],
+    "kv_write": ["kv_write_kernel"],
+    "indexer": ["index_scores", "index_topk"],
+    "proj": ["proj_skinny_kernel", "proj_tiled_kernel"],
+}
 
 
-def kernel_source_hash() -> str:
+def family(workload: str) -> str:
+    if workload.startswith("kv_write"):
+        return "kv_write"
+    if workload.startswith("indexer"):
+        return "indexer"
+    if workload.startswith("wo_proj"):
+        return "proj"
+    return "attn"
+
+
+def kernel_source_hash(fam: str = "attn") -> str:
     """Hash of the kernel sources' code: line and block comments and whitespace are left
     out (the sources hold no comment markers inside string literals), so that an edit of a
     comment does not orphan counters taken on identical code."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in FAMILY_SOURCES[fam]:
         with open(os.path.join(ROOT, "sparse_latent_attention_attn_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -321,7 +345,7 @@ def stored_traffic(workload: str, kv: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    return rec["traffic_bytes_per_call"] if rec.get("kernel_source_sha") == kernel_source_hash() else None
+    return rec["traffic_bytes_per_call"] if rec.get("kernel_source_sha") == kernel_source_hash(family(workload)) else None
 
 
 def profile_pass(sets, calls: int, dev):
@@ -339,45 +363,98 @@ def profile_pass(sets, calls: int, dev):
 
 
 def pmc_summary(workload: str, kv: str, fetch_csv: str, write_csv: str):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each scaled
-    by the ratio of the known size of the calibration copy to what the counter read for it."""
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernels of one call, each
+    scaled by the ratio of the known size of the calibration copy to what the counter read
+    for it."""
     import csv
+    pats = FAMILY_KERNELS[family(workload)]
 
     def read(path, counter):
-        att, comb, cal = [], [], []
+        per = {p: [] for p in pats}
+        cal = []
         with open(path) as fh:
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] != counter:
                     continue
                 name, v = r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0
-                if "attn_fwd_kernel" in name:
-                    att.append(v)
-                elif "attn_combine_kernel" in name:
-                    comb.append(v)
+                hit = [p for p in pats if p in name]
+                if hit:
+                    per[hit[0]].append(v)
                 elif "copyBuffer" in name or "elementwise" in name:
                     cal.append(v)
-        if not att or not cal:
-            raise SystemExit(f"{path}: no {counter} rows for the attention or the copy kernel")
+        if not per[pats[0]] or not cal:
+            raise SystemExit(f"{path}: no {counter} rows for {pats[0]} or the copy kernel")
         # the calibration copies are the three largest copy dispatches (input-set clones
         # before them are far smaller)
         cal = sorted(cal)[-3:]
-        return float(np.mean(att)), (float(np.mean(comb)) if comb else 0.0), float(np.median(cal))
+        return {p: (float(np.mean(v)) if v else 0.0) for p, v in per.items()}, float(np.median(cal))
 
-    fa, fc, fcal = read(fetch_csv, "FETCH_SIZE")
-    wa, wc, wcal = read(write_csv, "WRITE_SIZE")
+    fk, fcal = read(fetch_csv, "FETCH_SIZE")
+    wk, wcal = read(write_csv, "WRITE_SIZE")
     kf, kw = CAL_BYTES / fcal, CAL_BYTES / wcal
     rec = {
-        "workload": workload, "kv": kv, "kernel_source_sha": kernel_source_hash(),
-        "fetch_bytes_raw": fa, "write_bytes_raw": wa,
-        "combine_fetch_bytes_raw": fc, "combine_write_bytes_raw": wc,
+        "workload": workload, "kv": kv, "kernel_source_sha": kernel_source_hash(family(workload)),
+        "fetch_bytes_raw": fk, "write_bytes_raw": wk,
         "copy_fetch_bytes_raw": fcal, "copy_write_bytes_raw": wcal, "copy_bytes": CAL_BYTES,
         "fetch_scale": kf, "write_scale": kw,
-        "traffic_bytes_per_call": (fa + fc) * kf + (wa + wc) * kw,
+        "traffic_bytes_per_call": sum(fk.values()) * kf + sum(wk.values()) * kw,
     }
     os.makedirs(os.path.dirname(traffic_path(workload, kv)), exist_ok=True)
     with open(traffic_path(workload, kv), "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))
+
+
+def trace_summary(stats_csv: str):
+    """The kernel table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv)."""
+    import csv
+    print(f"{'kernel':70s} {'calls':>7s} {'avg us':>10s} {'min us':>10s} {'max us':>10s}")
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            print(f"{r['Name'][:70]:70s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                  f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+
+
+def counter_summary(workload: str, csvs):
+    """Per-call averages of the counters of one family's kernels over rocprofv3 --pmc runs,
+    with derived ratios: L2 hit rate, mean L1-to-L2 read latency, texture-unit stall share,
+    wait shares, MFMA busy share."""
+    import csv
+    import collections
+    pats = FAMILY_KERNELS[family(workload)]
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in csvs:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                hit = [p for p in pats if p in r["Kernel_Name"]]
+                if hit:
+                    vals[r["Kernel_Name"][:80]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for kern, cs in vals.items():
+        print(kern)
+        avg = {c: float(np.mean(v)) for c, v in cs.items()}
+        for c in sorted(avg):
+            print(f"  {c:36s} {avg[c]:14.4g}   (calls {len(cs[c])})")
+
+        def ratio(a, b):
+            return avg[a] / avg[b] if a in avg and b in avg and avg[b] else None
+        derived = [
+            ("L2 hit rate, TCC_HIT / (TCC_HIT + TCC_MISS)",
+             avg["TCC_HIT"] / (avg["TCC_HIT"] + avg["TCC_MISS"]) if "TCC_HIT" in avg and "TCC_MISS" in avg else None),
+            ("mean L1->L2 read latency (clocks), TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ",
+             ratio("TCP_TCC_READ_REQ_LATENCY", "TCP_TCC_READ_REQ")),
+            ("texture unit stalled by the L1, TA_ADDR_STALLED_BY_TC_CYCLES / TA_TA_BUSY",
+             ratio("TA_ADDR_STALLED_BY_TC_CYCLES", "TA_TA_BUSY")),
+            ("LDS-DMA gather wavefronts per call, TA_BUFFER_READ_LDS_WAVEFRONTS",
+             avg.get("TA_BUFFER_READ_LDS_WAVEFRONTS")),
+            ("waves waiting to issue, SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES", ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("waves waiting on a counter, SQ_WAIT_ANY / SQ_WAVE_CYCLES", ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+            ("LDS bank-conflict share, SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS",
+             ratio("SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")),
+        ]
+        print("  derived:")
+        for name, v in derived:
+            if v is not None:
+                print(f"    {name}: {v:.4g}")
 
 
 def prepare(w: W.Workload, kv: str, dev, epilogue: bool):
@@ -506,7 +583,14 @@ KV_WRITE = {   # name: (sequences, rows per sequence, ring positions start)
 }
 
 
-def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool):
+def run_eager(fns, calls: int):
+    """Counter-collection mode: `calls` eager launches over the input sets."""
+    for i in range(calls):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+
+
+def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool, profile_calls: int = 0):
     """The KV write path (sa_kv_write): normalised rows -> forward RoPE -> fp8 round trip ->
     ring slot, bf16 storage, with the rows returned for the prefill. HBM-bound: bytes = rows
     read + positions + (cos, sin) rows + rows returned + rows stored."""
@@ -529,6 +613,9 @@ def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool):
         sets.append((x, pos, ring, rows))
     fns = [(lambda x=x, pos=pos, ring=ring, rows=rows:
             sa.kv_write(x, pos, ring, rope=table, window=window, rows_out=rows)) for x, pos, ring, rows in sets]
+    if profile_calls:
+        run_eager(fns, profile_calls)
+        return None
     ms_step = time_graph_steps(fns, steps, warmup)
     k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
     achieved = alg_bytes / (k_mean * 1e-3) / 1e9
@@ -538,7 +625,7 @@ def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool):
         "config": {"workload": name, "sequences": b, "rows_per_sequence": s, "head_dim": d,
                    "rope_dim": rd, "window": window, "kv_storage": "bf16", "rows_returned": want_rows},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "kv_write_kernel",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic(name, "bf16"), "kernel": "kv_write_kernel",
                      "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": None,
@@ -565,7 +652,7 @@ INDEXER = {   # name: (sequences, queries per sequence, compressed positions, qu
 }
 
 
-def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool):
+def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool, profile_calls: int = 0):
     """The indexer (sa_indexer_topk: MFMA scores, then the radix-select top-k lists) with 32
     index heads of 128, ratio 4, 512 picks, and select_candidate_blocks (sa_candidate_blocks,
     2048 blocks of 8) on its scores. Decode reads 4 MB of index keys per sequence and is
@@ -593,9 +680,13 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool):
                          mask=torch.empty(b, s, n_pos, dtype=torch.uint8, device=dev)))
     fns = [(lambda x=x: sa.indexer_topk(x["q"], x["k"], x["w"], x["pos"], ratio, topk=topk, offset=128,
                                         scores=x["sc"], idx=x["idx"])) for x in sets]
+    cand_fns = [(lambda x=x: sa.candidate_blocks(x["sc"], x["pos"], ratio, 2048, 8, mask=x["mask"])) for x in sets]
+    if profile_calls:
+        run_eager(fns, profile_calls)
+        run_eager(cand_fns, profile_calls)
+        return None
     ms_step = time_graph_steps(fns, steps, warmup)
     k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
-    cand_fns = [(lambda x=x: sa.candidate_blocks(x["sc"], x["pos"], ratio, 2048, 8, mask=x["mask"])) for x in sets]
     c_mean, _ = time_launches(cand_fns, calls=min(400, max(50, 5 * steps)))
     if kind == "decode":
         achieved = alg_bytes / (k_mean * 1e-3) / 1e9
@@ -607,7 +698,7 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool):
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
         value, unit, metric = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", "indexer TFLOP/s (prefill)"
-    roof.update({"traffic": None, "kernel": "sa_indexer_topk (index_scores_kernel + index_topk_kernel)",
+    roof.update({"traffic": stored_traffic(name, "bf16"), "kernel": "sa_indexer_topk (index_scores_kernel + index_topk_kernel)",
                  "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
                  "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops})
     cand_bytes = b * s * n_pos * 5
@@ -653,7 +744,7 @@ PROJ = {   # name: (tokens, weight storage)
 }
 
 
-def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool):
+def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool, profile_calls: int = 0):
     """The grouped output projection (sa_grouped_proj) at the model config's 8 groups of
     o_lora_rank 1024 on 128 heads of 512 (k 8192 per group). Decode streams the weights once
     (HBM-bound); the prefill is a dense bf16 contraction (MFMA-bound)."""
@@ -673,6 +764,9 @@ def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool):
     sets = [dict(o=o0.to(dev), w=wd if i == 0 else wd.clone(), ws=None if wsc is None else (wsc if i == 0 else wsc.clone()),
                  out=torch.empty(m, g, r, dtype=torch.bfloat16, device=dev)) for i in range(nsets)]
     fns = [(lambda x=x: sa.grouped_proj(x["o"], x["w"], w_scale=x["ws"], out=x["out"])) for x in sets]
+    if profile_calls:
+        run_eager(fns, profile_calls)
+        return None
     ms_step = time_graph_steps(fns, steps, warmup)
     k_mean, k_best = time_launches(fns, calls=min(400, max(20, 5 * steps)))
     if m <= 64:
@@ -685,7 +779,7 @@ def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool):
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
         value, unit, metric = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", "grouped wo_a TFLOP/s (prefill)"
-    roof.update({"traffic": None, "kernel": "proj_skinny_kernel" if m <= 64 else "proj_tiled_kernel",
+    roof.update({"traffic": stored_traffic(name, "bf16"), "kernel": "proj_skinny_kernel" if m <= 64 else "proj_tiled_kernel",
                  "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
                  "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops})
     rec = {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step, "steps": steps,
@@ -716,7 +810,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="all", choices=["all"] + sorted(W.WORKLOADS))
+    extra = list(KV_WRITE) + list(INDEXER) + list(PROJ)
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(W.WORKLOADS) + extra)
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="storage of a single --workload (the default run times both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -732,9 +827,20 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "--profile-calls into profiles/traffic_<workload>_<kv>.json")
+    ap.add_argument("--trace-summary", metavar="KERNEL_STATS_CSV",
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--counter-summary", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-call counter averages and derived ratios of --workload's "
+                         "kernels from rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.workload, args.counter_summary)
+        return
     if args.pmc_summary:
         if args.workload == "all":
             ap.error("--pmc-summary needs --workload")
@@ -751,11 +857,26 @@ def main():
     global FUSED_WINDOW
     FUSED_WINDOW = not args.explicit_window
 
+    extra_fn = {**{k: measure_kv_write for k in KV_WRITE}, **{k: measure_indexer for k in INDEXER},
+                **{k: measure_proj for k in PROJ}}
     if args.profile_calls:
         if args.workload == "all":
             ap.error("--profile-calls needs --workload")
-        _, sets = prepare(W.make(args.workload), args.kv, dev, epilogue)
-        profile_pass(sets, args.profile_calls, dev)
+        if args.workload in extra_fn:
+            extra_fn[args.workload](args.workload, dev, 1, 0, False, profile_calls=args.profile_calls)
+            profile_pass([], 0, dev)
+        else:
+            _, sets = prepare(W.make(args.workload), args.kv, dev, epilogue)
+            profile_pass(sets, args.profile_calls, dev)
+        return
+    if args.workload in extra_fn:
+        rec = extra_fn[args.workload](args.workload, dev, args.steps, args.warmup, not args.no_cpu_baseline)
+        line = {"metric": rec["metric"], "value": rec["value"], "unit": rec["unit"], "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": rec["dtype"],
+                "data": "synthetic", "config": rec["config"], "roofline": rec["roofline"],
+                "cpu_baseline": rec["cpu_baseline"]}
+        print(json.dumps(line))
         return
 
     cpu = not args.no_cpu_baseline
