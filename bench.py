@@ -297,13 +297,13 @@ FAMILY_SOURCES = {
              "sa_device.hpp"],
     "kv_write": ["aux_kernels.hip", "sa_device.hpp"],
     "indexer": ["indexer.hip", "sa_device.hpp"],
-    "proj": ["wo_proj.hip", "sa_device.hpp"],
+    "proj": ["wo_proj.hip", "lds_dma.hpp", "sa_device.hpp"],
 }
 FAMILY_KERNELS = {
     "attn": ["attn_fwd_kernel", "attn_combine_kernel"],
     "kv_write": ["kv_write_kernel"],
     "indexer": ["index_scores", "index_topk"],
-    "proj": ["proj_skinny_kernel", "proj_tiled_kernel"],
+    "proj": ["proj_stream_kernel", "proj_skinny_kernel", "proj_tiled_kernel"],
 }
 
 
@@ -382,8 +382,8 @@ def pmc_summary(workload: str, kv: str, fetch_csv: str, write_csv: str):
                     per[hit[0]].append(v)
                 elif "copyBuffer" in name or "elementwise" in name:
                     cal.append(v)
-        if not per[pats[0]] or not cal:
-            raise SystemExit(f"{path}: no {counter} rows for {pats[0]} or the copy kernel")
+        if not any(per.values()) or not cal:
+            raise SystemExit(f"{path}: no {counter} rows for {' / '.join(pats)} or the copy kernel")
         # the calibration copies are the three largest copy dispatches (input-set clones
         # before them are far smaller)
         cal = sorted(cal)[-3:]

@@ -281,8 +281,9 @@ int sa_candidate_blocks(const sa_candidate_args *a, void *stream);
  * per 32 consecutive k (sa_quant_kv_fp8's form, rows of kg), whose values are exact bf16
  * values: the result is the bf16 product with the decoded weights, at half the weight
  * bytes (the page's note on an fp8 grouped GEMM). Supported: kg a multiple of 64 and r a
- * multiple of 128, or m <= 64 with r a multiple of 16 and kg a multiple of 512. Device
- * pointers, caller-owned, 16-byte aligned (w_scale: any); strides in elements. */
+ * multiple of 128, or m <= 64 with r a multiple of 32 and kg a multiple of 256, or with r a
+ * multiple of 16 and kg a multiple of 512; other shapes return SA_ERR_UNSUPPORTED. Device
+ * pointers, caller-owned, 16-byte aligned (w_scale: 4-byte aligned); strides in elements. */
 typedef struct sa_grouped_proj_args {
     int32_t m;              /* tokens */
     int32_t g;              /* groups (o_groups) */

@@ -398,11 +398,12 @@ SA_EXPORT int sa_grouped_proj(const sa_grouped_proj_args* a, void* stream) {
     if (a->w_format != SA_KV_BF16 && a->w_format != SA_KV_FP8_E4M3_B32) return SA_ERR_INVALID;
     const bool fp8 = a->w_format == SA_KV_FP8_E4M3_B32;
     if (!a->o || !a->w || !a->out || (fp8 && !a->w_scale)) return SA_ERR_INVALID;
-    if (!aligned(a->o, 16) || !aligned(a->w, 16) || !aligned(a->out, 16)) return SA_ERR_INVALID;
+    if (!aligned(a->o, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) || (fp8 && !aligned(a->w_scale, 4)))
+        return SA_ERR_INVALID;
     if (a->o_stride < (int64_t)a->g * a->kg || a->out_stride < (int64_t)a->g * a->r || a->o_stride % 8 ||
         a->out_stride % 8)
         return SA_ERR_INVALID;
-    const bool skinny = a->m <= 64 && a->r % 16 == 0 && a->kg % 512 == 0;
+    const bool skinny = a->m <= 64 && ((a->r % 32 == 0 && a->kg % 256 == 0) || (a->r % 16 == 0 && a->kg % 512 == 0));
     if (!skinny && (a->r % 128 != 0 || a->kg % 64 != 0)) return SA_ERR_UNSUPPORTED;
     if ((int64_t)a->g * a->r * a->kg > ((int64_t)1 << 40)) return SA_ERR_UNSUPPORTED;
     sa::ProjParams p{};

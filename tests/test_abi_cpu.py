@@ -174,7 +174,9 @@ def test_grouped_proj_validation(sa):
         return a
     for kw, st in (({"m": 0}, -1), ({"w_format": 5}, -1), ({"o": 0}, -1), ({"w_format": 1}, -1),
                    ({"o_stride": 1000}, -1), ({"out_stride": 100}, -1), ({"r": 200}, -2),
-                   ({"kg": 96, "o_stride": 192}, -2), ({"o": 0x10008}, -1)):
+                   ({"kg": 96, "o_stride": 192}, -2), ({"o": 0x10008}, -1),
+                   # fp8 scale bytes are read as words; a decode shape no kernel takes
+                   ({"w_format": 1, "w_scale": 0x10002}, -1), ({"m": 40, "r": 48, "kg": 256}, -2)):
         assert L.sa_grouped_proj(C.byref(args(**kw)), None) == st, kw
     assert L.sa_grouped_proj(None, None) == -1
 

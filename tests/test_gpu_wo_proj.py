@@ -38,10 +38,13 @@ def _inputs(seed, m, g, r, kg, integer=False):
 
 CASES = [
     (1, 64, 8, 1024, 4096, False),     # decode: 64 tokens, 64 heads of 512 in 8 groups
-    (2, 5, 2, 256, 512, False),        # the skinny kernel with one 16-token block
+    (2, 5, 2, 256, 512, False),        # the LDS-staged decode kernel with one 16-token block
     (3, 300, 3, 256, 640, False),      # the tiled kernel with a ragged token tail
-    (4, 40, 2, 128, 1024, True),       # exact arithmetic, skinny
+    (4, 40, 2, 128, 1024, True),       # exact arithmetic, LDS-staged, 40 of 64 token rows
     (5, 270, 2, 256, 192, True),       # exact arithmetic, tiled, k not a multiple of 512
+    (6, 20, 3, 48, 512, False),        # rows not a multiple of 32: the operand-load decode kernel
+    (7, 33, 1, 32, 256, True),         # one 32-row block, one k chunk, 33 tokens
+    (8, 17, 2, 64, 768, False),        # two 16-token blocks, three k chunks (one stage reused)
 ]
 
 
@@ -57,7 +60,8 @@ def test_grouped_proj_vs_oracle(sa, seed, m, g, r, kg, integer):
         assert_close(u16(out), ref, "grouped proj")
 
 
-@pytest.mark.parametrize("m,g,r,kg", [(64, 8, 1024, 8192), (300, 2, 256, 512), (7, 3, 64, 1024)])
+@pytest.mark.parametrize("m,g,r,kg", [(64, 8, 1024, 8192), (300, 2, 256, 512), (7, 3, 64, 1024),
+                                      (20, 2, 48, 512), (33, 2, 32, 1280)])
 def test_fp8_weights_equal_bf16_on_decoded_weights(sa, m, g, r, kg):
     """Weights stored as e4m3 + block-32 scales (sa_quant_kv_fp8 on rows of kg): the result
     is bit for bit the bf16 product with the decoded weights (the decode is exact), and
