@@ -300,7 +300,7 @@ FAMILY_SOURCES = {
     "proj": ["wo_proj.hip", "lds_dma.hpp", "sa_device.hpp"],
 }
 FAMILY_KERNELS = {
-    "attn": ["attn_fwd_kernel", "attn_combine_kernel"],
+    "attn": ["attn_fwd_kernel", "attn_combine_kernel", "dequant_kv_kernel"],
     "kv_write": ["kv_write_kernel"],
     "indexer": ["index_scores", "index_topk"],
     "proj": ["proj_stream_kernel", "proj_skinny_kernel", "proj_tiled_kernel"],
@@ -492,7 +492,7 @@ def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
     roof["traffic"] = stored_traffic(w.name, kv) if epilogue else None
-    roof["kernel"] = "sparse_attn (attn_fwd_kernel [+ attn_combine_kernel])"
+    roof["kernel"] = "sparse_attn (attn_fwd_kernel [+ attn_combine_kernel] [+ dequant_kv_kernel])"
     roof["kernel_ms_mean"] = k_mean
     roof["kernel_ms_best_batch"] = k_best
     roof["algorithmic_bytes_per_launch"] = alg["attn_bytes"]

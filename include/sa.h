@@ -100,8 +100,11 @@ typedef struct sa_attn_args {
                                                             position outside is left
                                                             unrotated (a caller error) */
 
-    /* split-K workspace (f32 partial results), sized by sa_sparse_attn_workspace; may be
-       NULL when that function reports 0 bytes */
+    /* workspace, sized by sa_sparse_attn_workspace (16-byte aligned; may be NULL when that
+       function reports 0 bytes): the f32 partial results of plans that split the index
+       columns, and, with fp8 storage whose rows are each named by many (query, column) pairs
+       (prefill: at least 16 on average), the cache turned into bf16 rows by one pass before
+       the attention kernel (exact, so the result is that of the bf16 rows) */
     void *workspace;        size_t workspace_bytes;
 
     uint32_t flags;                                      /* SA_FLAG_* */

@@ -1,5 +1,6 @@
 // sparse_attn launches: the key-loop kernel (attn_fwd_kernel.hpp) for every supported
-// shape except the wide bf16 one (attn_fwd_wide.hip), and the split combine kernel.
+// shape except the wide bf16 one (attn_fwd_wide.hip), the split combine kernel, and the pass
+// that turns fp8 storage into bf16 rows for plans that read each row many times.
 #include "attn_fwd_kernel.hpp"
 
 namespace sa {
@@ -78,6 +79,42 @@ static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int kg
     // one wave per (query, head); the host keeps b * s * h within int32 for split plans
     const int64_t waves = (int64_t)p.b * p.s * p.h;
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// fp8 storage -> bf16 rows: each thread turns one 16-byte piece of codes (16 elements of one
+// 32-element block) into 32 bytes of bf16, code x 2^(e - 127) on v_cvt_scalef32_pk_bf16_fp8
+// (exact: the stored values are bf16 values). Streams the cache once (HBM-bound).
+__global__ __launch_bounds__(256) void dequant_kv_kernel(const uint8_t* codes, int64_t codes_seq_stride,
+                                                         const uint8_t* scales, int64_t scales_seq_stride,
+                                                         int b, int rows, int d, uint16_t* out) {
+    const int pieces = d / 16;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_seq = (int64_t)rows * pieces;
+    if (i >= per_seq * b) return;
+    const int64_t n = i / per_seq, rem = i % per_seq;
+    const int64_t r = rem / pieces;
+    const int pc = (int)(rem % pieces);
+    const u32x4 c = *(const u32x4*)(codes + n * codes_seq_stride + r * d + 16 * pc);
+    const float sc = bits_f32((uint32_t)scales[n * scales_seq_stride + r * (d / 32) + pc / 2] << 23);
+    u32x4 o[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[j / 2][2 * (j % 2)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], sc, false));
+        o[j / 2][2 * (j % 2) + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[j], sc, true));
+    }
+    u32x4* dst = (u32x4*)(out + (n * rows + r) * d + 16 * pc);
+    dst[0] = o[0];
+    dst[1] = o[1];
+}
+
+hipError_t launch_dequant_kv(const uint8_t* codes, int64_t codes_seq_stride, const uint8_t* scales,
+                             int64_t scales_seq_stride, int b, int rows, int d, uint16_t* out, hipStream_t st) {
+    const int64_t threads = (int64_t)b * rows * (d / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(dequant_kv_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, codes_seq_stride,
+                       scales, scales_seq_stride, b, rows, d, out);
     return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // sa_sparse_attn_noalloc (include/sa.h): sparse_attn for callers that cannot allocate device
-// memory. The split partials live in a static device array of the library instead of a
-// caller workspace; everything else is sa_sparse_attn's own path (same plan, same kernels).
+// memory. The workspace (split partials, dequantised rows) lives in a static device array of
+// the library instead of a caller buffer; everything else is sa_sparse_attn's own path (same
+// plan, same kernels).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -55,7 +56,6 @@ SA_EXPORT int sa_sparse_attn_noalloc(const sa_attn_args* a, void* stream) {
     sa::Plan pl;
     rc = sa::prepare_sparse_attn(a, ws, kScratchBytes, p, pl);
     if (rc != SA_OK) return rc;
-    const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, pl.hpw, pl.kg,
-                                                (hipStream_t)stream);
+    const hipError_t e = sa::run_sparse_attn(a, p, pl, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }

@@ -91,12 +91,25 @@ int check_pointers(const sa_attn_args* a) {
 // compute units idle and each split keeps at least kMinTilesPerSplit tiles, because every
 // split writes an f32 partial of 16*nw heads x d (as large as 16*nw/8 key tiles).
 constexpr int kMinTilesPerSplit = 8;
+// fp8 storage whose rows are each named by at least this many (query, column) pairs on
+// average (prefill) is dequantised into bf16 rows once per call, and the bf16 kernels run on
+// those: the per-tile conversion in LDS then costs more than one pass over the cache
+// (measured on 8192 queries x 128 heads x 2176 rows: 4.41 ms with the in-kernel conversion).
+// Decode, where a row is named about once, keeps the conversion inside the kernel.
+constexpr int64_t kDequantReuse = 16;
 
 sa::Plan make_plan(const sa_attn_args* a, int cus) {
     using sa::kHeadsPerWave;
     using sa::kTileKeys;
     sa::Plan pl{};
     const int64_t nq = (int64_t)a->b * a->s;
+    if (a->kv_format == SA_KV_FP8_E4M3_B32 && nq * a->topk >= kDequantReuse * a->b * (int64_t)a->kv_rows &&
+        (int64_t)a->kv_rows * a->d * 2 <= INT32_MAX) {
+        pl.dequant = true;
+        pl.dq_bytes = ((size_t)a->b * a->kv_rows * a->d * 2 + 255) / 256 * 256;
+    }
+    // the storage the attention kernel reads
+    const bool bf16_rows = a->kv_format == SA_KV_BF16 || pl.dequant;
     auto blocks_for = [&](int nw) { return (a->h + nw * kHeadsPerWave - 1) / (nw * kHeadsPerWave); };
     const int max_nw = std::min<int>(sa::kMaxWaves, (a->h + kHeadsPerWave - 1) / kHeadsPerWave);
     // The widest workgroup the heads allow: one gathered tile then serves the most heads,
@@ -110,7 +123,7 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // Two head blocks per wave (one gathered operand feeds two MFMAs) when there are enough
     // workgroups without splitting: bf16 rows of 512, 128 heads or more.
     pl.hpw = 1;
-    if (a->kv_format == SA_KV_BF16 && a->d == 512 && pl.nw == 4 && a->h >= 8 * kHeadsPerWave &&
+    if (bf16_rows && a->d == 512 && pl.nw == 4 && a->h >= 8 * kHeadsPerWave &&
         nq * blocks_for(8) >= cus)
         pl.hpw = 2;
     pl.kg = 1;
@@ -132,7 +145,7 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // 12.9 us that way and 13.6 us with four key groups, the merge costing what the shorter
     // loop saved.)
     if (splits > 1 && a->d == 512 && pl.hpw == 1) {
-        for (int kg = a->kv_format == SA_KV_BF16 ? 4 : 2; kg >= 2; kg /= 2) {
+        for (int kg = bf16_rows ? 4 : 2; kg >= 2; kg /= 2) {
             if (nq * blocks_for(4 / kg) <= cus && ntiles >= kg) {
                 pl.kg = kg;
                 pl.nw = 4;
@@ -145,16 +158,16 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     pl.h_pad = pl.head_blocks * pl.nw / pl.kg * pl.hpw * kHeadsPerWave;
     // a workgroup stages at most kMaxColsPerSplit index columns (kMaxColsFp8Pipe for fp8
     // storage at d = 512)
-    const int max_cols = a->kv_format != SA_KV_BF16 && a->d == 512 ? sa::kMaxColsFp8Pipe : sa::kMaxColsPerSplit;
+    const int max_cols = !bf16_rows && a->d == 512 ? sa::kMaxColsFp8Pipe : sa::kMaxColsPerSplit;
     const int max_tiles = max_cols / kTileKeys;
     splits = std::max(splits, (ntiles + max_tiles - 1) / max_tiles);
     const int tiles_per_split = (ntiles + splits - 1) / splits;
     pl.cols_per_split = tiles_per_split * kTileKeys;
     pl.splits = (a->topk + pl.cols_per_split - 1) / pl.cols_per_split;
-    pl.ws_bytes = 0;
+    pl.ws_bytes = pl.dq_bytes;
     if (pl.splits > 1) {
         const size_t slots = (size_t)a->b * a->s * pl.splits * pl.h_pad;
-        pl.ws_bytes = slots * a->d * sizeof(float) + slots * 2 * sizeof(float);
+        pl.ws_bytes += slots * a->d * sizeof(float) + slots * 2 * sizeof(float);
     }
     return pl;
 }
@@ -204,9 +217,14 @@ int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParam
     p = KParams{};
     p.b = a->b; p.s = a->s; p.h = a->h; p.d = a->d; p.topk = a->topk; p.kv_rows = a->kv_rows;
     p.q = (const uint16_t*)a->q; p.q_seq_stride = a->q_seq_stride;
-    p.kv = (const uint8_t*)a->kv;
-    p.kv_seq_stride_bytes = a->kv_format == SA_KV_BF16 ? a->kv_seq_stride * 2 : a->kv_seq_stride;
-    p.kv_scale = a->kv_scale; p.kv_scale_seq_stride = a->kv_scale_seq_stride;
+    if (pl.dequant) {       // the kernels read the bf16 rows the dequantisation pass writes
+        p.kv = (const uint8_t*)ws;
+        p.kv_seq_stride_bytes = (int64_t)a->kv_rows * a->d * 2;
+    } else {
+        p.kv = (const uint8_t*)a->kv;
+        p.kv_seq_stride_bytes = a->kv_format == SA_KV_BF16 ? a->kv_seq_stride * 2 : a->kv_seq_stride;
+        p.kv_scale = a->kv_scale; p.kv_scale_seq_stride = a->kv_scale_seq_stride;
+    }
     p.sink = a->sink;
     p.idx = a->idx; p.idx_seq_stride = a->idx_seq_stride;
     p.scale_log2 = a->scale * 1.4426950408889634f;
@@ -217,7 +235,7 @@ int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParam
     p.head_blocks = pl.head_blocks; p.h_pad = pl.h_pad;
     if (pl.splits > 1) {
         const size_t slots = (size_t)a->b * a->s * pl.splits * pl.h_pad;
-        p.ws_o = (float*)ws;
+        p.ws_o = (float*)((uint8_t*)ws + pl.dq_bytes);
         p.ws_ml = p.ws_o + slots * a->d;
     }
     p.flags = a->flags; p.err_word = a->err_word;
@@ -229,6 +247,16 @@ int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParam
     return SA_OK;
 }
 
+hipError_t run_sparse_attn(const sa_attn_args* a, const KParams& p, const Plan& pl, hipStream_t st) {
+    if (pl.dequant) {
+        const hipError_t e = launch_dequant_kv((const uint8_t*)a->kv, a->kv_seq_stride, a->kv_scale,
+                                               a->kv_scale_seq_stride, a->b, a->kv_rows, a->d,
+                                               (uint16_t*)p.kv, st);
+        if (e != hipSuccess) return e;
+    }
+    return launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32 && !pl.dequant, pl.nw, pl.hpw, pl.kg, st);
+}
+
 }  // namespace sa
 
 SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
@@ -236,7 +264,7 @@ SA_EXPORT int sa_sparse_attn(const sa_attn_args* a, void* stream) {
     sa::Plan pl;
     const int rc = sa::prepare_sparse_attn(a, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, p, pl);
     if (rc != SA_OK) return rc;
-    const hipError_t e = sa::launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32, pl.nw, pl.hpw, pl.kg, (hipStream_t)stream);
+    const hipError_t e = sa::run_sparse_attn(a, p, pl, (hipStream_t)stream);
     return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

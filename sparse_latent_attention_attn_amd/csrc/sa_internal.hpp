@@ -93,14 +93,23 @@ struct Plan {
     int head_blocks;
     int h_pad;
     int splits;
-    int cols_per_split; // a multiple of the 64-column key tile
-    size_t ws_bytes;
+    int cols_per_split; // a multiple of the key tile
+    bool dequant;       // fp8 storage turned into bf16 rows at the start of the workspace first
+    size_t dq_bytes;    // bytes of those rows (0 without)
+    size_t ws_bytes;    // the whole workspace: dequantised rows, then the split partials
 };
 
 // Validation, plan and kernel parameters of a sparse_attn call (sa_api.cpp); returns an SA_*
 // status. ws / ws_bytes: the buffer of the split partials.
 int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParams& p, Plan& pl);
 hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st);
+// The kernels of a prepared call: the dequantisation pass when the plan has one, then
+// sparse_attn (and its combine kernel).
+hipError_t run_sparse_attn(const sa_attn_args* a, const KParams& p, const Plan& pl, hipStream_t st);
+// fp8 storage rows (e4m3 codes [b][rows][d] + e8m0 scales [b][rows][d/32], sequence strides
+// in bytes) to bf16 rows [b][rows][d], contiguous.
+hipError_t launch_dequant_kv(const uint8_t* codes, int64_t codes_seq_stride, const uint8_t* scales,
+                             int64_t scales_seq_stride, int b, int rows, int d, uint16_t* out, hipStream_t st);
 hipError_t launch_window_idxs(int32_t window, int32_t seqlen, int32_t nseq, const int32_t* start_pos,
                               int32_t* idx, int64_t seq_stride, int64_t row_stride, int32_t cols,
                               hipStream_t st);

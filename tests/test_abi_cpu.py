@@ -117,6 +117,21 @@ def test_split_plans_keep_the_combine_grid_in_int32(sa):
     assert sa.lib().sa_sparse_attn(C.byref(a), None) == -2
 
 
+def test_fp8_prefill_plans_take_dequantised_rows(sa):
+    """fp8 storage: a prefill shape (each row named by thousands of (query, column) pairs)
+    asks for a workspace holding the cache as bf16 rows; a decode shape (each row named about
+    once) converts inside the kernel and needs none."""
+    n = C.c_size_t(0)
+    a = _args(sa, b=1, s=8192, h=128, d=512, topk=2176, kv_rows=2176, kv_format=1,
+              q_seq_stride=0, out_seq_stride=0, kv_seq_stride=0, idx_seq_stride=0)
+    assert sa.lib().sa_sparse_attn_workspace(C.byref(a), C.byref(n)) == 0
+    assert n.value == 2176 * 512 * 2
+    a = _args(sa, b=64, s=1, h=128, d=512, topk=640, kv_rows=16512, kv_format=1,
+              q_seq_stride=128 * 512, out_seq_stride=128 * 512, kv_seq_stride=16512 * 512,
+              idx_seq_stride=640, kv_scale_seq_stride=16512 * 16)
+    assert sa.lib().sa_sparse_attn_workspace(C.byref(a), C.byref(n)) == 0 and n.value == 0
+
+
 def test_rope_table_validation(sa):
     L = sa.lib()
     fake = C.c_void_p(0x10000)

@@ -643,6 +643,34 @@ def test_fp8_storage_other_head_dims(sa, seed, b, s, h, d, rows, topk, hole, dup
     assert_close(u16(out).reshape(-1, h, d), ref, f"fp8 d={d}")
 
 
+@pytest.mark.parametrize("seed,b,s,h,d,rows,topk,hole,dup", [
+    (111, 2, 64, 32, 512, 96, 80, 0.1, False),       # bf16 kernels on the dequantised rows
+    (112, 1, 40, 64, 128, 50, 45, 0.2, True),
+    (113, 2, 2, 16, 256, 300, 5000, 0.05, True),     # dequantised rows and split partials
+])
+def test_fp8_dequantised_rows_plan(sa, seed, b, s, h, d, rows, topk, hole, dup):
+    """fp8 storage whose rows are each named by many (query, column) pairs: the plan turns the
+    cache into bf16 rows in the workspace first (reported by the workspace query) and runs the
+    bf16 kernels on them; against the oracle on the round-tripped rows, epilogue on."""
+    _say("fp8 dequantised rows", seed, d, rows, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, d, rows, topk, hole, dup)
+    scale = float(np.float32(d ** -0.5))
+    codes, kv_scale = sa.quant_kv_fp8(kv.cuda(), want=("codes", "scales"))
+    rd = 64 if d == 512 else d // 4
+    pos = torch.randint(0, 3000, (b, s), generator=torch.Generator().manual_seed(seed), dtype=torch.int32)
+    table = sa.rope_table(rd, 3000, 10000.0, "cuda")
+    out = torch.empty_like(q, device="cuda")
+    args = sa.make_args(q.cuda(), codes, sink.cuda(), idx.cuda(), scale, out, kv_scale=kv_scale,
+                        rope=(table, pos.cuda()))
+    assert sa.sparse_attn_workspace_bytes(args) >= b * rows * d * 2
+    out = sa.sparse_attn(q.cuda(), codes, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale,
+                         rope=(table, pos.cuda()))
+    kv_ref = oracle.act_quant(u16(kv).reshape(-1, d))[0].reshape(kv.shape)
+    core = oracle.sparse_attn(u16(q), kv_ref, sink.numpy(), idx.numpy(), scale)
+    ref = oracle.apply_rotary(core, rd, oracle.freqs_cis(rd, 3000, 10000.0), pos.view(-1).numpy(), inverse=True)
+    assert_close(u16(out).reshape(-1, h, d), ref, f"fp8 dequantised rows {seed}")
+
+
 # ------------------------------------------------------------------ fused window lists
 def _fused_case(w, fmt):
     """(explicit output, fused output, idx with the window columns poisoned)."""
