@@ -380,30 +380,44 @@ __device__ __forceinline__ int count_selectable(SA_LDS const uint32_t* keys, int
     return total;
 }
 
-// The ordered selection: every thread owns the run of `per` consecutive entries
-// [tid * per, ...); among equal keys at the threshold the lowest positions are taken first.
-// Calls take(i, rank) for every selected entry i with its rank among the selected (in
-// position order). Two block scans in all.
+// The ordered selection: wave w owns positions [w * chunk, (w + 1) * chunk), read as rows of
+// 64 consecutive keys (lane l takes position base + 64 r + l, so every LDS read is free of
+// bank conflicts); the rank of a selected entry among the selected, in position order, counts
+// the selected entries of earlier waves (one block scan over the waves' totals), of earlier
+// rows of its wave and of lower lanes of its row. Among equal keys at the threshold the
+// lowest positions are taken first. Calls take(i, rank) for every selected entry i.
 template <int NT, typename Take>
 __device__ __forceinline__ void select_in_order(SA_LDS const uint32_t* keys, int n, uint32_t thr, int ties,
                                                 SA_LDS int* tot, Take take) {
-    const int per = (n + NT - 1) / NT;
-    const int i0 = min(n, (int)threadIdx.x * per), i1 = min(n, i0 + per);
-    int eq = 0;
-    for (int i = i0; i < i1; ++i) eq += keys[i] == thr;
-    int eq_total;
-    int tie_rank = block_excl_sum<NT>(eq, tot, eq_total);
-    int cnt = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t u = keys[i];
-        if (u > thr || (u == thr && tie_rank++ < ties)) ++cnt;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rows = (n + NT - 1) / NT;
+    const int base = wid * rows * 64;
+    const uint64_t below = (1ull << lane) - 1;
+    // keys equal to the threshold before this wave's chunk
+    int eq_w = 0;
+    for (int r = 0; r < rows; ++r) {
+        const int i = base + 64 * r + lane;
+        eq_w += __builtin_popcountll(__ballot(i < n && keys[i] == thr));
     }
-    int cnt_total;
-    int rank = block_excl_sum<NT>(cnt, tot, cnt_total);
-    tie_rank -= eq;                                              // back to this run's first tie
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t u = keys[i];
-        if (u > thr || (u == thr && tie_rank++ < ties)) take(i, rank++);
+    int total;
+    const int eq_before = __shfl(block_excl_sum<NT>(lane == 0 ? eq_w : 0, tot, total), 0, 64);
+    // whether entry i is selected, given the ties met before its row
+    auto sel_row = [&](int r, int& tie_seen) {
+        const int i = base + 64 * r + lane;
+        const uint32_t u = i < n ? keys[i] : 0u;
+        const uint64_t beq = __ballot(i < n && u == thr);
+        const bool sel = u > thr || (((beq >> lane) & 1) && tie_seen + __builtin_popcountll(beq & below) < ties);
+        tie_seen += __builtin_popcountll(beq);
+        return __ballot(sel);
+    };
+    int sel_w = 0, tie_seen = eq_before;
+    for (int r = 0; r < rows; ++r) sel_w += __builtin_popcountll(sel_row(r, tie_seen));
+    int rank = __shfl(block_excl_sum<NT>(lane == 0 ? sel_w : 0, tot, total), 0, 64);
+    tie_seen = eq_before;
+    for (int r = 0; r < rows; ++r) {
+        const uint64_t bs = sel_row(r, tie_seen);
+        if ((bs >> lane) & 1) take(base + 64 * r + lane, rank + __builtin_popcountll(bs & below));
+        rank += __builtin_popcountll(bs);
     }
 }
 
