@@ -454,8 +454,8 @@ __global__ __launch_bounds__(NT) void index_topk_kernel(const IdxParams p) {
 // with -inf), the block of the newest visible position, (len - 1) / block_size with floor
 // division, pinned to +inf, the min(topk_blocks, blocks) best blocks kept when above -inf
 // (ties: the lower block first), each block's flag repeated over its positions.
-__global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams p) {
-    constexpr int NT = 256;
+template <int NT>
+__global__ __launch_bounds__(NT) void candidate_blocks_kernel(const CandParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
     SA_LDS uint32_t* hist = (SA_LDS uint32_t*)smem_raw;
     SA_LDS int* misc = (SA_LDS int*)(hist + 256);
@@ -470,9 +470,12 @@ __global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams 
     const int64_t len = pos < 0 ? 0 : ((int64_t)pos + 1) / p.ratio;
     const int64_t last = len > 0 ? (len - 1) / p.block_size : -1;
     // block maxima as the maxima of the order-preserving keys (-inf padding is key 0), with
-    // 8 logit loads in flight per thread
+    // 8 logit loads in flight per thread. A block size that is a power of two up to 64 puts
+    // each block in consecutive lanes of one wave: their maximum is taken by lane exchanges
+    // and stored by the block's first lane; other sizes use LDS atomics.
+    const bool lanes = p.block_size <= 64 && (p.block_size & (p.block_size - 1)) == 0;
     for (int j = tid; j < nblk; j += NT) {
-        keys[j] = 0u;
+        if (!lanes) keys[j] = 0u;
         keep[j] = 0;
     }
     __syncthreads();
@@ -486,24 +489,45 @@ __global__ __launch_bounds__(256) void candidate_blocks_kernel(const CandParams 
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = i0 + u * NT + tid;
-            const uint32_t key = score_key(v[u]);
-            if (i < p.n_pos && key != 0u)
+            uint32_t key = score_key(v[u]);
+            if (lanes) {
+                for (int o = 1; o < p.block_size; o <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, o, 64));
+                if (i % p.block_size == 0 && i < p.n_pos) keys[i / p.block_size] = key;
+            } else if (i < p.n_pos && key != 0u) {
                 __hip_atomic_fetch_max(&keys[i / p.block_size], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
     }
     __syncthreads();
     if (tid == 0 && last >= 0 && last < nblk) keys[last] = score_key(INFINITY);
     __syncthreads();
-    const int k = min(p.topk_blocks, count_selectable<NT>(keys, nblk, misc));
-    if (k > 0) {
+    const int selectable = count_selectable<NT>(keys, nblk, misc);
+    const int k = min(p.topk_blocks, selectable);
+    if (k > 0 && k == selectable) {
+        // every block with a visible position is kept: no selection needed
+        for (int j = tid; j < nblk; j += NT) keep[j] = keys[j] != 0u;
+    } else if (k > 0) {
         uint32_t thr;
         int ties;
         radix_threshold<NT>(keys, nblk, k, hist, misc, thr, ties);
         select_in_order<NT>(keys, nblk, thr, ties, misc, [&](int j, int) { keep[j] = 1; });
     }
     __syncthreads();
+    // each block's flag repeated over its positions, 16 bytes per store where the row allows
     uint8_t* mask = p.mask + (int64_t)n * p.mask_seq_stride + (int64_t)t * p.n_pos;
-    for (int u = tid; u < p.n_pos; u += NT) mask[u] = keep[u / p.block_size];
+    const int n16 = ((uintptr_t)mask % 16 == 0) ? p.n_pos / 16 : 0;
+    for (int c = tid; c < n16; c += NT) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) word |= (uint32_t)keep[(16 * c + 4 * q + b) / p.block_size] << (8 * b);
+            w[q] = word;
+        }
+        *(u32x4*)(mask + 16 * c) = w;
+    }
+    for (int u = 16 * n16 + tid; u < p.n_pos; u += NT) mask[u] = keep[u / p.block_size];
 }
 
 // ------------------------------------------------------------------ launches
@@ -569,9 +593,13 @@ hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st) {
     const size_t lds = (256 + 16) * 4 + (size_t)nblk * 5;
     const int64_t nq = (int64_t)p.b * p.s;
     if (lds > 160 * 1024 || nq > 0x7fffffff) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute((const void*)candidate_blocks_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // long rows get four times the threads (more logit loads in flight per query)
+    const bool wide = p.n_pos > 4096;
+    const void* k = wide ? (const void*)candidate_blocks_kernel<1024> : (const void*)candidate_blocks_kernel<256>;
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(candidate_blocks_kernel, dim3((unsigned)nq), dim3(256), lds, st, p);
+    if (wide) hipLaunchKernelGGL(candidate_blocks_kernel<1024>, dim3((unsigned)nq), dim3(1024), lds, st, p);
+    else hipLaunchKernelGGL(candidate_blocks_kernel<256>, dim3((unsigned)nq), dim3(256), lds, st, p);
     return hipGetLastError();
 }
 

@@ -116,10 +116,13 @@ def test_indexer_candidates_and_two_levels(sa):
 
 
 def test_candidate_blocks_random_logits(sa):
-    """Random logits with -inf beyond each query's visible positions, several block sizes,
-    ragged last blocks."""
+    """Random logits with -inf beyond each query's visible positions, several block sizes
+    (powers of two up to 64 take block maxima by lane exchanges, others by LDS atomics), ragged
+    last blocks, selections that keep every visible block and ones that choose."""
     g = torch.Generator().manual_seed(21)
-    for b, s, n_pos, ratio, tb, bs in ((2, 6, 1000, 4, 17, 8), (1, 3, 16384, 4, 2048, 8), (3, 4, 999, 1, 3, 7)):
+    for b, s, n_pos, ratio, tb, bs in ((2, 6, 1000, 4, 17, 8), (1, 3, 16384, 4, 2048, 8), (3, 4, 999, 1, 3, 7),
+                                       (2, 5, 1001, 2, 40, 16), (2, 3, 4096, 4, 64, 64), (1, 4, 777, 1, 500, 4),
+                                       (2, 3, 2048, 4, 9, 1)):
         pos = torch.randint(0, ratio * n_pos, (b, s), generator=g, dtype=torch.int32)
         lg = torch.randn(b, s, n_pos, generator=g)
         vis = torch.clamp((pos.long() + 1) // ratio, max=n_pos)
