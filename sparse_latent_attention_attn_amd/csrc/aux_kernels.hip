@@ -209,10 +209,12 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {
     const bool live = row < (int64_t)p.b * p.s;
     const int n = live ? (int)(row / p.s) : 0;
     const int t = live ? (int)(row % p.s) : 0;
+    // the row's bytes and its position are loaded side by side (one memory round trip)
+    u32x4 v = live ? *(const u32x4*)(p.x + (int64_t)n * p.x_seq_stride + (int64_t)t * D + 8 * part)
+                   : u32x4{0, 0, 0, 0};
     const int pos = live ? p.pos[(int64_t)n * p.pos_seq_stride + t] : 0;
     const bool pos_ok = live && pos >= 0 && (p.rope_dim == 0 || pos < p.max_pos);
-    u32x4 v = pos_ok ? *(const u32x4*)(p.x + (int64_t)n * p.x_seq_stride + (int64_t)t * D + 8 * part)
-                     : u32x4{0, 0, 0, 0};
+    if (!pos_ok) v = u32x4{0, 0, 0, 0};
     float x[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) { x[2 * k] = bf16_lo(v[k]); x[2 * k + 1] = bf16_hi(v[k]); }
