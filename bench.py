@@ -657,7 +657,8 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool, profile_
     index heads of 128, ratio 4, 512 picks, and select_candidate_blocks (sa_candidate_blocks,
     2048 blocks of 8) on its scores. Decode reads 4 MB of index keys per sequence and is
     HBM-bound; the prefill does 2 h d flops per visible (query, position) pair and is bound by
-    the MFMA roofline."""
+    the MFMA roofline. Bytes: keys, q, w, positions, the lists, and the f32 scores (an output
+    of the call, written by the score kernel and read back by the top-k)."""
     b, s, n_pos, kind = INDEXER[name]
     h, d, ratio, topk = 32, 128, 4, 512
     g = torch.Generator().manual_seed(41)
@@ -670,7 +671,7 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool, profile_
     pairs = int(vis.sum())
     flops = 2.0 * h * d * pairs
     key_bytes = b * n_pos * d * 2
-    alg_bytes = key_bytes + b * s * (h * d * 2 + h * 4 + 4 + topk * 4)
+    alg_bytes = key_bytes + b * s * (h * d * 2 + h * 4 + 4 + topk * 4) + b * s * n_pos * 4 * 2
     nsets = max(2, min(64, math.ceil(2 * MALL_BYTES / alg_bytes)))
     sets = []
     for _ in range(nsets):
