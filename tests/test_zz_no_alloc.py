@@ -1,7 +1,8 @@
 """sa_sparse_attn_noalloc (the allocation-free variant) against sa_sparse_attn, called
-through the C ABI on plans that need a workspace (split partials): two calls in a row, the
-second on a smaller problem, each bit for bit equal to the workspace entry point and within
-the tolerance of the oracle; and a plan larger than the static buffer is refused."""
+through the C ABI on plans that need a workspace (split partials, dequantised fp8 rows): two
+calls in a row, the second on a smaller problem, each bit for bit equal to the workspace
+entry point and within the tolerance of the oracle; and a plan larger than the static buffer
+is refused."""
 import ctypes as C
 import sys
 
@@ -35,10 +36,13 @@ PAIRS = [
     [(201, 3, 2, 64, 256, 3000, 2000, "bf16"), (202, 1, 1, 32, 256, 800, 700, "bf16")],
     [(203, 2, 1, 64, 512, 9000, 5000, "bf16"), (204, 1, 2, 16, 512, 6000, 4200, "bf16")],
     [(205, 2, 1, 48, 128, 4000, 3500, "fp8"), (206, 1, 1, 16, 64, 900, 640, "fp8")],
+    # fp8 rows named by many queries: the workspace holds the dequantised rows (and, the
+    # first time, split partials behind them)
+    [(208, 1, 40, 16, 256, 4600, 4400, "fp8"), (209, 1, 64, 32, 512, 96, 80, "fp8")],
 ]
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=["d256", "d512-long", "fp8"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["d256", "d512-long", "fp8", "fp8-dequantised"])
 def test_noalloc_matches_workspace_entry_point(sa, pair):
     for seed, b, s, h, d, rows, topk, fmt in pair:
         print("[case] noalloc", seed, b, s, h, d, topk, fmt, file=sys.stderr, flush=True)
