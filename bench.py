@@ -303,7 +303,7 @@ FAMILY_KERNELS = {
     "attn": ["attn_fwd_kernel", "attn_combine_kernel", "dequant_kv_kernel"],
     "kv_write": ["kv_write_kernel"],
     "indexer": ["index_scores", "index_topk"],
-    "proj": ["proj_stream_kernel", "proj_skinny_kernel", "proj_tiled_kernel"],
+    "proj": ["proj_stream_kernel", "proj_skinny_kernel", "proj_wide_kernel", "proj_tiled_kernel"],
 }
 
 
@@ -780,7 +780,7 @@ def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool, profile_cal
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
         value, unit, metric = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s", "grouped wo_a TFLOP/s (prefill)"
-    roof.update({"traffic": stored_traffic(name, "bf16"), "kernel": "proj_skinny_kernel" if m <= 64 else "proj_tiled_kernel",
+    roof.update({"traffic": stored_traffic(name, "bf16"), "kernel": "proj_stream_kernel" if m <= 64 else ("proj_tiled_kernel" if wfmt == "fp8" else "proj_wide_kernel"),
                  "kernel_ms_mean": k_mean, "kernel_ms_best_batch": k_best,
                  "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops})
     rec = {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_step, "steps": steps,

@@ -8,9 +8,12 @@
 // The kernels compute the transposed product C^T[n][t] = W . O^T on v_mfma_f32_16x16x32_bf16
 // (A = rows of W, B = token rows of O), so each lane ends with 4 consecutive outputs of one
 // token and stores them as 8 bytes.
-//   * proj_tiled_kernel (many tokens): 128 rows of W x 256 tokens per workgroup, k steps of
-//     64 staged in LDS (double-buffered, 16-byte chunks XOR-swizzled by row), 4 waves of
-//     64 x 128.
+//   * proj_wide_kernel (many tokens, bf16 weights): 256 rows of W x 256 tokens per workgroup
+//     of 8 waves (two per SIMD), k steps of 64 copied into LDS by direct-to-LDS loads of whole
+//     rows, double-buffered.
+//   * proj_tiled_kernel (many tokens, fp8 weights or other shapes): 128 rows of W x 256
+//     tokens per workgroup, k steps of 64 staged in LDS through registers (double-buffered,
+//     16-byte chunks XOR-swizzled by row), 4 waves of 64 x 128.
 //   * proj_stream_kernel (decode, at most 64 tokens, r a multiple of 32, kg of 256): the cost
 //     is streaming W once; 32 rows of W per workgroup, weights and tokens copied into LDS by
 //     direct-to-LDS loads of whole rows, the 4 waves split k and LDS sums the parts.
@@ -424,6 +427,101 @@ __global__ __launch_bounds__(256) void proj_tiled_kernel(const ProjParams p) {
     }
 }
 
+// ------------------------------------------------------------------ wide tiles (bf16)
+// Many tokens, bf16 weights: 256 rows of W x 256 tokens per workgroup of 8 waves (two per
+// SIMD, so one wave's memory stalls are covered by the other's matrix work), each wave 64
+// rows x 128 tokens. k advances in steps of 64: the step's 512 rows of 128 bytes are copied
+// straight into LDS by direct-to-LDS loads (8 whole rows per load instruction), two steps in
+// LDS, the next one loading while the current one is multiplied. Rows are stored with their
+// 16-byte pieces XOR-ed by (row >> 1) & 7 (conflict-free operand reads, as proj_lds).
+constexpr int kWideN = 256, kWideM = 256, kWideK = 64, kWideWaves = 8;
+constexpr int kWideRowBytes = kWideK * 2;                            // 128: 8 pieces
+constexpr int kWideStage = (kWideN + kWideM) * kWideRowBytes;       // 64 KB
+constexpr int kWideLoads = (kWideN + kWideM) / 8 / kWideWaves;      // load instructions per wave and step
+
+__global__ __launch_bounds__(kWideWaves * 64) void proj_wide_kernel(const ProjParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+    SA_LDS uint8_t* smem = (SA_LDS uint8_t*)smem_raw;
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, gq = lane >> 4;
+    const int wn = wid & 3, wm = wid >> 2;                       // wave: rows 64 wn.., tokens 128 wm..
+    // XCD-aware order, as in proj_tiled_kernel: the row tiles of one (token tile, group) pair
+    // go to one XCD back to back
+    const int nt = p.r / kWideN, nm = (p.m + kWideM - 1) / kWideM;
+    const int xcd = blockIdx.x % 8, q = blockIdx.x / 8;
+    const int pair = (q / nt) * 8 + xcd;
+    if (pair >= nm * p.g) return;
+    const int n_base = (q % nt) * kWideN, m_base = (pair % nm) * kWideM, gg = pair / nm;
+    const int m_rows = min(kWideM, p.m - m_base);                // token rows that exist
+    const i32x4 w_rsrc = make_buffer_rsrc(p.w + ((int64_t)gg * p.r + n_base) * p.kg, (uint32_t)(kWideN * p.kg * 2));
+    const i32x4 t_rsrc = make_buffer_rsrc(p.o + (int64_t)m_base * p.o_stride + (int64_t)gg * p.kg,
+                                          (uint32_t)(((int64_t)(m_rows - 1) * p.o_stride + p.kg) * 2));
+    // load j of this wave fills rows 8 I .. 8 I + 7 of the stage (I = wid * kWideLoads + j;
+    // stage rows 0 .. 255 are W, 256 .. 511 tokens): lane fills piece position lane & 7 of
+    // row lane >> 3 from the global piece stored there
+    int off[kWideLoads];
+#pragma unroll
+    for (int j = 0; j < kWideLoads; ++j) {
+        const int row = 8 * (wid * kWideLoads + j) + (lane >> 3);
+        const int pc = (lane & 7) ^ ((row >> 1) & 7);
+        off[j] = row < kWideN ? row * p.kg * 2 + 16 * pc
+                              : min(row - kWideN, m_rows - 1) * (int)(p.o_stride * 2) + 16 * pc;
+    }
+    auto issue = [&](int kt) {
+        const uint32_t base = lds_byte_addr(smem + (kt & 1) * kWideStage);
+#pragma unroll
+        for (int j = 0; j < kWideLoads; ++j) {
+            const int I = wid * kWideLoads + j;                  // uniform: W or token rows
+            lds_dma16(I < kWideN / 8 ? w_rsrc : t_rsrc, base + I * 1024, off[j] + kt * kWideRowBytes);
+        }
+    };
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = p.kg / kWideK;
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
+        vmcnt_wait<0>();
+        lds_sync();                                  // step kt landed; step kt-1 done by all
+        if (kt + 1 < nk) issue(kt + 1);
+        SA_LDS const uint8_t* wt = smem + (kt & 1) * kWideStage;
+        SA_LDS const uint8_t* ot = wt + kWideN * kWideRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4 a[4], b[8];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                a[nb] = *(SA_LDS const u32x4*)(wt + proj_lds(wn * 64 + nb * 16 + l16, 4 * kk + gq));
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+                b[mb] = *(SA_LDS const u32x4*)(ot + proj_lds(wm * 128 + mb * 16 + l16, 4 * kk + gq));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = mfma16(a[nb], b[mb], acc[nb][mb]);
+        }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int t = m_base + wm * 128 + mb * 16 + l16;
+        if (t >= p.m) continue;
+        uint16_t* orow_out = p.out + (int64_t)t * p.out_stride + (int64_t)gg * p.r + n_base + wn * 64 + 4 * gq;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            *(u32x2*)(orow_out + nb * 16) = u32x2{pack_bf16x2(acc[nb][mb][0], acc[nb][mb][1]),
+                                                  pack_bf16x2(acc[nb][mb][2], acc[nb][mb][3])};
+    }
+}
+
+// The wide kernel's conditions: bf16 weights, whole 256-row tiles and 64-wide k steps, and
+// every buffer it addresses under 2^31 bytes.
+static bool wide_fits(const ProjParams& p) {
+    return p.w != nullptr && p.r % kWideN == 0 && p.kg % kWideK == 0 && (int64_t)kWideN * p.kg * 2 < (1ll << 31) &&
+           ((int64_t)(kWideM - 1) * p.o_stride + p.kg) * 2 < (1ll << 31) - 64;
+}
+
 // ------------------------------------------------------------------ launch
 template <bool FP8>
 static hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
@@ -435,6 +533,16 @@ static hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
     if (p.m <= 64 && p.r % 16 == 0 && p.kg % 512 == 0) {
         if (p.r % 32 == 0) launch_skinny_nb<FP8, 2>(p, st);
         else launch_skinny_nb<FP8, 1>(p, st);
+        return hipGetLastError();
+    }
+    if (!FP8 && wide_fits(p)) {
+        const int64_t pairs = ((p.m + kWideM - 1) / kWideM) * (int64_t)p.g;
+        const int64_t blocks = (pairs + 7) / 8 * 8 * (p.r / kWideN);
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        const size_t lds = 2 * (size_t)kWideStage;
+        hipError_t e = hipFuncSetAttribute((const void*)proj_wide_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(proj_wide_kernel, dim3((unsigned)blocks), dim3(kWideWaves * 64), lds, st, p);
         return hipGetLastError();
     }
     if (p.r % kProjN != 0 || p.kg % kProjK != 0) return hipErrorInvalidValue;
