@@ -294,7 +294,7 @@ CAL_BYTES = 1 << 30              # calibration copy: 1 GiB read, 1 GiB written
 # (substrings) of one call
 FAMILY_SOURCES = {
     "attn": ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "sa_api.cpp", "sa_internal.hpp",
-             "sa_device.hpp"],
+             "sa_device.hpp", "lds_dma.hpp"],
     "kv_write": ["aux_kernels.hip", "sa_device.hpp"],
     "indexer": ["indexer.hip", "sa_device.hpp"],
     "proj": ["wo_proj.hip", "lds_dma.hpp", "sa_device.hpp"],

@@ -35,6 +35,7 @@
 //     bf16, optional inverse RoPE) runs here.
 #pragma once
 
+#include "lds_dma.hpp"
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -73,47 +74,6 @@ struct Geo {
 // vmcnt: a skipped row is loaded from an offset past the end of the buffer, for which the
 // buffer's range check returns zeros without a memory access, so it lands as a zero row (a
 // zero row can never turn a zero probability into a NaN).
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer load of 16 bytes per lane straight into LDS: lane i's bytes land at lds + 16 i
-// (M0 holds the LDS address). Written as inline assembly on purpose: the compiler's memory
-// model, seeing an LDS write whose completion it cannot order, would otherwise wait for
-// every such load in flight before each LDS read and each barrier, which serialises the
-// tile pipeline. Completion is tracked here with explicit vmcnt waits instead (wait_vmcnt),
-// and the "memory" clobber keeps the compiler from moving LDS accesses across the issue.
-// M0 is an operand ("{m0}"), so the compiler itself writes it and knows it is changed; the
-// s_nop covers the wait state between an M0 write and an LDS-DMA load.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
-// vector-memory loads (__syncthreads would also drain every tile gather in flight).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(SA_LDS const void* p) {
-    return (uint32_t)(uintptr_t)p;
-}
-
-// Buffer resource of one sequence's kv rows: base, no stride, `bytes` records (reads past
-// them return zeros), gfx9 default format word.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    i32x4 r;
-    r[0] = (int32_t)(uint32_t)a;
-    r[1] = (int32_t)(uint32_t)(a >> 32) & 0xffff;
-    r[2] = (int32_t)bytes;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// A buffer offset past every kv buffer (the host rejects kv buffers of 2^31 bytes or more,
-// and their sizes are multiples of 16).
-constexpr int kPastEnd = 0x7ffffff0;
-
 // Wave wid issues loads wid*kPer .. wid*kPer+kPer-1 of the tile; load j covers rows
 // j*kRowsPerInst .. +kRowsPerInst-1. All row indices are read before the first load issues.
 template <int D, int NW>
@@ -128,13 +88,13 @@ __device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_
     int rows[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) rows[j] = tidx[(wid * kPer + j) * G::kRowsPerInst + sub];
-    const uint32_t base = lds_addr(buf);
+    const uint32_t base = lds_byte_addr(buf);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int r0 = (wid * kPer + j) * G::kRowsPerInst;
         const int r = r0 + sub;
-        const int voff = rows[j] < 0 ? kPastEnd : rows[j] * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
-        dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
+        const int voff = rows[j] < 0 ? kBufferPastEnd : rows[j] * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
     }
 }
 
@@ -230,13 +190,13 @@ struct RawGather {
         for (int j = 0; j < kCodeLoads; ++j) rows[j] = tidx[2 * (wid * kCodeLoads + j) + sub];
         constexpr int kScRows = kTileKeys / NW;
         const int sc_row = tidx[wid * kScRows + (lane & (kScRows - 1))];
-        const uint32_t base = lds_addr(slot);
+        const uint32_t base = lds_byte_addr(slot);
 #pragma unroll
         for (int j = 0; j < kCodeLoads; ++j)
-            dma16(codes_rsrc, __builtin_amdgcn_readfirstlane(base + 2 * (wid * kCodeLoads + j) * D),
+            lds_dma16(codes_rsrc, __builtin_amdgcn_readfirstlane(base + 2 * (wid * kCodeLoads + j) * D),
                   max(rows[j], 0) * D + 16 * pc);
         if (lane < kScRows)
-            dma16(sc_rsrc, __builtin_amdgcn_readfirstlane(base + RawSlot<D>::kCodes + wid * kScRows * (D / 32)),
+            lds_dma16(sc_rsrc, __builtin_amdgcn_readfirstlane(base + RawSlot<D>::kCodes + wid * kScRows * (D / 32)),
                   max(sc_row, 0) * (D / 32));
     }
 };
@@ -427,13 +387,6 @@ struct KernelLds {
     static constexpr size_t kTiles = (size_t)kTileBufs * Geo<D>::kTileBytes + (size_t)kRawSlots * RawSlot<D>::kBytes;
 };
 
-// s_waitcnt on the vector-memory counter only; a compiler barrier for memory accesses too,
-// so LDS reads and writes of a landed tile stay behind it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
 
 // KG key groups: the NW waves form NW / KG head groups times KG key groups; the waves of
 // one key group take every KG-th tile of the item's index columns, so one query's keys are
@@ -500,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
 
     const uint8_t* kv_seq = p.kv + (int64_t)seq * p.kv_seq_stride_bytes;
     const uint8_t* sc_seq = FP8 ? p.kv_scale + (int64_t)seq * p.kv_scale_seq_stride : nullptr;
-    const i32x4 kv_rsrc = make_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
+    const i32x4 kv_rsrc = make_buffer_rsrc(kv_seq, (uint32_t)p.kv_rows * (uint32_t)(FP8 ? D : 2 * D));
 
     // ---- start-up, arranged so that its memory latencies overlap: the position and the
     // index loads go out first, then Q and the sink; the index stage is written as soon as
@@ -806,7 +759,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     };
 
     // fp8 storage: the rows' scale bytes
-    const i32x4 sc_rsrc = FP8 ? make_rsrc(sc_seq, (uint32_t)p.kv_rows * (uint32_t)(D / 32)) : kv_rsrc;
+    const i32x4 sc_rsrc = FP8 ? make_buffer_rsrc(sc_seq, (uint32_t)p.kv_rows * (uint32_t)(D / 32)) : kv_rsrc;
     for (int pass = 0;; ++pass) {
     if constexpr (FP8 && !kFp8Pipe) {
         // fp8 storage (d other than 512): one bf16 tile; the codes of the next tile are
@@ -865,18 +818,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             // the wave's tile's column indices, read before the waits (the valid-key mask is
             // formed after them, so the LDS read's latency hides behind the waits)
             const int tv = ti < ntiles ? istage[ti * kTileKeys + (lane & 31)] : -1;
-            wait_vmcnt<0>();
+            vmcnt_wait<0>();
             if constexpr (kFp8Pipe) {
-                lds_barrier();             // super tile su's codes; every wave done with su-1
+                lds_sync();             // super tile su's codes; every wave done with su-1
 #pragma unroll
                 for (int g = 0; g < KG; ++g) {
                     const int ti = su * KG + g;
                     if (ti < ntiles) convert_raw_fp8<D, NW>(raw(g), istage + ti * kTileKeys, tile(g), wid, lane);
                 }
-                lds_barrier();             // super tile su converted; its raw slots free
+                lds_sync();             // super tile su converted; its raw slots free
                 if (su + 1 < nsuper) gather_super(su + 1);
             } else {
-                lds_barrier();             // super tile su visible to all
+                lds_sync();             // super tile su visible to all
                 if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             }
             const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tv >= 0);
@@ -896,7 +849,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 pv(cur, pb, [](int) {});
             }
             if (!kFp8Pipe && NS == 1 && su + 1 < nsuper) {
-                lds_barrier();             // every wave is done with the super tile
+                lds_sync();             // every wave is done with the super tile
                 gather_super(su + 1);
             }
         }
@@ -917,10 +870,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             for (int j = 0; j < 3; ++j)
                 if (j < ntiles) RG::issue(kv_rsrc, sc_rsrc, istage + j * kTileKeys, raw(j), wid, lane);
             if (ntiles > 0) {
-                if (ntiles >= 3) wait_vmcnt<2 * RG::kLoads>();
-                else if (ntiles == 2) wait_vmcnt<RG::kLoads>();
-                else wait_vmcnt<0>();
-                lds_barrier();                 // tile 0's codes from every wave
+                if (ntiles >= 3) vmcnt_wait<2 * RG::kLoads>();
+                else if (ntiles == 2) vmcnt_wait<RG::kLoads>();
+                else vmcnt_wait<0>();
+                lds_sync();                 // tile 0's codes from every wave
                 convert_raw_fp8<D, NW>(raw(0), istage, tile(0), wid, lane);
             }
         } else {
@@ -947,17 +900,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 const int tv = tidx[lane & 31];
                 if constexpr (kFp8Pipe) {
                     using RG = RawGather<D, NW>;
-                    if (it + 2 < ntiles) wait_vmcnt<RG::kLoads>();
-                    else wait_vmcnt<0>();
+                    if (it + 2 < ntiles) vmcnt_wait<RG::kLoads>();
+                    else vmcnt_wait<0>();
                     // tile it converted by every wave, tile it+1's codes visible; the slot of
                     // tile it and the buffer of tile it-2 are free
-                    lds_barrier();
+                    lds_sync();
                     if (it + 3 < ntiles)
                         RG::issue(kv_rsrc, sc_rsrc, tidx + 3 * kTileKeys, raw((it + 3) % 3), wid, lane);
                 } else {
-                    if (it + 1 < ntiles) wait_vmcnt<PP::kLoadsPerWave>();
-                    else wait_vmcnt<0>();
-                    lds_barrier();         // tile it visible to all; buffer of tile it-2 free
+                    if (it + 1 < ntiles) vmcnt_wait<PP::kLoadsPerWave>();
+                    else vmcnt_wait<0>();
+                    lds_sync();         // tile it visible to all; buffer of tile it-2 free
                     if (it + kAh < ntiles)
                         gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
                 }

@@ -25,10 +25,13 @@ constexpr int kBufferPastEnd = 0x7ffffff0;
 __device__ __forceinline__ uint32_t lds_byte_addr(SA_LDS const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // 16 bytes per lane from the buffer straight into LDS at m0 + 16 lane, and 4 bytes per lane
-// at m0 + 4 lane. Inline assembly with a "memory" clobber: completion is tracked with
-// explicit vmcnt waits (vmcnt_wait), not by the compiler, which would otherwise drain every
-// such load before each LDS access. M0 is an operand, so the compiler writes it and knows
-// it is changed; the s_nop covers the wait state between an M0 write and the load.
+// at m0 + 4 lane (M0 holds the LDS address). Written as inline assembly on purpose: the
+// compiler's memory model, seeing an LDS write whose completion it cannot order, would wait
+// for every such load in flight before each LDS read and each barrier, which serialises a
+// load pipeline. Completion is tracked with explicit vmcnt waits instead (vmcnt_wait), and
+// the "memory" clobber keeps the compiler from moving LDS accesses across the issue. M0 is an
+// operand ("{m0}"), so the compiler itself writes it and knows it is changed; the s_nop
+// covers the wait state between an M0 write and an LDS-DMA load.
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds, int voff) {
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
@@ -38,8 +41,9 @@ __device__ __forceinline__ void lds_dma4(i32x4 rsrc, uint32_t lds, int voff) {
                  :: "v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
-// Wait until at most N of this wave's vector-memory loads are in flight (they complete in
-// issue order for this count).
+// Wait until at most N of this wave's vector-memory operations are in flight (they complete
+// in issue order for this count); also a compiler barrier for memory accesses, so LDS reads
+// and writes of landed data stay behind it.
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -61,7 +65,8 @@ __device__ __forceinline__ void vmcnt_wait_groups(int n) {
     }
 }
 
-// Workgroup barrier that waits for this wave's LDS operations only, not for its loads.
+// Workgroup barrier that waits for this wave's LDS operations only, not for its loads
+// (__syncthreads would also drain every direct-to-LDS load in flight).
 __device__ __forceinline__ void lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
