@@ -140,10 +140,7 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // merging their partial results in LDS, which saves the f32 partials (one per head and
     // split, as large as 2 KB per head) and the combine kernel. Measured on 64 queries x 128 heads x 640 columns: 41.5 us with
     // two splits, 36.7 us with two key groups. The most key groups that keep one round of
-    // workgroups on the GPU and leave no group without tiles. (Without splits, a short key
-    // list does better on one wave per head block: 32 queries x 64 heads x 128 columns took
-    // 12.9 us that way and 13.6 us with four key groups, the merge costing what the shorter
-    // loop saved.)
+    // workgroups on the GPU and leave no group without tiles.
     if (splits > 1 && a->d == 512 && pl.hpw == 1) {
         for (int kg = bf16_rows ? 4 : 2; kg >= 2; kg /= 2) {
             if (nq * blocks_for(4 / kg) <= cus && ntiles >= kg) {
@@ -154,6 +151,14 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
                 break;
             }
         }
+    } else if (wgs < cus && ntiles >= 2 && a->d == 512 && pl.hpw == 1 && nq * blocks_for(2) <= cus) {
+        // A short list that leaves compute units idle: two key groups of two waves on the
+        // same heads. Measured on 32 queries x 64 heads x 128 columns: 11.65 us against 12.0
+        // with one two-wave group (four key groups: 12.0), and with fp8 storage 12.4 against
+        // 15.4 us (four waves convert each tile).
+        pl.kg = 2;
+        pl.nw = 4;
+        pl.head_blocks = blocks_for(2);
     }
     pl.h_pad = pl.head_blocks * pl.nw / pl.kg * pl.hpw * kHeadsPerWave;
     // a workgroup stages at most kMaxColsPerSplit index columns (kMaxColsFp8Pipe for fp8

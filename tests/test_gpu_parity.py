@@ -264,18 +264,28 @@ def test_late_large_scores(sa, boost, where, fmt):
     (86, 1, 2, 48, 60, 50, 1.0, 0.0),       # every column skipped
     (87, 1, 3, 64, 300, 200, 0.0, 4.0),     # a late large score: the second key pass
     (88, 2, 1, 64, 1200, 1024, 0.05, 4.0),  # decode-shaped: two key groups, merge and second pass
+    # enough workgroups to fill the GPU and rows named only a few times each: the pipelined
+    # loop with in-kernel conversion (one and four waves), also with the second pass
+    (89, 4, 64, 16, 2000, 200, 0.1, 0.0),
+    (90, 2, 128, 64, 3000, 300, 0.2, 0.0),
+    (91, 2, 130, 64, 3000, 300, 0.1, 4.0),
 ])
 def test_fp8_pipeline(sa, seed, b, s, h, rows, topk, hole, boost):
-    """fp8 storage at d = 512 (codes and scales gathered into raw slots two tiles ahead,
-    converted to bf16 tiles between the two products) against the oracle on the
-    round-tripped rows."""
+    """fp8 storage at d = 512 converted inside the kernel (codes and scales gathered into raw
+    slots ahead of the tile they fill and converted to bf16 tiles between the products, in the
+    pipelined loop or, for short lists that leave compute units idle, by the key groups)
+    against the oracle on the round-tripped rows."""
     _say("fp8 pipeline", seed, b, s, h, rows, topk, hole, boost)
     q, kv, sink, idx = W.rand_problem(seed, b, s, h, 512, rows, topk, hole, False)
     if boost:
+        # a late row aligned with head 2's query: its score (about boost/2 * 0.8 * 512 raw,
+        # 50 and more in log2 units) runs far past the first tile's reference, while its
+        # values stay at +-boost/2 (P is rounded to bf16 for the PV product, an error of up to
+        # 2^-9 of the largest |value| per output element)
         for t in range(s):
             col = topk - 5
             if idx[0, t, col] >= 0:
-                kv[0, int(idx[0, t, col])] = (q[0, t, 2].float() * boost).to(torch.bfloat16)
+                kv[0, int(idx[0, t, col])] = (torch.sign(q[0, t, 2].float()) * (boost / 2)).to(torch.bfloat16)
     scale = float(np.float32(512 ** -0.5))
     codes, kv_scale = sa.quant_kv_fp8(kv.cuda(), want=("codes", "scales"))
     kv_ref = oracle.act_quant(u16(kv).reshape(-1, 512))[0].reshape(kv.shape)
