@@ -430,14 +430,25 @@ __global__ __launch_bounds__(256) void proj_tiled_kernel(const ProjParams p) {
 // ------------------------------------------------------------------ wide tiles (bf16)
 // Many tokens, bf16 weights: 256 rows of W x 256 tokens per workgroup of 8 waves (two per
 // SIMD, so one wave's memory stalls are covered by the other's matrix work), each wave 64
-// rows x 128 tokens. k advances in steps of 64: the step's 512 rows of 128 bytes are copied
-// straight into LDS by direct-to-LDS loads (8 whole rows per load instruction), two steps in
-// LDS, the next one loading while the current one is multiplied. Rows are stored with their
-// 16-byte pieces XOR-ed by (row >> 1) & 7 (conflict-free operand reads, as proj_lds).
-constexpr int kWideN = 256, kWideM = 256, kWideK = 64, kWideWaves = 8;
-constexpr int kWideRowBytes = kWideK * 2;                            // 128: 8 pieces
-constexpr int kWideStage = (kWideN + kWideM) * kWideRowBytes;       // 64 KB
-constexpr int kWideLoads = (kWideN + kWideM) / 8 / kWideWaves;      // load instructions per wave and step
+// rows x 128 tokens. k advances in steps of kWideK: the step's 512 rows are copied straight
+// into LDS by direct-to-LDS loads of whole rows, kWideStages steps in LDS, the next ones
+// loading while the current one is multiplied.
+constexpr int kWideN = 256, kWideM = 256, kWideK = 64, kWideWaves = 8, kWideStages = 2;
+constexpr int kWideRowBytes = kWideK * 2;                            // bytes of one staged row
+constexpr int kWidePieces = kWideRowBytes / 16;                      // 16-byte pieces per row
+constexpr int kWideRowsPerLoad = 64 / kWidePieces;
+constexpr int kWideStage = (kWideN + kWideM) * kWideRowBytes;
+constexpr int kWideLoads = (kWideN + kWideM) / kWideRowsPerLoad / kWideWaves;   // per wave and step
+static_assert(kWidePieces == 4 || kWidePieces == 8, "rows of 64 or 128 bytes");
+
+// Position of piece c of staged row r: with 8 pieces (128-byte rows, two rows per bank
+// cycle) XOR (r >> 1) & 7, with 4 pieces (64-byte rows, four per bank cycle) XOR (r >> 2) & 3;
+// either way the 16 rows of an operand read (8 at piece c, 8 at the next) hit 16 distinct
+// bank groups.
+__device__ __forceinline__ int wide_lds(int r, int c) {
+    const int x = kWidePieces == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+    return r * kWideRowBytes + ((c ^ x) << 4);
+}
 
 __global__ __launch_bounds__(kWideWaves * 64) void proj_wide_kernel(const ProjParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
@@ -456,23 +467,24 @@ __global__ __launch_bounds__(kWideWaves * 64) void proj_wide_kernel(const ProjPa
     const i32x4 w_rsrc = make_buffer_rsrc(p.w + ((int64_t)gg * p.r + n_base) * p.kg, (uint32_t)(kWideN * p.kg * 2));
     const i32x4 t_rsrc = make_buffer_rsrc(p.o + (int64_t)m_base * p.o_stride + (int64_t)gg * p.kg,
                                           (uint32_t)(((int64_t)(m_rows - 1) * p.o_stride + p.kg) * 2));
-    // load j of this wave fills rows 8 I .. 8 I + 7 of the stage (I = wid * kWideLoads + j;
-    // stage rows 0 .. 255 are W, 256 .. 511 tokens): lane fills piece position lane & 7 of
-    // row lane >> 3 from the global piece stored there
+    // load j of this wave fills the kWideRowsPerLoad rows from R = I * kWideRowsPerLoad on
+    // (I = wid * kWideLoads + j; stage rows 0 .. 255 are W, 256 .. 511 tokens): lane fills
+    // piece position lane % kWidePieces of row R + lane / kWidePieces from the global piece
+    // stored there
     int off[kWideLoads];
 #pragma unroll
     for (int j = 0; j < kWideLoads; ++j) {
-        const int row = 8 * (wid * kWideLoads + j) + (lane >> 3);
-        const int pc = (lane & 7) ^ ((row >> 1) & 7);
-        off[j] = row < kWideN ? row * p.kg * 2 + 16 * pc
-                              : min(row - kWideN, m_rows - 1) * (int)(p.o_stride * 2) + 16 * pc;
+        const int row = kWideRowsPerLoad * (wid * kWideLoads + j) + lane / kWidePieces;
+        const int pos = (wide_lds(row, lane % kWidePieces) - row * kWideRowBytes) >> 4;   // = piece stored there
+        off[j] = row < kWideN ? row * p.kg * 2 + 16 * pos
+                              : min(row - kWideN, m_rows - 1) * (int)(p.o_stride * 2) + 16 * pos;
     }
     auto issue = [&](int kt) {
-        const uint32_t base = lds_byte_addr(smem + (kt & 1) * kWideStage);
+        const uint32_t base = lds_byte_addr(smem + (kt % kWideStages) * kWideStage);
 #pragma unroll
         for (int j = 0; j < kWideLoads; ++j) {
             const int I = wid * kWideLoads + j;                  // uniform: W or token rows
-            lds_dma16(I < kWideN / 8 ? w_rsrc : t_rsrc, base + I * 1024, off[j] + kt * kWideRowBytes);
+            lds_dma16(I < kWideN / kWideRowsPerLoad ? w_rsrc : t_rsrc, base + I * 1024, off[j] + kt * kWideRowBytes);
         }
     };
     f32x4 acc[4][8];
@@ -481,22 +493,23 @@ __global__ __launch_bounds__(kWideWaves * 64) void proj_wide_kernel(const ProjPa
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = p.kg / kWideK;
-    issue(0);
+    for (int kt = 0; kt < kWideStages - 1 && kt < nk; ++kt) issue(kt);
     for (int kt = 0; kt < nk; ++kt) {
-        vmcnt_wait<0>();
+        // steps kt .. kt + stages - 2 are in flight: wait until only the later ones are
+        vmcnt_wait_groups<kWideLoads, kWideStages - 2>(min(kWideStages - 2, nk - 1 - kt));
         lds_sync();                                  // step kt landed; step kt-1 done by all
-        if (kt + 1 < nk) issue(kt + 1);
-        SA_LDS const uint8_t* wt = smem + (kt & 1) * kWideStage;
+        if (kt + kWideStages - 1 < nk) issue(kt + kWideStages - 1);
+        SA_LDS const uint8_t* wt = smem + (kt % kWideStages) * kWideStage;
         SA_LDS const uint8_t* ot = wt + kWideN * kWideRowBytes;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < kWideK / 32; ++kk) {
             u32x4 a[4], b[8];
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-                a[nb] = *(SA_LDS const u32x4*)(wt + proj_lds(wn * 64 + nb * 16 + l16, 4 * kk + gq));
+                a[nb] = *(SA_LDS const u32x4*)(wt + wide_lds(wn * 64 + nb * 16 + l16, 4 * kk + gq));
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb)
-                b[mb] = *(SA_LDS const u32x4*)(ot + proj_lds(wm * 128 + mb * 16 + l16, 4 * kk + gq));
+                b[mb] = *(SA_LDS const u32x4*)(ot + wide_lds(wm * 128 + mb * 16 + l16, 4 * kk + gq));
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -539,7 +552,7 @@ static hipError_t launch_proj(const ProjParams& p, hipStream_t st) {
         const int64_t pairs = ((p.m + kWideM - 1) / kWideM) * (int64_t)p.g;
         const int64_t blocks = (pairs + 7) / 8 * 8 * (p.r / kWideN);
         if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-        const size_t lds = 2 * (size_t)kWideStage;
+        const size_t lds = kWideStages * (size_t)kWideStage;
         hipError_t e = hipFuncSetAttribute((const void*)proj_wide_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(proj_wide_kernel, dim3((unsigned)blocks), dim3(kWideWaves * 64), lds, st, p);
