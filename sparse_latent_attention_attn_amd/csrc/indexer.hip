@@ -3,9 +3,9 @@
 //   * index_scores_kernel: score[t] = sum_h w_h relu(q_h . k_t) per query, on bf16 MFMA with
 //     f32 accumulation; positions the query cannot see (and, for the second level, positions
 //     outside the candidate mask) are -inf;
-//   * index_topk_kernel: per query, the topk best finite scores by a radix select on LDS,
-//     listed in position order (ties: the lower position first), shifted by the offset and
-//     padded with -1;
+//   * index_topk_kernel: per query, the topk best finite scores by a bitwise threshold
+//     search over keys held in registers, listed in position order (ties: the lower position
+//     first), shifted by the offset and padded with -1;
 //   * candidate_blocks_kernel: per query, block maxima, the newest visible block pinned, the
 //     best blocks kept by the same radix select, expanded to a position mask.
 #include "sa_device.hpp"
@@ -354,25 +354,6 @@ __device__ void radix_threshold(SA_LDS const uint32_t* keys, int n, int k, SA_LD
     ties = rem;
 }
 
-// keys[i] = score_key(src[i]) for i < n, with 8 loads in flight per thread (a loop of single
-// loads would wait one memory round trip per iteration).
-template <int NT>
-__device__ __forceinline__ void load_keys(const float* src, int n, SA_LDS uint32_t* keys) {
-    for (int i0 = 0; i0 < n; i0 += 8 * NT) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * NT + (int)threadIdx.x;
-            v[u] = i < n ? src[i] : -INFINITY;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * NT + (int)threadIdx.x;
-            if (i < n) keys[i] = score_key(v[u]);
-        }
-    }
-}
-
 // Number of non-zero keys among keys[0 .. n) (the selectable ones), in every thread.
 template <int NT>
 __device__ __forceinline__ int count_selectable(SA_LDS const uint32_t* keys, int n, SA_LDS int* tot) {
@@ -425,31 +406,116 @@ __device__ __forceinline__ void select_in_order(SA_LDS const uint32_t* keys, int
 }
 
 // ------------------------------------------------------------------ top-k lists
-// One workgroup per query: the query's scores become keys in LDS; the k-th largest is found
-// by a 4-pass radix select; one ordered pass then lists the chosen positions in ascending
-// order (which is also the order the page re-sorts them into), shifted by the offset.
-// NT threads: 256 for short lists, 1024 for long ones.
-template <int NT>
-__global__ __launch_bounds__(NT) void index_topk_kernel(const IdxParams p) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-    SA_LDS uint32_t* hist = (SA_LDS uint32_t*)smem_raw;          // 256
-    SA_LDS int* misc = (SA_LDS int*)(hist + 256);                // 16
-    SA_LDS uint32_t* keys = (SA_LDS uint32_t*)(misc + 16);       // n_pos
-    const int tid = threadIdx.x;
-    const int64_t qi = blockIdx.x;
+// W waves per query hold its scores as keys in registers: wave w, row j, lane l holds
+// position (w * J + j) * 64 + l (positions past n_pos hold key 0, as -inf does). The k-th
+// largest key is built from the top bit down: a bit stays set when at least k keys are at or
+// above the candidate; a count is the popcount of one compare ballot per row, summed over the
+// query's waves through LDS. The search ends early at a candidate with exactly k keys at or
+// above it. One ordered pass over the same registers then lists the chosen positions in
+// ascending order (which is also the order the page re-sorts them into), shifted by the
+// offset; among keys equal to the threshold the lower positions are taken first. W = 1: four
+// queries per workgroup, one per wave, with no barriers at all.
+template <int W, int J>
+__global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const IdxParams p) {
+    __shared__ int red[2][W];                       // per-wave partial sums, two generations
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t qi = W == 1 ? (int64_t)blockIdx.x * 4 + wid : (int64_t)blockIdx.x;
+    if (W == 1 && qi >= (int64_t)p.b * p.s) return;             // no barriers when W = 1
+    const int w = W == 1 ? 0 : wid;                              // wave within the query
     const int n = (int)(qi / p.s), t = (int)(qi % p.s);
     const float* sc = p.scores + (int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos;
-    load_keys<NT>(sc, p.n_pos, keys);
-    __syncthreads();
-    int32_t* out = p.idx + (int64_t)n * p.idx_seq_stride + (int64_t)t * p.idx_row_stride;
-    const int k = min(p.topk, count_selectable<NT>(keys, p.n_pos, misc));
-    if (k > 0) {
-        uint32_t thr;
-        int ties;
-        radix_threshold<NT>(keys, p.n_pos, k, hist, misc, thr, ties);
-        select_in_order<NT>(keys, p.n_pos, thr, ties, misc, [&](int i, int r) { out[r] = i + p.offset; });
+    const int base = w * J * 64;
+    // every load issued before the first use (addresses clamped rather than branched around)
+    float v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = sc[min(base + 64 * j + lane, p.n_pos - 1)];
+    uint32_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) key[j] = score_key(v[j]) & (base + 64 * j + lane < p.n_pos ? ~0u : 0u);
+    // Sum of a wave-uniform value over the query's waves (the same in every wave), and the
+    // part of waves before this one. Consecutive calls alternate between the two rows of
+    // `red`: a wave writes row g only after every wave has passed the barrier of the call
+    // before, i.e. has finished reading row g two calls back.
+    int gen = 0;
+    auto block_sum = [&](int v, int& before) {
+        before = 0;
+        if constexpr (W == 1) {
+            return v;
+        } else {
+            if (lane == 0) red[gen][wid] = v;
+            __syncthreads();
+            int tot = 0;
+#pragma unroll
+            for (int u = 0; u < W; ++u) {
+                const int c = red[gen][u];
+                tot += c;
+                before += u < wid ? c : 0;
+            }
+            gen ^= 1;
+            return tot;
+        }
+    };
+    auto count_ge = [&](uint32_t c) {
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) cnt += __builtin_popcountll(__ballot(key[j] >= c));
+        int before;
+        return block_sum(cnt, before);
+    };
+    const int selectable = count_ge(1u);
+    const int k = min(p.topk, selectable);
+    // chosen: key > thr, or key == thr among the first `ties` such positions
+    uint32_t thr = 0;
+    int ties = 0;
+    if (k > 0 && k < selectable) {
+        uint32_t lo = 0;                                         // count_ge(lo) >= k throughout
+        bool exact = false;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = lo | (1u << bit);
+            const int cnt = count_ge(c);
+            if (cnt >= k) {
+                lo = c;
+                if (cnt == k) { exact = true; break; }
+            }
+        }
+        if (exact) {
+            thr = lo - 1;                                        // the k keys >= lo (lo >= 1)
+        } else {
+            // lo is the k-th largest key; the keys above it are fewer than k
+            thr = lo;
+            ties = k - (lo == 0xffffffffu ? 0 : count_ge(lo + 1));
+        }
     }
-    for (int j = k + tid; j < p.topk; j += NT) out[j] = -1;
+    // ties met before this wave's positions
+    int tie_before = 0;
+    if (ties > 0) {
+        int eq = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) eq += __builtin_popcountll(__ballot(key[j] == thr));
+        block_sum(eq, tie_before);
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    auto row_sel = [&](int j, int& tie_seen) {
+        if (ties == 0) return (uint64_t)__ballot(key[j] > thr);
+        const uint64_t beq = __ballot(key[j] == thr);
+        const bool sel = key[j] > thr || (key[j] == thr && tie_seen + __builtin_popcountll(beq & below) < ties);
+        tie_seen += __builtin_popcountll(beq);
+        return (uint64_t)__ballot(sel);
+    };
+    int sel_w = 0, tie_seen = tie_before;
+#pragma unroll
+    for (int j = 0; j < J; ++j) sel_w += __builtin_popcountll(row_sel(j, tie_seen));
+    int rank;
+    block_sum(sel_w, rank);
+    int32_t* out = p.idx + (int64_t)n * p.idx_seq_stride + (int64_t)t * p.idx_row_stride;
+    tie_seen = tie_before;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const uint64_t bs = row_sel(j, tie_seen);
+        if ((bs >> lane) & 1) out[rank + __builtin_popcountll(bs & below)] = base + 64 * j + lane + p.offset;
+        rank += __builtin_popcountll(bs);
+    }
+    for (int c = k + w * 64 + lane; c < p.topk; c += W * 64) out[c] = -1;
 }
 
 // ------------------------------------------------------------------ candidate blocks
@@ -577,18 +643,26 @@ hipError_t launch_index_scores(const IdxParams& p, hipStream_t st) {
     }
 }
 
-hipError_t launch_index_topk(const IdxParams& p, hipStream_t st) {
-    const size_t lds = (256 + 16) * 4 + (size_t)p.n_pos * 4;
+template <int W, int J>
+static hipError_t launch_topk_wj(const IdxParams& p, hipStream_t st) {
     const int64_t nq = (int64_t)p.b * p.s;
-    if (lds > 160 * 1024 || nq > 0x7fffffff) return hipErrorInvalidValue;
-    // long lists get four times the threads: the passes over the keys dominate there
-    const bool wide = p.n_pos > 4096;
-    const void* k = wide ? (const void*)index_topk_kernel<1024> : (const void*)index_topk_kernel<256>;
-    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    if (wide) hipLaunchKernelGGL(index_topk_kernel<1024>, dim3((unsigned)nq), dim3(1024), lds, st, p);
-    else hipLaunchKernelGGL(index_topk_kernel<256>, dim3((unsigned)nq), dim3(256), lds, st, p);
+    const int64_t grid = W == 1 ? (nq + 3) / 4 : nq;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((index_topk_kernel<W, J>), dim3((unsigned)grid), dim3(W == 1 ? 256 : W * 64), 0, st, p);
     return hipGetLastError();
+}
+
+// keys per query: up to 2048 in one wave, 8192 in four, 32768 in sixteen
+hipError_t launch_index_topk(const IdxParams& p, hipStream_t st) {
+    const int n = p.n_pos;
+    if (n <= 512) return launch_topk_wj<1, 8>(p, st);
+    if (n <= 1024) return launch_topk_wj<1, 16>(p, st);
+    if (n <= 2048) return launch_topk_wj<1, 32>(p, st);
+    if (n <= 4096) return launch_topk_wj<4, 16>(p, st);
+    if (n <= 8192) return launch_topk_wj<4, 32>(p, st);
+    if (n <= 16384) return launch_topk_wj<16, 16>(p, st);
+    if (n <= 32768) return launch_topk_wj<16, 32>(p, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st) {

@@ -72,6 +72,8 @@ def _check_structure(idx, scores, topk, offset):
     (3, 1, 33, 64, 128, 129, 1, 40, False),
     (4, 2, 4, 32, 256, 1000, 4, 100, True),
     (5, 4, 1, 64, 64, 5000, 4, 512, False),
+    (6, 2, 3, 32, 64, 3000, 1, 700, True),
+    (7, 1, 2, 16, 64, 20000, 1, 2000, True),
 ])
 def test_indexer_against_oracle(sa, seed, b, s, h, d, n_pos, ratio, topk, integer):
     _say("indexer", seed, b, s, h, d, n_pos, ratio, topk, "integer" if integer else "random")
