@@ -28,7 +28,7 @@ __device__ __forceinline__ int visible_positions(int pos, int ratio, int n_pos) 
 // position and 4 heads, so the weighted head sum is in-lane work plus two exchanges across
 // the lane groups. A wave takes QPW queries of one sequence (sharing every K load) and
 // kChunk positions; a workgroup is 4 such waves.
-constexpr int kScoreChunk = 256;
+constexpr int kScoreChunk = 256, kScoreAhead = 2;
 
 template <int D, int HB, int QPW>
 __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
@@ -75,11 +75,12 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
         for (int kk = 0; kk < KS; ++kk) kb[kk] = *(const u32x4*)(kseq + (int64_t)pp * D + 32 * kk + 8 * g);
     };
     const int vend = min(cend, vmax);                            // blocks with a visible position
-    // one 16-position block: its K operands are in `cur`; the next block's go to `nxt`
+    // one 16-position block: its K operands are in `cur`; those of the block kScoreAhead
+    // blocks later go to `nxt` (the buffer the previous block used)
     auto step = [&](int pb, const u32x4 (&cur)[KS], u32x4 (&nxt)[KS]) {
         const int pp = pb + l16;
         const bool any = pb < vend;
-        if (any && pb + 16 < vend) load_k(pb + 16, nxt);
+        if (any && pb + 16 * kScoreAhead < vend) load_k(pb + 16 * kScoreAhead, nxt);
 #pragma unroll
         for (int j = 0; j < QPW; ++j) {
             float part = 0.0f;
@@ -107,11 +108,16 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
             }
         }
     };
-    u32x4 ka[KS], kb[KS];
-    if (c0 < vend) load_k(c0, ka);
-    for (int pb = c0; pb < cend; pb += 32) {
-        step(pb, ka, kb);
-        if (pb + 16 < cend) step(pb + 16, kb, ka);
+    // a ring of kScoreAhead + 1 operand buffers, kScoreAhead blocks of loads in flight
+    constexpr int NBUF = kScoreAhead + 1;
+    u32x4 kr[NBUF][KS];
+#pragma unroll
+    for (int j = 0; j < kScoreAhead; ++j)
+        if (c0 + 16 * j < vend) load_k(c0 + 16 * j, kr[j]);
+    for (int pb = c0; pb < cend; pb += 16 * NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u)
+            if (pb + 16 * u < cend) step(pb + 16 * u, kr[u], kr[(u + kScoreAhead) % NBUF]);
     }
 }
 
