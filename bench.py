@@ -296,7 +296,7 @@ FAMILY_SOURCES = {
     "attn": ["attn_fwd_kernel.hpp", "attn_fwd.hip", "attn_fwd_wide.hip", "sa_api.cpp", "sa_internal.hpp",
              "sa_device.hpp", "lds_dma.hpp"],
     "kv_write": ["aux_kernels.hip", "sa_device.hpp"],
-    "indexer": ["indexer.hip", "sa_device.hpp"],
+    "indexer": ["indexer.hip", "lds_dma.hpp", "sa_device.hpp"],
     "proj": ["wo_proj.hip", "lds_dma.hpp", "sa_device.hpp"],
 }
 FAMILY_KERNELS = {

@@ -8,6 +8,7 @@
 //     first), shifted by the offset and padded with -1;
 //   * candidate_blocks_kernel: per query, block maxima, the newest visible block pinned, the
 //     best blocks kept by the same radix select, expanded to a position mask.
+#include "lds_dma.hpp"
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -22,34 +23,69 @@ __device__ __forceinline__ int visible_positions(int pos, int ratio, int n_pos) 
     return v < n_pos ? (int)v : n_pos;
 }
 
+// Row t of sequence n of a [b][s][n_pos] array of `bytes_per`-byte elements as a buffer:
+// stores at an offset past its end are dropped and loads there return zero, so lanes that
+// have nothing to store or load need no branch (a branch around a memory operation makes
+// the compiler's wait counts assume the worst on both paths, which in a pipelined loop
+// means waiting for every load in flight). Rows of dead queries (t >= s) get no records.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t score_row(const void* base, int64_t seq_stride, int n, int t,
+                                                            int s, int n_pos, int bytes_per) {
+    const uint8_t* row = (const uint8_t*)base + ((int64_t)n * seq_stride + (int64_t)min(t, s - 1) * n_pos) * bytes_per;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, t < s ? n_pos * bytes_per : 0, 0x00020000);
+}
+
+__device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t row, int pp, bool on, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(f32_bits(v), row, on ? pp * 4 : kBufferPastEnd, 0, 0);
+}
+
 // S[head][position] = Q . K^T on v_mfma_f32_16x16x32_bf16: Q is the A operand (rows = 16
 // heads, held in registers), K the B operand (columns = 16 positions, loaded straight from
 // memory, one 16-byte piece per lane and k-step). In the accumulator each lane holds one
 // position and 4 heads, so the weighted head sum is in-lane work plus two exchanges across
 // the lane groups. A wave takes QPW queries of one sequence (sharing every K load) and
-// kChunk positions; a workgroup is 4 such waves.
-constexpr int kScoreChunk = 256, kScoreAhead = 2;
+// kScoreChunk positions, with the keys of kScoreAhead blocks of 16 positions in flight; a
+// workgroup is 4 such waves. CAND: positions outside the candidate mask score -inf (its
+// bytes are loaded with the keys).
+constexpr int kScoreChunk = 256, kScoreAhead = 3;
 
-template <int D, int HB, int QPW>
+template <int D, int HB, int QPW, bool CAND>
 __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
     constexpr int KS = D / 32;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    // the wave index in a scalar register: the buffer resources built from it below must be
+    // uniform (a resource in vector registers costs a loop around every access)
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int groups = (p.s + QPW - 1) / QPW;                   // query groups per sequence
     const int64_t wave = (int64_t)blockIdx.x * 4 + wid;
     if (wave >= (int64_t)p.b * groups) return;                  // no barriers in this kernel
     const int n = (int)(wave / groups);
     const int t0 = (int)(wave % groups) * QPW;
-    const int c0 = blockIdx.y * kScoreChunk;
+    // chunks staggered by sequence: the waves in flight together then read at different
+    // offsets of their sequences' keys rather than all at the same one (4 MB apart at 16384
+    // positions; 79 -> 75 us on 64 sequences x 16384 positions)
+    const int c0 = (int)((blockIdx.y + (uint32_t)n * 7u) % gridDim.y) * kScoreChunk;
     const int cend = min(p.n_pos, c0 + kScoreChunk);
 
     int vis[QPW];
     int vmax = 0;
+    __amdgpu_buffer_rsrc_t srow[QPW], crow[QPW];
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
         const bool live = t0 + j < p.s;
         vis[j] = live ? visible_positions(p.pos[(int64_t)n * p.pos_seq_stride + t0 + j], p.ratio, p.n_pos) : 0;
         vmax = max(vmax, vis[j]);
+        srow[j] = score_row(p.scores, p.scores_seq_stride, n, t0 + j, p.s, p.n_pos, 4);
+        if constexpr (CAND) crow[j] = score_row(p.cand, p.cand_seq_stride, n, t0 + j, p.s, p.n_pos, 1);
+    }
+    const int vend = min(cend, vmax);                            // blocks with a visible position
+    if (vend <= c0) {
+        // nothing visible in this chunk: -inf throughout, no keys needed
+        for (int pb = c0; pb < cend; pb += 16) {
+            const int pp = pb + l16;
+#pragma unroll
+            for (int j = 0; j < QPW; ++j) store_score(srow[j], pp, g == 0 && pp < cend, -INFINITY);
+        }
+        return;
     }
     const uint16_t* kseq = p.k + (int64_t)n * p.k_seq_stride;
     // Q of each query: A operand of (head block mb, k-step kk): head 16 mb + l16, d 32 kk + 8 g
@@ -69,18 +105,25 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
             for (int r = 0; r < 4; ++r) wv[j][mb][r] = ww[16 * mb + 4 * g + r];
         }
     }
-    auto load_k = [&](int pb, u32x4 (&kb)[KS]) {
-        const int pp = min(pb + l16, p.n_pos - 1);
+    // Keys (and candidate bytes) of block pb: positions past the last visible one re-read it,
+    // so every block issues the same loads.
+    const int klast = vend - 1;
+    auto load_blk = [&](int pb, u32x4 (&kb)[KS], uint32_t (&cb)[QPW]) {
+        const int pp = min(pb + l16, klast);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) kb[kk] = *(const u32x4*)(kseq + (int64_t)pp * D + 32 * kk + 8 * g);
+        if constexpr (CAND) {
+#pragma unroll
+            for (int j = 0; j < QPW; ++j) cb[j] = __builtin_amdgcn_raw_buffer_load_b8(crow[j], pp, 0, 0);
+        }
     };
-    const int vend = min(cend, vmax);                            // blocks with a visible position
-    // one 16-position block: its K operands are in `cur`; those of the block kScoreAhead
-    // blocks later go to `nxt` (the buffer the previous block used)
-    auto step = [&](int pb, const u32x4 (&cur)[KS], u32x4 (&nxt)[KS]) {
+    // one 16-position block: its operands are in (cur, ccur); those of the block kScoreAhead
+    // blocks later go to (nxt, cnxt), the buffers the previous block used
+    auto step = [&](int pb, const u32x4 (&cur)[KS], const uint32_t (&ccur)[QPW], u32x4 (&nxt)[KS],
+                    uint32_t (&cnxt)[QPW]) {
+        load_blk(pb + 16 * kScoreAhead, nxt, cnxt);
         const int pp = pb + l16;
-        const bool any = pb < vend;
-        if (any && pb + 16 * kScoreAhead < vend) load_k(pb + 16 * kScoreAhead, nxt);
+        const bool any = pb < vend;                              // wave-uniform
 #pragma unroll
         for (int j = 0; j < QPW; ++j) {
             float part = 0.0f;
@@ -100,25 +143,23 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
                     for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
                 part = sum_xor32(sum_xor16(part));
             }
-            const int t = t0 + j;
-            if (g == 0 && t < p.s && pp < cend) {
-                bool keep = pp < vis[j];
-                if (keep && p.cand) keep = p.cand[(int64_t)n * p.cand_seq_stride + (int64_t)t * p.n_pos + pp] != 0;
-                p.scores[(int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos + pp] = keep ? part : -INFINITY;
-            }
+            bool keep = pp < vis[j];
+            if constexpr (CAND) keep = keep && ccur[j] != 0;
+            store_score(srow[j], pp, g == 0 && pp < cend, keep ? part : -INFINITY);
         }
     };
-    // a ring of kScoreAhead + 1 operand buffers, kScoreAhead blocks of loads in flight
+    // A ring of kScoreAhead + 1 operand buffers over the chunk's blocks, fully unrolled:
+    // straight-line code, so the compiler's wait before each block counts exactly the loads
+    // issued after it (a loop back edge would make it wait for all of them). Steps past the
+    // end of a short last chunk load clamped keys and store nothing.
     constexpr int NBUF = kScoreAhead + 1;
     u32x4 kr[NBUF][KS];
+    uint32_t cr[NBUF][QPW];
 #pragma unroll
-    for (int j = 0; j < kScoreAhead; ++j)
-        if (c0 + 16 * j < vend) load_k(c0 + 16 * j, kr[j]);
-    for (int pb = c0; pb < cend; pb += 16 * NBUF) {
+    for (int j = 0; j < kScoreAhead; ++j) load_blk(c0 + 16 * j, kr[j], cr[j]);
 #pragma unroll
-        for (int u = 0; u < NBUF; ++u)
-            if (pb + 16 * u < cend) step(pb + 16 * u, kr[u], kr[(u + kScoreAhead) % NBUF]);
-    }
+    for (int u = 0; u < kScoreChunk / 16; ++u)
+        step(c0 + 16 * u, kr[u % NBUF], cr[u % NBUF], kr[(u + kScoreAhead) % NBUF], cr[(u + kScoreAhead) % NBUF]);
 }
 
 // The same scores for many queries of one sequence (prefill): a workgroup of 4 waves takes
@@ -129,13 +170,13 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
 // read fall in distinct banks). Every staged key then feeds 8 queries x h heads.
 constexpr int kLdsQueries = 8, kLdsTile = 64;
 
-template <int D, int HB>
+template <int D, int HB, bool CAND>
 __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p) {
     constexpr int KS = D / 32, CH = D / 8;                      // k-steps; 16-byte chunks per row
     constexpr int kTileBytes = kLdsTile * D * 2;
     constexpr int kPer = kTileBytes / 16 / 256;                 // staging loads per thread
     __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTileBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int n = blockIdx.y;
     // this wave's two queries; the last query groups go first: in a prefill chunk positions
@@ -144,10 +185,13 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
     const int t0 = (gridDim.x - 1 - blockIdx.x) * kLdsQueries + 2 * wid;
     int vis[2];
     int vmax_w = 0;
+    __amdgpu_buffer_rsrc_t srow[2], crow[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         vis[j] = t0 + j < p.s ? visible_positions(p.pos[(int64_t)n * p.pos_seq_stride + t0 + j], p.ratio, p.n_pos) : 0;
         vmax_w = max(vmax_w, vis[j]);
+        srow[j] = score_row(p.scores, p.scores_seq_stride, n, t0 + j, p.s, p.n_pos, 4);
+        if constexpr (CAND) crow[j] = score_row(p.cand, p.cand_seq_stride, n, t0 + j, p.s, p.n_pos, 1);
     }
     // the workgroup's extent: the maximum over its 8 queries (all waves walk the same tiles)
     __shared__ int vmax_s[4];
@@ -171,13 +215,15 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
             for (int r = 0; r < 4; ++r) wv[j][mb][r] = ww[16 * mb + 4 * g + r];
         }
     }
-    // staging: load u of thread tid moves chunk (tid + 256 u) of the tile (row = chunk / CH)
+    // staging: load u of thread tid moves chunk (tid + 256 u) of the tile (row = chunk / CH);
+    // rows past the last visible position re-read it
+    const int klast = max(vmax, 1) - 1;
     u32x4 st[kPer];
     auto fetch = [&](int tb) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int c = tid + 256 * u, row = c / CH;
-            const int pp = min(tb + row, p.n_pos - 1);
+            const int pp = min(tb + row, klast);
             st[u] = *(const u32x4*)(kseq + (int64_t)pp * D + 8 * (c % CH));
         }
     };
@@ -194,55 +240,64 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
         fetch(0);
         stage(0);
     }
+    // Q, the weights and the first tile have landed: no load from before the loop is still
+    // counted inside it (the loop's waits then count only its own loads and stores)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int it = 0; it < nall; ++it) {
+    // The loop issues the same memory operations on every path: the next tile's loads (the
+    // last iteration re-reads its own tile), one buffer store per score (dropped for lanes
+    // and positions that store nothing), and the staging of the next tile (the last copy is
+    // never read).
+    for (int it = 0; it < ntiles; ++it) {
         const int tb = it * kLdsTile;
-        if (it < ntiles) {
-            if (it + 1 < ntiles) fetch(tb + kLdsTile);
-            SA_LDS const uint8_t* tile = (SA_LDS const uint8_t*)tiles[it & 1];
+        uint32_t cb[kLdsTile / 16][2];
+        if constexpr (CAND) {
+            // this tile's candidate bytes, before the next tile's loads so that waiting for
+            // them never waits for those
 #pragma unroll
-            for (int nb = 0; nb < kLdsTile / 16; ++nb) {
-                const int row = 16 * nb + l16, pp = tb + row;
-                u32x4 kb[KS];
+            for (int nb = 0; nb < kLdsTile / 16; ++nb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) cb[nb][j] = __builtin_amdgcn_raw_buffer_load_b8(crow[j], tb + 16 * nb + l16, 0, 0);
+        }
+        fetch(min(tb + kLdsTile, (ntiles - 1) * kLdsTile));
+        SA_LDS const uint8_t* tile = (SA_LDS const uint8_t*)tiles[it & 1];
+#pragma unroll
+        for (int nb = 0; nb < kLdsTile / 16; ++nb) {
+            const int row = 16 * nb + l16, pp = tb + row;
+            u32x4 kb[KS];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                kb[kk] = *(SA_LDS const u32x4*)(tile + row * (D * 2) + (((4 * kk + g) ^ (row & (CH - 1) & 15)) << 4));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x4 acc[HB];
+#pragma unroll
+                for (int mb = 0; mb < HB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk)
-                    kb[kk] = *(SA_LDS const u32x4*)(tile + row * (D * 2) + (((4 * kk + g) ^ (row & (CH - 1) & 15)) << 4));
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x4 acc[HB];
-#pragma unroll
-                    for (int mb = 0; mb < HB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-                        for (int mb = 0; mb < HB; ++mb)
-                            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, qa[j][mb][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[mb], 0, 0, 0);
-                    float part = 0.0f;
 #pragma unroll
                     for (int mb = 0; mb < HB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, qa[j][mb][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[mb], 0, 0, 0);
+                float part = 0.0f;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
-                    part = sum_xor32(sum_xor16(part));
-                    const int t = t0 + j;
-                    if (g == 0 && t < p.s && pp < p.n_pos) {
-                        bool keep = pp < vis[j];
-                        if (keep && p.cand) keep = p.cand[(int64_t)n * p.cand_seq_stride + (int64_t)t * p.n_pos + pp] != 0;
-                        p.scores[(int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos + pp] = keep ? part : -INFINITY;
-                    }
-                }
-            }
-            if (it + 1 < ntiles) stage((it + 1) & 1);
-            __syncthreads();
-        } else {
-            // beyond every query's visible positions: -inf, no keys needed
-            for (int j = 0; j < 2; ++j) {
-                const int t = t0 + j;
-                if (t >= p.s) continue;
-                float* row = p.scores + (int64_t)n * p.scores_seq_stride + (int64_t)t * p.n_pos;
-                for (int u = lane; u < kLdsTile && tb + u < p.n_pos; u += 64) row[tb + u] = -INFINITY;
+                for (int mb = 0; mb < HB; ++mb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
+                part = sum_xor32(sum_xor16(part));
+                bool keep = pp < vis[j];
+                if constexpr (CAND) keep = keep && cb[nb][j] != 0;
+                store_score(srow[j], pp, g == 0 && pp < p.n_pos, keep ? part : -INFINITY);
             }
         }
+        stage((it + 1) & 1);
+        __syncthreads();
+    }
+    // tiles past every query's visible positions: -inf, no keys needed
+    for (int it = ntiles; it < nall; ++it) {
+        const int pp = it * kLdsTile + lane;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) store_score(srow[j], pp, pp < p.n_pos, -INFINITY);
     }
 }
 
@@ -612,7 +667,8 @@ static hipError_t launch_scores_hb(const IdxParams& p, hipStream_t st) {
         if (p.s >= kLdsQueries) {
             const int64_t gx = (p.s + kLdsQueries - 1) / kLdsQueries;
             if (gx > 0x7fffffff || p.b > 65535) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((index_scores_lds_kernel<D, HB>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
+            if (p.cand) hipLaunchKernelGGL((index_scores_lds_kernel<D, HB, true>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL((index_scores_lds_kernel<D, HB, false>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
             return hipGetLastError();
         }
     }
@@ -623,8 +679,11 @@ static hipError_t launch_scores_hb(const IdxParams& p, hipStream_t st) {
     const int gy = (p.n_pos + kScoreChunk - 1) / kScoreChunk;
     if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)gx, (unsigned)gy);
-    if (qpw == 2) hipLaunchKernelGGL((index_scores_kernel<D, HB, QPW>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((index_scores_kernel<D, HB, 1>), grid, dim3(256), 0, st, p);
+    const bool cand = p.cand != nullptr;
+    if (qpw == 2 && cand) hipLaunchKernelGGL((index_scores_kernel<D, HB, QPW, true>), grid, dim3(256), 0, st, p);
+    else if (qpw == 2) hipLaunchKernelGGL((index_scores_kernel<D, HB, QPW, false>), grid, dim3(256), 0, st, p);
+    else if (cand) hipLaunchKernelGGL((index_scores_kernel<D, HB, 1, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((index_scores_kernel<D, HB, 1, false>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
