@@ -467,6 +467,32 @@ __device__ __forceinline__ void select_in_order(SA_LDS const uint32_t* keys, int
 }
 
 // ------------------------------------------------------------------ top-k lists
+// Sum of a wave-uniform value over the W waves that hold one query (the same result in every
+// wave), and the part of the waves before this one. `red` holds 2 x W words; consecutive
+// calls alternate between its halves (gen), so one barrier per call suffices: a wave writes
+// half g only after every wave has passed the barrier of the call before, i.e. has finished
+// reading half g two calls back. W = 1: no LDS, no barrier.
+template <int W>
+__device__ __forceinline__ int query_sum(int v, SA_LDS int* red, int& gen, int& before) {
+    before = 0;
+    if constexpr (W == 1) {
+        return v;
+    } else {
+        const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+        if (lane == 0) red[gen * W + wid] = v;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int u = 0; u < W; ++u) {
+            const int c = red[gen * W + u];
+            tot += c;
+            before += u < wid ? c : 0;
+        }
+        gen ^= 1;
+        return tot;
+    }
+}
+
 // W waves per query hold its scores as keys in registers: wave w, row j, lane l holds
 // position (w * J + j) * 64 + l (positions past n_pos hold key 0, as -inf does). The k-th
 // largest key is built from the top bit down: a bit stays set when at least k keys are at or
@@ -493,29 +519,8 @@ __global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const
     uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) key[j] = score_key(v[j]) & (base + 64 * j + lane < p.n_pos ? ~0u : 0u);
-    // Sum of a wave-uniform value over the query's waves (the same in every wave), and the
-    // part of waves before this one. Consecutive calls alternate between the two rows of
-    // `red`: a wave writes row g only after every wave has passed the barrier of the call
-    // before, i.e. has finished reading row g two calls back.
     int gen = 0;
-    auto block_sum = [&](int v, int& before) {
-        before = 0;
-        if constexpr (W == 1) {
-            return v;
-        } else {
-            if (lane == 0) red[gen][wid] = v;
-            __syncthreads();
-            int tot = 0;
-#pragma unroll
-            for (int u = 0; u < W; ++u) {
-                const int c = red[gen][u];
-                tot += c;
-                before += u < wid ? c : 0;
-            }
-            gen ^= 1;
-            return tot;
-        }
-    };
+    auto block_sum = [&](int v, int& before) { return query_sum<W>(v, (SA_LDS int*)&red[0][0], gen, before); };
     auto count_ge = [&](uint32_t c) {
         int cnt = 0;
 #pragma unroll
@@ -580,6 +585,119 @@ __global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const
 }
 
 // ------------------------------------------------------------------ candidate blocks
+// select_candidate_blocks for rows whose blocks fit in lanes: W waves per query, lane l of
+// wave w holds the J consecutive positions from (w * 64 + l) * J on, so a block of BS
+// positions (a power of two up to J) lies inside one lane and its maximum is in-lane work.
+// Block order is (wave, lane, slot). The kept blocks are chosen as in index_topk_kernel
+// (bitwise threshold over the block keys, equal keys: the lower block first), or all of
+// them when they are at most topk_blocks; each lane writes its J mask bytes as 16-byte
+// stores. Rows of whole 16-byte pieces only (n_pos, the mask pointer and its strides
+// multiples of 16).
+template <int W, int J, int BS>
+__global__ __launch_bounds__(W == 1 ? 256 : W * 64) void candidate_wave_kernel(const CandParams p) {
+    constexpr int NBL = J / BS;                                  // blocks per lane
+    static_assert(J % 16 == 0 && BS >= 1 && J % BS == 0 && (BS & (BS - 1)) == 0, "blocks inside lanes");
+    __shared__ int red[2][W];
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t qi = W == 1 ? (int64_t)blockIdx.x * 4 + wid : (int64_t)blockIdx.x;
+    if (W == 1 && qi >= (int64_t)p.b * p.s) return;             // no barriers when W = 1
+    const int w = W == 1 ? 0 : wid;
+    const int n = (int)(qi / p.s), t = (int)(qi % p.s);
+    const int u0 = (w * 64 + lane) * J;                          // this lane's first position
+    const float* lg = p.logits + (int64_t)n * p.logits_seq_stride + (int64_t)t * p.n_pos;
+    const __amdgpu_buffer_rsrc_t lrow = __builtin_amdgcn_make_buffer_rsrc((void*)lg, 0, p.n_pos * 4, 0x00020000);
+    u32x4 x[J / 4];
+#pragma unroll
+    for (int c = 0; c < J / 4; ++c)
+        x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrow, (u0 + 4 * c) * 4, 0, 0));
+    // block keys: the maximum of the order-preserving keys (-inf padding past n_pos: key 0)
+    uint32_t bk[NBL];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = i * BS; e < (i + 1) * BS; ++e)
+            m = max(m, score_key(bits_f32(x[e / 4][e % 4])) & (u0 + e < p.n_pos ? ~0u : 0u));
+        bk[i] = m;
+    }
+    const int pos = p.pos[(int64_t)n * p.pos_seq_stride + t];
+    const int64_t len = pos < 0 ? 0 : ((int64_t)pos + 1) / p.ratio;
+    const int64_t last = len > 0 ? (len - 1) / BS : -1;          // the newest visible block
+    const int nblk = (p.n_pos + BS - 1) / BS;
+    const int b0 = u0 / BS;                                      // this lane's first block
+#pragma unroll
+    for (int i = 0; i < NBL; ++i)
+        if (last < nblk && b0 + i == last) bk[i] = score_key(INFINITY);
+    int gen = 0;
+    auto count = [&](auto pred) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) c += __builtin_popcountll(__ballot(pred(bk[i])));
+        int before;
+        return query_sum<W>(c, (SA_LDS int*)&red[0][0], gen, before);
+    };
+    const int selectable = count([](uint32_t k) { return k != 0u; });
+    const int k = min(p.topk_blocks, selectable);
+    uint32_t thr = 0;                                            // kept: key > thr, or == thr
+    int ties = 0;                                                // among the first `ties`
+    if (k > 0 && k < selectable) {
+        uint32_t lo = 0;
+        bool exact = false;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = lo | (1u << bit);
+            const int cnt = count([c](uint32_t kv) { return kv >= c; });
+            if (cnt >= k) {
+                lo = c;
+                if (cnt == k) { exact = true; break; }
+            }
+        }
+        if (exact) {
+            thr = lo - 1;
+        } else {
+            thr = lo;
+            ties = k - (lo == 0xffffffffu ? 0 : count([lo](uint32_t kv) { return kv > lo; }));
+        }
+    }
+    uint32_t keep = 0;                                           // bit i: slot i kept
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) keep |= (uint32_t)(bk[i] > thr) << i;
+    if (ties > 0) {
+        // rank of each tied block in block order: tied blocks of earlier waves, of lower
+        // lanes, of earlier slots of this lane
+        const uint64_t below = (1ull << lane) - 1;
+        int lower = 0, wave_ties = 0;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            const uint64_t m = __ballot(bk[i] == thr);
+            lower += __builtin_popcountll(m & below);
+            wave_ties += __builtin_popcountll(m);
+        }
+        int before;
+        query_sum<W>(wave_ties, (SA_LDS int*)&red[0][0], gen, before);
+        int r = before + lower;
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            const bool eq = bk[i] == thr;
+            keep |= (uint32_t)(eq && r < ties) << i;
+            r += eq;
+        }
+    }
+    uint8_t* mrow = p.mask + (int64_t)n * p.mask_seq_stride + (int64_t)t * p.n_pos;
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc((void*)mrow, 0, p.n_pos, 0x00020000);
+#pragma unroll
+    for (int c = 0; c < J / 16; ++c) {
+        u32x4 word;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v |= ((keep >> ((16 * c + 4 * q + e) / BS)) & 1u) << (8 * e);
+            word[q] = v;
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(word, mr, u0 + 16 * c, 0, 0);
+    }
+}
+
 // select_candidate_blocks for one query per workgroup: block maxima (the last block padded
 // with -inf), the block of the newest visible position, (len - 1) / block_size with floor
 // division, pinned to +inf, the min(topk_blocks, blocks) best blocks kept when above -inf
@@ -730,7 +848,33 @@ hipError_t launch_index_topk(const IdxParams& p, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int W, int J, int BS>
+static hipError_t launch_cand_wj(const CandParams& p, hipStream_t st) {
+    const int64_t nq = (int64_t)p.b * p.s;
+    const int64_t grid = W == 1 ? (nq + 3) / 4 : nq;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((candidate_wave_kernel<W, J, BS>), dim3((unsigned)grid), dim3(W == 1 ? 256 : W * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int BS>
+static hipError_t launch_cand_bs(const CandParams& p, hipStream_t st) {
+    if (p.n_pos <= 2048) return launch_cand_wj<1, 32, BS>(p, st);
+    if (p.n_pos <= 4096) return launch_cand_wj<4, 16, BS>(p, st);
+    if (p.n_pos <= 8192) return launch_cand_wj<4, 32, BS>(p, st);
+    if (p.n_pos <= 16384) return launch_cand_wj<16, 16, BS>(p, st);
+    return launch_cand_wj<16, 32, BS>(p, st);
+}
+
 hipError_t launch_candidate_blocks(const CandParams& p, hipStream_t st) {
+    // rows of whole 16-byte mask pieces, blocks of 4, 8 or 16 positions: one wave (or 4, or
+    // 16) per query, blocks inside lanes
+    const bool rows16 = p.n_pos % 16 == 0 && (uintptr_t)p.mask % 16 == 0 && (p.b == 1 || p.mask_seq_stride % 16 == 0);
+    if (rows16 && p.n_pos <= 32768) {
+        if (p.block_size == 4) return launch_cand_bs<4>(p, st);
+        if (p.block_size == 8) return launch_cand_bs<8>(p, st);
+        if (p.block_size == 16) return launch_cand_bs<16>(p, st);
+    }
     const int nblk = (p.n_pos + p.block_size - 1) / p.block_size;
     const size_t lds = (256 + 16) * 4 + (size_t)nblk * 5;
     const int64_t nq = (int64_t)p.b * p.s;

@@ -119,14 +119,20 @@ def test_indexer_candidates_and_two_levels(sa):
 
 def test_candidate_blocks_random_logits(sa):
     """Random logits with -inf beyond each query's visible positions, several block sizes
-    (powers of two up to 64 take block maxima by lane exchanges, others by LDS atomics), ragged
-    last blocks, selections that keep every visible block and ones that choose."""
+    (rows of whole 16-byte pieces with blocks of 4, 8 or 16 take one, four or sixteen waves
+    per query with blocks inside lanes; other powers of two up to 64 take block maxima by lane
+    exchanges, the rest by LDS atomics), ragged last blocks, selections that keep every
+    visible block and ones that choose, and small-integer logits whose block maxima tie."""
     g = torch.Generator().manual_seed(21)
-    for b, s, n_pos, ratio, tb, bs in ((2, 6, 1000, 4, 17, 8), (1, 3, 16384, 4, 2048, 8), (3, 4, 999, 1, 3, 7),
-                                       (2, 5, 1001, 2, 40, 16), (2, 3, 4096, 4, 64, 64), (1, 4, 777, 1, 500, 4),
-                                       (2, 3, 2048, 4, 9, 1)):
+    for b, s, n_pos, ratio, tb, bs, ints in (
+            (2, 6, 1000, 4, 17, 8, False), (1, 3, 16384, 4, 2048, 8, False), (3, 4, 999, 1, 3, 7, False),
+            (2, 5, 1001, 2, 40, 16, False), (2, 3, 4096, 4, 64, 64, False), (1, 4, 777, 1, 500, 4, False),
+            (2, 3, 2048, 4, 9, 1, False),
+            (2, 5, 2048, 4, 17, 8, False), (2, 5, 2048, 1, 17, 8, True), (1, 4, 4096, 1, 100, 16, True),
+            (2, 3, 8192, 2, 300, 4, False), (1, 3, 16384, 4, 100, 8, True), (1, 2, 20000, 1, 1000, 8, False),
+            (3, 2, 512, 1, 5, 16, True)):
         pos = torch.randint(0, ratio * n_pos, (b, s), generator=g, dtype=torch.int32)
-        lg = torch.randn(b, s, n_pos, generator=g)
+        lg = torch.randint(-3, 4, (b, s, n_pos), generator=g).float() if ints else torch.randn(b, s, n_pos, generator=g)
         vis = torch.clamp((pos.long() + 1) // ratio, max=n_pos)
         lg[torch.arange(n_pos)[None, None, :] >= vis[..., None]] = -float("inf")
         mask = sa.candidate_blocks(lg.cuda(), pos.cuda(), ratio, tb, bs).cpu().numpy()
