@@ -268,23 +268,30 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk)
                 kb[kk] = *(SA_LDS const u32x4*)(tile + row * (D * 2) + (((4 * kk + g) ^ (row & (CH - 1) & 15)) << 4));
+            // both queries' head blocks accumulate side by side (k-step outermost): 2 HB
+            // independent accumulators between dependent matrix instructions
+            f32x4 acc[2][HB];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                f32x4 acc[HB];
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int mb = 0; mb < HB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int mb = 0; mb < HB; ++mb) acc[j][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < KS; ++kk)
+            for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int mb = 0; mb < HB; ++mb)
-                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, qa[j][mb][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[mb], 0, 0, 0);
-                float part = 0.0f;
+                        acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, qa[j][mb][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[j][mb], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // two partial sums per lane, added at the end
+                float part2[2] = {0.0f, 0.0f};
 #pragma unroll
                 for (int mb = 0; mb < HB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
-                part = sum_xor32(sum_xor16(part));
+                    for (int r = 0; r < 4; ++r) part2[r & 1] += wv[j][mb][r] * fmaxf(acc[j][mb][r], 0.0f);
+                const float part = sum_xor32(sum_xor16(part2[0] + part2[1]));
                 bool keep = pp < vis[j];
                 if constexpr (CAND) keep = keep && cb[nb][j] != 0;
                 store_score(srow[j], pp, g == 0 && pp < p.n_pos, keep ? part : -INFINITY);
