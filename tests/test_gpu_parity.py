@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import sa_workloads as W
-from sa_harness import (ATOL, RTOL, assert_close, gpu_indices, gpu_inputs, gpu_run, oracle_core,
-                        oracle_indices, oracle_rotate, oracle_run, u16)
+from sa_harness import (ATOL, RTOL, assert_close, f32_of_u16, gpu_indices, gpu_inputs, gpu_run,
+                        oracle_core, oracle_indices, oracle_rotate, oracle_run, u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -711,6 +711,33 @@ def test_fused_window_lists_equal_explicit_lists(sa, name, size):
     for fmt in (("bf16", "fp8") if size == "small" else ("bf16",)):
         ref, got = _fused_case(w, fmt)
         assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), f"{name} {fmt}"
+
+
+def test_fused_ring_with_unreached_slots(sa):
+    """Fused ring lists (128 slots, two key groups at d 512) at positions before, at and past
+    the ring's first tiles, with every slot the position has not reached holding NaN: the
+    output matches the oracle on the lists of sa_window_topk_idxs and is finite."""
+    b, h, d, window = 8, 64, 512, 128
+    q, kv, sink, _ = W.rand_problem(161, b, 1, h, d, window, window, 0.0, False)
+    pos = torch.tensor([0, 5, 31, 40, 62, 63, 64, 500], dtype=torch.int32).view(b, 1)
+    for bi in range(b):
+        p = int(pos[bi, 0])
+        if p + 1 < window:
+            kv[bi, p + 1:] = float("nan")
+    win = oracle.window_topk_idxs(window, 1, pos.view(-1).numpy())
+    full = torch.from_numpy(win.reshape(b, 1, window))
+    poisoned = torch.full((b, 1, window), 10 ** 9, dtype=torch.int32)
+    rd = 64
+    table = sa.rope_table(rd, 1024, 10000.0, "cuda")
+    posd = pos.cuda()
+    scale = float(np.float32(d ** -0.5))
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), poisoned.cuda(), scale, rope=(table, posd),
+                         window=(window, "ring", posd))
+    got = u16(out).reshape(-1, h, d)
+    assert np.all(np.isfinite(f32_of_u16(got)))
+    core = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), full.numpy(), scale)
+    ref = oracle.apply_rotary(core, rd, oracle.freqs_cis(rd, 1024, 10000.0), pos.view(-1).numpy(), inverse=True)
+    assert_close(got, ref, "ring with unreached slots")
 
 
 def test_fused_window_across_splits_and_against_oracle(sa):
