@@ -237,8 +237,8 @@ int sa_kv_write(const sa_kv_write_args *a, void *stream);
  * compressed ones in sparse_attn's kv), then -1 up to topk columns; the pages' list length
  * is min(index_topk, end_pos // ratio). Output: idx[n * idx_seq_stride + t * idx_row_stride
  * + j] for j < topk (other columns untouched, so the window part of a list can share the
- * row). Supported: h = 16, 32 or 64 (64 with d <= 128), d = 64, 128 or 256, n_pos <= 32768
- * when idx != NULL. Pointers are device pointers, caller-owned; q, k 16-byte aligned. */
+ * row). Supported: h = 16, 32 or 64 (64 with d <= 128), d = 64, 128 or 256, n_pos <= 2^28
+ * (<= 32768 when idx != NULL). Pointers are device pointers, caller-owned; q, k 16-byte aligned. */
 typedef struct sa_indexer_args {
     int32_t b, s, h, d;     /* sequences, queries per sequence, index heads, index head dim */
     int32_t n_pos;          /* compressed positions of k per sequence */

@@ -379,6 +379,8 @@ SA_EXPORT int sa_indexer_topk(const sa_indexer_args* a, void* stream) {
         !aligned(a->scores, 4) || (a->idx && !aligned(a->idx, 4)))
         return SA_ERR_INVALID;
     if (a->q_seq_stride % 8 || a->k_seq_stride % 8) return SA_ERR_INVALID;
+    // a query's score row is addressed as one buffer of n_pos f32 (32-bit byte offsets)
+    if (a->n_pos > (1 << 28)) return SA_ERR_UNSUPPORTED;
     const int64_t s_np = (int64_t)a->s * a->n_pos;
     if (a->b > 1) {
         if (a->q_seq_stride < (int64_t)a->s * a->h * a->d || a->k_seq_stride < (int64_t)a->n_pos * a->d ||

@@ -202,3 +202,50 @@ def test_fused_window_validation(sa):
         # topk is 8: a ring of 9 slots does not fit, and a window needs 4-byte aligned positions
         a = _args(sa, **kw)
         assert sa.lib().sa_sparse_attn(C.byref(a), None) == -1, kw
+
+
+def _indexer_args(sa, **kw):
+    a = sa.IndexerArgs()
+    a.b, a.s, a.h, a.d, a.n_pos, a.ratio = 2, 4, 32, 128, 1000, 4
+    a.q = a.k = a.w = a.pos = a.scores = 0x10000
+    a.q_seq_stride, a.k_seq_stride = 4 * 32 * 128, 1000 * 128
+    a.w_seq_stride, a.pos_seq_stride, a.scores_seq_stride = 4 * 32, 4, 4 * 1000
+    a.topk, a.offset = 64, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"b": 0}, -1), ({"ratio": 0}, -1), ({"d": 96}, -2), ({"h": 48}, -2), ({"h": 64, "d": 256}, -2),
+    ({"q": 0}, -1), ({"q": 0x10008}, -1), ({"scores": 0x10002}, -1), ({"q_seq_stride": 12}, -1),
+    ({"k_seq_stride": 999 * 128}, -1), ({"scores_seq_stride": 3999}, -1),
+    ({"n_pos": (1 << 28) + 1, "k_seq_stride": ((1 << 28) + 1) * 128, "scores_seq_stride": 4 * ((1 << 28) + 1)}, -2),
+    ({"idx": 0x10000, "topk": 0, "idx_row_stride": 64, "idx_seq_stride": 256}, -1),
+    ({"idx": 0x10000, "idx_row_stride": 32, "idx_seq_stride": 256}, -1),
+    ({"idx": 0x10000, "idx_row_stride": 64, "idx_seq_stride": 100}, -1),
+    ({"idx": 0x10000, "idx_row_stride": 64, "idx_seq_stride": 256, "n_pos": 40000,
+      "k_seq_stride": 40000 * 128, "scores_seq_stride": 4 * 40000}, -2),
+])
+def test_indexer_rejects_before_any_hip_call(sa, kw, status):
+    """sa_indexer_topk: bad sizes, pointers, alignments and strides are refused on the host,
+    shapes no kernel takes are unsupported (no launch is ever attempted here)."""
+    assert sa.lib().sa_indexer_topk(C.byref(_indexer_args(sa, **kw)), None) == status
+    assert sa.lib().sa_indexer_topk(None, None) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"b": 0}, -1), ({"topk_blocks": 0}, -1), ({"block_size": 0}, -1), ({"logits": 0}, -1),
+    ({"logits": 0x10002}, -1), ({"mask": 0}, -1), ({"logits_seq_stride": 100}, -1),
+    ({"mask_seq_stride": 100}, -1), ({"n_pos": 40000, "block_size": 1, "logits_seq_stride": 120000,
+                                      "mask_seq_stride": 120000}, -2),
+])
+def test_candidate_blocks_rejects_before_any_hip_call(sa, kw, status):
+    a = sa.CandidateArgs()
+    a.b, a.s, a.n_pos, a.ratio, a.topk_blocks, a.block_size = 2, 3, 1000, 4, 16, 8
+    a.logits = a.pos = a.mask = 0x10000
+    a.logits_seq_stride, a.pos_seq_stride, a.mask_seq_stride = 3000, 3, 3000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    assert sa.lib().sa_candidate_blocks(C.byref(a), None) == status
+    assert sa.lib().sa_candidate_blocks(None, None) == -1
