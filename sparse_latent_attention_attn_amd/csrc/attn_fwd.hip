@@ -57,7 +57,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const KParams p) {
 
 // ------------------------------------------------------------------ launch
 template <int D, bool FP8>
-static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int kg, int blocks, hipStream_t st) {
+static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int kg, bool compact, int blocks, hipStream_t st) {
+    if (compact) {
+        if constexpr (D == 512 && !FP8)
+            if (nw == 2 && hpw == 1 && kg == 1) return launch_fwd<512, false, 2, 1, 1, true>(p, blocks, st);
+        return hipErrorInvalidValue;
+    }
     if constexpr (D == 512) {
         if constexpr (!FP8)
             if (hpw == 2) return nw == 4 && kg == 1 ? launch_fwd_wide(p, blocks, st) : hipErrorInvalidValue;
@@ -72,9 +77,10 @@ static hipError_t launch_fwd_nw(const KParams& p, int nw, int hpw, int kg, int b
 }
 
 template <int D>
-static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int kg, int blocks, hipStream_t st) {
-    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, kg, blocks, st)
-                       : launch_fwd_nw<D, false>(p, nw, hpw, kg, blocks, st);
+static hipError_t launch_all(const KParams& p, bool fp8, int nw, int hpw, int kg, bool compact, int blocks,
+                             hipStream_t st) {
+    hipError_t e = fp8 ? launch_fwd_nw<D, true>(p, nw, hpw, kg, compact, blocks, st)
+                       : launch_fwd_nw<D, false>(p, nw, hpw, kg, compact, blocks, st);
     if (e != hipSuccess || p.splits == 1) return e;
     // one wave per (query, head); the host keeps b * s * h within int32 for split plans
     const int64_t waves = (int64_t)p.b * p.s * p.h;
@@ -118,13 +124,13 @@ hipError_t launch_dequant_kv(const uint8_t* codes, int64_t codes_seq_stride, con
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st) {
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, bool compact, hipStream_t st) {
     const int blocks = p.b * p.s * p.head_blocks * p.splits;
     switch (p.d) {
-        case 64: return launch_all<64>(p, fp8, nw, hpw, kg, blocks, st);
-        case 128: return launch_all<128>(p, fp8, nw, hpw, kg, blocks, st);
-        case 256: return launch_all<256>(p, fp8, nw, hpw, kg, blocks, st);
-        case 512: return launch_all<512>(p, fp8, nw, hpw, kg, blocks, st);
+        case 64: return launch_all<64>(p, fp8, nw, hpw, kg, compact, blocks, st);
+        case 128: return launch_all<128>(p, fp8, nw, hpw, kg, compact, blocks, st);
+        case 256: return launch_all<256>(p, fp8, nw, hpw, kg, compact, blocks, st);
+        case 512: return launch_all<512>(p, fp8, nw, hpw, kg, compact, blocks, st);
         default: return hipErrorInvalidValue;
     }
 }

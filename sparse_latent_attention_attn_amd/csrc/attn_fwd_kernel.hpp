@@ -375,15 +375,17 @@ struct Pipe {
 
 // LDS plan of one kernel instance: the index stage, the bf16 tile buffers and, for fp8
 // storage, the raw slots of codes and scales.
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, bool CMP = false>
 struct KernelLds {
     static constexpr bool kFp8Pipe = FP8 && D == 512;
-    // bf16: the ring of the pipelined loop; fp8 at d = 512: the tiles being scored, multiplied
-    // and converted; other fp8: one tile
-    static constexpr int kTileBufs = FP8 ? (kFp8Pipe ? 3 : 1) : Pipe<D, NW>::kBuffers;
+    // bf16: the ring of the pipelined loop (compact: two tiles, the next gathered while the
+    // current one is worked on); fp8 at d = 512: the tiles being scored, multiplied and
+    // converted; other fp8: one tile
+    static constexpr int kTileBufs = CMP ? 2 : FP8 ? (kFp8Pipe ? 3 : 1) : Pipe<D, NW>::kBuffers;
     static constexpr int kRawSlots = FP8 ? (kFp8Pipe ? 3 : 2) : 0;
-    // the pipelined fp8 path stages fewer index columns so that its slots fit in LDS
-    static constexpr int kStageCols = kFp8Pipe ? kMaxColsFp8Pipe : kMaxColsPerSplit;
+    // the pipelined fp8 path stages fewer index columns so that its slots fit in LDS; the
+    // compact layout stages few, so that two workgroups share a compute unit's LDS
+    static constexpr int kStageCols = CMP ? kMaxColsCompact : kFp8Pipe ? kMaxColsFp8Pipe : kMaxColsPerSplit;
     static constexpr size_t kTiles = (size_t)kTileBufs * Geo<D>::kTileBytes + (size_t)kRawSlots * RawSlot<D>::kBytes;
 };
 
@@ -392,13 +394,14 @@ struct KernelLds {
 // one key group take every KG-th tile of the item's index columns, so one query's keys are
 // worked on by KG waves side by side, and their partial results are merged in LDS at the
 // end (KG = 1: every wave takes every tile, for its own heads).
-template <int D, bool FP8, int NW, int HPW, int KG = 1>
+template <int D, bool FP8, int NW, int HPW, int KG = 1, bool CMP = false>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     static_assert(KG == 1 || ((!FP8 || D == 512) && NW % KG == 0), "key groups: bf16, or fp8 at d = 512");
+    static_assert(!CMP || (KG == 1 && !FP8), "compact layout: bf16 storage, one key group");
     constexpr int HB = NW / KG;                 // head groups of the workgroup
     using G = Geo<D>;
     using PP = Pipe<D, NW>;
-    using KL = KernelLds<D, FP8, NW>;
+    using KL = KernelLds<D, FP8, NW, CMP>;
     constexpr int NB = KL::kTileBufs;
     constexpr bool kFp8Pipe = KL::kFp8Pipe;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
@@ -789,8 +792,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             __builtin_amdgcn_sched_barrier(0);
             pv(tile(0), pb, [](int) {});
         }
-    } else if constexpr (KG > 1) {
-        // Key groups: the waves of key group g work on tile s*KG + g of super tile s.
+    } else if constexpr (KG > 1 || CMP) {
+        // Key groups: the waves of key group g work on tile s*KG + g of super tile s (the
+        // compact layout runs this loop with one group: a two-tile ring, the next tile
+        // gathered while the current one is worked on).
         //   bf16 storage: the tile ring holds NS super tiles of KG tiles and all waves gather
         //   every tile. With two super tiles in the ring the next one is gathered while the
         //   current one is worked on; with one, after it (a barrier in between).
@@ -1166,10 +1171,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     }
 }
 
-template <int D, bool FP8, int NW, int HPW = 1, int KG = 1>
+template <int D, bool FP8, int NW, int HPW = 1, int KG = 1, bool CMP = false>
 inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     using G = Geo<D>;
-    using KL = KernelLds<D, FP8, NW>;
+    using KL = KernelLds<D, FP8, NW, CMP>;
     // after the tile buffers (and the fp8 raw slots) the region must also hold the
     // epilogue's 16 padded output rows per wave
     constexpr size_t kTiles = KL::kTiles;
@@ -1183,7 +1188,7 @@ inline hipError_t launch_fwd(const KParams& p, int blocks, hipStream_t st) {
     static_assert(KG <= 2 || (size_t)(NW / KG) * kHeadsPerWave * (2 * D + 16) +
                                  (size_t)(KG - 1) * (NW / KG) * (HPW * G::kDBlocks * kWave * 16 + HPW * kWave * 8) <= kTiles,
                   "key-group merge does not fit the tile region");
-    auto k = attn_fwd_kernel<D, FP8, NW, HPW, KG>;
+    auto k = attn_fwd_kernel<D, FP8, NW, HPW, KG, CMP>;
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(blocks), dim3(NW * kWave), lds, st, p);

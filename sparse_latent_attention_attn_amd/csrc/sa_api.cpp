@@ -128,6 +128,15 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
         pl.hpw = 2;
     pl.kg = 1;
     const int ntiles = (a->topk + kTileKeys - 1) / kTileKeys;
+    // Short lists (at most kMaxColsCompact columns) with enough workgroups for two per
+    // compute unit: two-wave workgroups with a two-tile ring and a small index stage, so that
+    // two of them share a compute unit and one's memory round trips (Q, the first tile, the
+    // output) overlap the other's products.
+    if (bf16_rows && a->d == 512 && a->topk <= sa::kMaxColsCompact && nq * blocks_for(2) >= 2 * (int64_t)cus) {
+        pl.nw = 2;
+        pl.hpw = 1;
+        pl.compact = true;
+    }
     pl.head_blocks = blocks_for(pl.nw * pl.hpw);
     int64_t wgs = nq * pl.head_blocks;
     int splits = 1;
@@ -141,7 +150,7 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // split, as large as 2 KB per head) and the combine kernel. Measured on 64 queries x 128 heads x 640 columns: 41.5 us with
     // two splits, 36.7 us with two key groups. The most key groups that keep one round of
     // workgroups on the GPU and leave no group without tiles.
-    if (splits > 1 && a->d == 512 && pl.hpw == 1) {
+    if (splits > 1 && a->d == 512 && pl.hpw == 1 && !pl.compact) {
         for (int kg = bf16_rows ? 4 : 2; kg >= 2; kg /= 2) {
             if (nq * blocks_for(4 / kg) <= cus && ntiles >= kg) {
                 pl.kg = kg;
@@ -151,7 +160,7 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
                 break;
             }
         }
-    } else if (wgs < cus && ntiles >= 2 && a->d == 512 && pl.hpw == 1 && nq * blocks_for(2) <= cus) {
+    } else if (wgs < cus && ntiles >= 2 && a->d == 512 && pl.hpw == 1 && !pl.compact && nq * blocks_for(2) <= cus) {
         // A short list that leaves compute units idle: two key groups of two waves on the
         // same heads. Measured on 32 queries x 64 heads x 128 columns: 11.65 us against 12.0
         // with one two-wave group (four key groups: 12.0), and with fp8 storage 12.4 against
@@ -163,7 +172,8 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     pl.h_pad = pl.head_blocks * pl.nw / pl.kg * pl.hpw * kHeadsPerWave;
     // a workgroup stages at most kMaxColsPerSplit index columns (kMaxColsFp8Pipe for fp8
     // storage at d = 512)
-    const int max_cols = !bf16_rows && a->d == 512 ? sa::kMaxColsFp8Pipe : sa::kMaxColsPerSplit;
+    const int max_cols = pl.compact ? sa::kMaxColsCompact
+                         : !bf16_rows && a->d == 512 ? sa::kMaxColsFp8Pipe : sa::kMaxColsPerSplit;
     const int max_tiles = max_cols / kTileKeys;
     splits = std::max(splits, (ntiles + max_tiles - 1) / max_tiles);
     const int tiles_per_split = (ntiles + splits - 1) / splits;
@@ -259,7 +269,7 @@ hipError_t run_sparse_attn(const sa_attn_args* a, const KParams& p, const Plan& 
                                                (uint16_t*)p.kv, st);
         if (e != hipSuccess) return e;
     }
-    return launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32 && !pl.dequant, pl.nw, pl.hpw, pl.kg, st);
+    return launch_sparse_attn(p, a->kv_format == SA_KV_FP8_E4M3_B32 && !pl.dequant, pl.nw, pl.hpw, pl.kg, pl.compact, st);
 }
 
 }  // namespace sa

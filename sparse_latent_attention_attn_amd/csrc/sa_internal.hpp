@@ -14,6 +14,7 @@ constexpr int kTileKeys = 32;       // index columns per key tile
 constexpr int kHeadsPerWave = 16;   // heads in one block (the N of a 16x16 MFMA tile)
 constexpr int kMaxWaves = 4;        // waves per workgroup
 constexpr int kMaxColsPerSplit = 4096;  // index columns one workgroup stages in LDS
+constexpr int kMaxColsCompact = 256;    // the same in the compact layout (two workgroups per CU)
 constexpr int kMaxColsFp8Pipe = 3072;   // the same for fp8 storage at d = 512 (its raw slots take the rest)
 
 // Everything one sparse_attn launch needs, passed by value as the kernel argument.
@@ -94,6 +95,7 @@ struct Plan {
     int h_pad;
     int splits;
     int cols_per_split; // a multiple of the key tile
+    bool compact;       // two-wave workgroups with a two-tile ring, two of them per compute unit
     bool dequant;       // fp8 storage turned into bf16 rows at the start of the workspace first
     size_t dq_bytes;    // bytes of those rows (0 without)
     size_t ws_bytes;    // the whole workspace: dequantised rows, then the split partials
@@ -102,7 +104,7 @@ struct Plan {
 // Validation, plan and kernel parameters of a sparse_attn call (sa_api.cpp); returns an SA_*
 // status. ws / ws_bytes: the buffer of the split partials.
 int prepare_sparse_attn(const sa_attn_args* a, void* ws, size_t ws_bytes, KParams& p, Plan& pl);
-hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, hipStream_t st);
+hipError_t launch_sparse_attn(const KParams& p, bool fp8, int nw, int hpw, int kg, bool compact, hipStream_t st);
 // The kernels of a prepared call: the dequantisation pass when the plan has one, then
 // sparse_attn (and its combine kernel).
 hipError_t run_sparse_attn(const sa_attn_args* a, const KParams& p, const Plan& pl, hipStream_t st);
