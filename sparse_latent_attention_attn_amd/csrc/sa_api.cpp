@@ -132,7 +132,9 @@ sa::Plan make_plan(const sa_attn_args* a, int cus) {
     // compute unit: two-wave workgroups with a two-tile ring and a small index stage, so that
     // two of them share a compute unit and one's memory round trips (Q, the first tile, the
     // output) overlap the other's products.
-    if (bf16_rows && a->d == 512 && a->topk <= sa::kMaxColsCompact && nq * blocks_for(2) >= 2 * (int64_t)cus) {
+    // (Plans with two head blocks per wave keep them: one workgroup then gathers for 128 heads.)
+    if (bf16_rows && a->d == 512 && pl.hpw == 1 && a->topk <= sa::kMaxColsCompact &&
+        nq * blocks_for(2) >= 2 * (int64_t)cus) {
         pl.nw = 2;
         pl.hpw = 1;
         pl.compact = true;

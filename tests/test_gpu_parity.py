@@ -208,6 +208,27 @@ def test_wide_waves(sa, seed, b, s, h, rows, topk, hole):
     assert_close(u16(out).reshape(-1, h, 512), ref, f"wide {seed}")
 
 
+@pytest.mark.parametrize("seed,b,s,h,rows,topk,hole,dup", [
+    (71, 1, 300, 64, 500, 200, 0.1, False),   # 600 two-wave workgroups, a ragged last tile
+    (72, 2, 150, 40, 90, 256, 0.3, True),     # 40 heads: the second workgroup half padding
+    (73, 1, 520, 48, 300, 33, 0.0, False),    # two tiles, the second with one column
+])
+def test_compact_plan(sa, seed, b, s, h, rows, topk, hole, dup):
+    """Short lists (at most 256 columns) at d = 512 with enough queries for two workgroups
+    per compute unit: the compact plan (two-wave workgroups, a two-tile ring), including a
+    late key far above the rest for some queries (the second key pass)."""
+    _say("compact", seed, b, s, h, rows, topk)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, 512, rows, topk, hole, dup)
+    scale = float(np.float32(512 ** -0.5))
+    for t in range(0, s, 41):
+        r = int(idx[0, t, topk - 1])
+        kv[0, r if r >= 0 else 0] = (q[0, t, 1].float() * 2).to(torch.bfloat16)
+    out = sa.sparse_attn(q.cuda(), kv.cuda(), sink.cuda(), idx.cuda(), scale)
+    ref = oracle.sparse_attn(u16(q), u16(kv), sink.numpy(), idx.numpy(), scale)
+    assert_close(u16(out).reshape(-1, h, 512), ref, f"compact {seed}")
+    assert bool(torch.isfinite(out.float()).all())
+
+
 def test_strided_sequences(sa):
     """Per-sequence blocks inside larger buffers (non-packed sequence strides)."""
     q, kv, sink, idx = W.rand_problem(21, 3, 2, 32, 128, 50, 40, 0.1, False)
