@@ -6,8 +6,10 @@
 //   * index_topk_kernel: per query, the topk best finite scores by a bitwise threshold
 //     search over keys held in registers, listed in position order (ties: the lower position
 //     first), shifted by the offset and padded with -1;
-//   * candidate_blocks_kernel: per query, block maxima, the newest visible block pinned, the
-//     best blocks kept by the same radix select, expanded to a position mask.
+//   * candidate_wave_kernel (blocks of 4, 8 or 16 in rows of whole 16-byte mask pieces) and
+//     candidate_blocks_kernel (other shapes): per query, block maxima, the newest visible
+//     block pinned, the best blocks kept (the wave kernel by the same threshold search, the
+//     other by a radix select in LDS), expanded to a position mask.
 #include "lds_dma.hpp"
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
