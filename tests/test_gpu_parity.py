@@ -229,6 +229,52 @@ def test_compact_plan(sa, seed, b, s, h, rows, topk, hole, dup):
     assert bool(torch.isfinite(out.float()).all())
 
 
+# seed, b, s, h, d, rows, topk, hole, dup, fmt, rope_dim: one case per plan family
+SWEEP = [
+    (81, 3, 5, 16, 64, 40, 40, 0.2, False, "bf16", 16),       # one-wave workgroups
+    (82, 2, 33, 24, 128, 300, 260, 0.1, True, "fp8", 0),       # ragged heads and tiles, fp8 (d 128)
+    (83, 1, 3, 64, 256, 5000, 4500, 0.1, False, "bf16", 64),   # two splits and the combine kernel
+    (84, 2, 1, 64, 512, 1000, 700, 0.05, False, "fp8", 64),    # key groups, fp8 in-kernel conversion
+    (85, 4, 1, 128, 512, 2000, 640, 0.02, False, "bf16", 64),  # two key groups (window + compressed decode)
+    (86, 1, 7, 16, 512, 64, 64, 0.0, False, "bf16", 0),        # one head block, short lists
+    (87, 1, 700, 40, 512, 300, 100, 0.1, False, "bf16", 64),   # compact plan, ragged heads
+    (88, 1, 260, 128, 512, 600, 300, 0.1, False, "fp8", 64),   # dequantised rows, two head blocks per wave
+    (89, 2, 1, 64, 128, 9000, 5000, 0.3, True, "fp8", 0),      # fp8 at d 128 with splits
+    (90, 3, 20, 16, 256, 500, 1, 0.0, False, "bf16", 32),      # one column per list
+    (91, 8, 1, 64, 512, 128, 128, 0.0, False, "fp8", 64),      # window-decode shape, fp8
+    (92, 1, 64, 128, 64, 2048, 2048, 0.5, True, "fp8", 0),     # long lists at d 64, half holes
+]
+
+
+@pytest.mark.parametrize("seed,b,s,h,d,rows,topk,hole,dup,fmt,rd", SWEEP)
+def test_plan_sweep(sa, seed, b, s, h, d, rows, topk, hole, dup, fmt, rd):
+    """Random problems across the planner's branches (workgroup widths, head blocks per wave,
+    key groups, splits, the compact layout, dequantised rows), bf16 and fp8 storage, with and
+    without the inverse-RoPE epilogue, against the oracle on the same (round-tripped) rows."""
+    _say("sweep", seed, b, s, h, d, rows, topk, fmt, rd)
+    q, kv, sink, idx = W.rand_problem(seed, b, s, h, d, rows, topk, hole, dup)
+    scale = float(np.float32(d ** -0.5))
+    kv_scale = None
+    if fmt == "fp8":
+        codes, kv_scale = sa.quant_kv_fp8(kv.cuda(), want=("codes", "scales"))
+        kv_dev = codes
+        kv_ref = oracle.act_quant(u16(kv))[0]
+    else:
+        kv_dev = kv.cuda()
+        kv_ref = u16(kv)
+    rope = None
+    pos = torch.randint(0, 5000, (b, s), generator=torch.Generator().manual_seed(seed), dtype=torch.int32)
+    if rd:
+        rope = (sa.rope_table(rd, 5000, 10000.0, "cuda"), pos.cuda())
+    out = sa.sparse_attn(q.cuda(), kv_dev, sink.cuda(), idx.cuda(), scale, kv_scale=kv_scale, rope=rope)
+    got = u16(out).reshape(-1, h, d)
+    assert np.all(np.isfinite(f32_of_u16(got)))
+    ref = oracle.sparse_attn(u16(q), kv_ref.reshape(b, rows, d), sink.numpy(), idx.numpy(), scale)
+    if rd:
+        ref = oracle.apply_rotary(ref, rd, oracle.freqs_cis(rd, 5000, 10000.0), pos.view(-1).numpy(), inverse=True)
+    assert_close(got, ref, f"sweep {seed}")
+
+
 def test_strided_sequences(sa):
     """Per-sequence blocks inside larger buffers (non-packed sequence strides)."""
     q, kv, sink, idx = W.rand_problem(21, 3, 2, 32, 128, 50, 40, 0.1, False)
