@@ -40,6 +40,17 @@ __device__ __forceinline__ void store_score(__amdgpu_buffer_rsrc_t row, int pp, 
     __builtin_amdgcn_raw_buffer_store_b32(f32_bits(v), row, on ? pp * 4 : kBufferPastEnd, 0, 0);
 }
 
+// relu(x) as one median of three (x, 0, +inf): fmaxf(x, 0) costs a canonicalising max first
+// in IEEE mode. The upper bound goes through an empty asm so that the compiler cannot see it
+// is +inf (it would turn the median back into that max). NaN gives 0 (with a NaN operand the
+// median of three is their minimum), as fmaxf does.
+__device__ __forceinline__ float relu_inf() {
+    float v = INFINITY;
+    asm("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ float relu_f32(float x, float inf) { return __builtin_amdgcn_fmed3f(x, 0.0f, inf); }
+
 // S[head][position] = Q . K^T on v_mfma_f32_16x16x32_bf16: Q is the A operand (rows = 16
 // heads, held in registers), K the B operand (columns = 16 positions, loaded straight from
 // memory, one 16-byte piece per lane and k-step). In the accumulator each lane holds one
@@ -93,6 +104,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
     // Q of each query: A operand of (head block mb, k-step kk): head 16 mb + l16, d 32 kk + 8 g
     u32x4 qa[QPW][HB][KS];
     float wv[QPW][HB][4];
+    const float pinf = relu_inf();
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
         const int t = min(t0 + j, p.s - 1);
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(const IdxParams p) {
 #pragma unroll
                 for (int mb = 0; mb < HB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * fmaxf(acc[mb][r], 0.0f);
+                    for (int r = 0; r < 4; ++r) part += wv[j][mb][r] * relu_f32(acc[mb][r], pinf);
                 part = sum_xor32(sum_xor16(part));
             }
             bool keep = pp < vis[j];
@@ -203,6 +215,7 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
     const uint16_t* kseq = p.k + (int64_t)n * p.k_seq_stride;
     u32x4 qa[2][HB][KS];
     float wv[2][HB][4];
+    const float pinf = relu_inf();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int t = min(t0 + j, p.s - 1);
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
 #pragma unroll
                 for (int mb = 0; mb < HB; ++mb)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) part2[r & 1] += wv[j][mb][r] * fmaxf(acc[j][mb][r], 0.0f);
+                    for (int r = 0; r < 4; ++r) part2[r & 1] += wv[j][mb][r] * relu_f32(acc[j][mb][r], pinf);
                 const float part = sum_xor32(sum_xor16(part2[0] + part2[1]));
                 bool keep = pp < vis[j];
                 if constexpr (CAND) keep = keep && cb[nb][j] != 0;
@@ -307,6 +320,161 @@ __global__ __launch_bounds__(256) void index_scores_lds_kernel(const IdxParams p
         const int pp = it * kLdsTile + lane;
 #pragma unroll
         for (int j = 0; j < 2; ++j) store_score(srow[j], pp, pp < p.n_pos, -INFINITY);
+    }
+}
+
+// The prefill scores for 32 index heads (the model's indexer shape) on
+// v_mfma_f32_32x32x16_bf16: one 32 x 32 tile holds S[head][position] for all heads of a query
+// and 32 positions. In that accumulator lane l holds position l % 32 and 16 of the heads (the
+// other 16 are in lane l ^ 32), so the weighted head sum is 16 in-lane terms, and a single
+// permlane32 swap completes it for both of the wave's queries at once: lanes 0..31 end with
+// the first query's 32 scores, lanes 32..63 with the second's, and one store writes both rows.
+// Against the 16 x 16 form this halves the non-matrix instructions per score, which bound
+// that loop. Workgroups as in index_scores_lds_kernel (8 queries, 4 waves of 2, key tiles of
+// 64 rows staged in LDS, double-buffered), with two differences: the staged rows are padded
+// by 16 bytes instead of swizzled (the 16 rows of each operand read still fall in distinct
+// banks, and every LDS address is a fixed per-lane base plus an immediate), and the keys come
+// in through a buffer resource per tile whose rows past the workgroup's last visible position
+// read as zero (the scores of those positions are masked like any invisible one's).
+template <int D, bool CAND>
+__global__ __launch_bounds__(256) void index_scores_h32_kernel(const IdxParams p) {
+    static_assert(D == 64 || D == 128, "32-head scores: D is 64 or 128");
+    constexpr int KS = D / 16;                                  // k-steps of 16
+    constexpr int CH = D / 8;                                   // 16-byte chunks per key row
+    constexpr int RB = D * 2 + 16;                              // padded LDS row
+    constexpr int kTileBytes = kLdsTile * RB;
+    constexpr int kPer = kLdsTile * CH / 256;                   // staging loads per thread
+    constexpr int kRowsPer = 256 / CH;                          // rows per staging load
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2][kTileBytes];
+    __shared__ int vmax_s[4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int n = blockIdx.y;
+    // the wave's two queries t0, t0 + 1 (the last query groups first, as above); lane half hi
+    // stores row t0 + hi
+    const int t0 = (gridDim.x - 1 - blockIdx.x) * kLdsQueries + 2 * wid;
+    const int tl = min(t0, p.s - 1);
+    const int live = max(0, min(2, p.s - t0));                  // rows of the pair that exist
+    const int32_t* posq = p.pos + (int64_t)n * p.pos_seq_stride;
+    const int vis0 = live > 0 ? visible_positions(posq[t0], p.ratio, p.n_pos) : 0;
+    const int vis1 = live > 1 ? visible_positions(posq[t0 + 1], p.ratio, p.n_pos) : 0;
+    const int vis_l = hi ? vis1 : vis0;
+    if (lane == 0) vmax_s[wid] = max(vis0, vis1);
+    // both score rows (and candidate rows) as one buffer: stores past the live rows are dropped
+    const __amdgpu_buffer_rsrc_t srows = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.scores + (int64_t)n * p.scores_seq_stride + (int64_t)tl * p.n_pos), 0,
+        __builtin_amdgcn_readfirstlane((int)((uint32_t)live * (uint32_t)p.n_pos * 4u)), 0x00020000);
+    __amdgpu_buffer_rsrc_t crows;
+    if constexpr (CAND)
+        crows = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.cand + (int64_t)n * p.cand_seq_stride + (int64_t)tl * p.n_pos), 0,
+            __builtin_amdgcn_readfirstlane((int)((uint32_t)live * (uint32_t)p.n_pos)), 0x00020000);
+    const int rowoff = hi * p.n_pos;                            // the lane's row, in elements
+    // Q: A operand of k-step kk is head l32, d 16 kk + 8 hi; w of accumulator element r is
+    // that of head 8 (r / 4) + 4 hi + r % 4
+    u32x4 qa[2][KS];
+    float wv[2][16];
+    const float pinf = relu_inf();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = min(t0 + j, p.s - 1);
+        const uint16_t* qq = p.q + (int64_t)n * p.q_seq_stride + (int64_t)t * 32 * D + l32 * D + 8 * hi;
+        const float* ww = p.w + (int64_t)n * p.w_seq_stride + (int64_t)t * 32 + 4 * hi;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qa[j][kk] = *(const u32x4*)(qq + 16 * kk);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wv[j][r] = ww[8 * (r / 4) + r % 4];
+    }
+    __syncthreads();
+    const int vmax = __builtin_amdgcn_readfirstlane(max(max(vmax_s[0], vmax_s[1]), max(vmax_s[2], vmax_s[3])));
+    const uint16_t* kseq = p.k + (int64_t)n * p.k_seq_stride;
+    // staging: load u of thread tid moves bytes 16 (tid + 256 u) of tile tb's rows, i.e. row
+    // tid / CH + kRowsPer u, chunk tid % CH
+    u32x4 st[kPer];
+    // (the clamps below would otherwise be computed by a vector median instruction, and a
+    // buffer resource in vector registers costs a loop around every access)
+    auto fetch = [&](int tb) {
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kseq + (int64_t)tb * D), 0, __builtin_amdgcn_readfirstlane(max(0, min(kLdsTile, vmax - tb)) * D * 2),
+            0x00020000);
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            st[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, 16 * tid + 4096 * u, 0, 0));
+    };
+    const int wbase = (tid / CH) * RB + (tid % CH) * 16;
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            *(SA_LDS u32x4*)((SA_LDS uint8_t*)tiles[buf] + wbase + kRowsPer * RB * u) = st[u];
+    };
+    const int ntiles = (vmax + kLdsTile - 1) / kLdsTile;
+    const int nall = (p.n_pos + kLdsTile - 1) / kLdsTile;
+    if (ntiles > 0) {
+        fetch(0);
+        stage(0);
+    }
+    // Q, w and the first tile have landed: the loop's waits count only its own memory operations
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int rbase = l32 * RB + hi * 16;                       // B operand: row l32, chunk 2 kk + hi
+    // Each iteration issues the same memory operations on every path (as in
+    // index_scores_lds_kernel): the next tile's loads (the last one re-reads its own tile),
+    // one store per 32 positions, the staging of the next tile.
+    for (int it = 0; it < ntiles; ++it) {
+        const int tb = it * kLdsTile;
+        uint32_t cb[kLdsTile / 32];
+        if constexpr (CAND) {
+#pragma unroll
+            for (int nb = 0; nb < kLdsTile / 32; ++nb) {
+                const int pp = tb + 32 * nb + l32;
+                cb[nb] = __builtin_amdgcn_raw_buffer_load_b8(crows, pp < p.n_pos ? rowoff + pp : kBufferPastEnd, 0, 0);
+            }
+        }
+        fetch(min(tb + kLdsTile, (ntiles - 1) * kLdsTile));
+        SA_LDS const uint8_t* tile = (SA_LDS const uint8_t*)tiles[it & 1] + rbase;
+#pragma unroll
+        for (int nb = 0; nb < kLdsTile / 32; ++nb) {
+            f32x16 acc[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const u32x4 kb = *(SA_LDS const u32x4*)(tile + 32 * nb * RB + 32 * kk);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, qa[j][kk]), __builtin_bit_cast(bf16x8, kb), acc[j], 0, 0, 0);
+            }
+            float part[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float a[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int r = 0; r < 16; ++r) a[r & 1] += wv[j][r] * relu_f32(acc[j][r], pinf);
+                part[j] = a[0] + a[1];
+            }
+            // lanes 32..63 of part[0] trade places with lanes 0..31 of part[1]
+            const auto sw = __builtin_amdgcn_permlane32_swap(f32_bits(part[0]), f32_bits(part[1]), false, false);
+            const float score = bits_f32(sw[0]) + bits_f32(sw[1]);
+            const int pp = tb + 32 * nb + l32;
+            bool keep = pp < vis_l;
+            if constexpr (CAND) keep = keep && cb[nb] != 0;
+            __builtin_amdgcn_raw_buffer_store_b32(f32_bits(keep ? score : -INFINITY), srows,
+                                                  pp < p.n_pos ? (rowoff + pp) * 4 : kBufferPastEnd, 0, 0);
+        }
+        stage((it + 1) & 1);
+        __syncthreads();
+    }
+    // tiles past every query's visible positions: -inf, no keys needed
+    for (int it = ntiles; it < nall; ++it) {
+#pragma unroll
+        for (int nb = 0; nb < kLdsTile / 32; ++nb) {
+            const int pp = it * kLdsTile + 32 * nb + l32;
+            __builtin_amdgcn_raw_buffer_store_b32(f32_bits(-INFINITY), srows,
+                                                  pp < p.n_pos ? (rowoff + pp) * 4 : kBufferPastEnd, 0, 0);
+        }
     }
 }
 
@@ -790,6 +958,17 @@ __global__ __launch_bounds__(NT) void candidate_blocks_kernel(const CandParams p
 // ------------------------------------------------------------------ launches
 template <int D, int HB>
 static hipError_t launch_scores_hb(const IdxParams& p, hipStream_t st) {
+    if constexpr (HB == 2 && (D == 64 || D == 128)) {
+        // 32 heads: one buffer over a wave's two score rows stays far below the offset that
+        // stands for "past the end" while n_pos <= 2^26
+        if (p.s >= kLdsQueries && p.n_pos <= (1 << 26)) {
+            const int64_t gx = (p.s + kLdsQueries - 1) / kLdsQueries;
+            if (gx > 0x7fffffff || p.b > 65535) return hipErrorInvalidValue;
+            if (p.cand) hipLaunchKernelGGL((index_scores_h32_kernel<D, true>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL((index_scores_h32_kernel<D, false>), dim3((unsigned)gx, (unsigned)p.b), dim3(256), 0, st, p);
+            return hipGetLastError();
+        }
+    }
     if constexpr (HB * D <= 256) {
         if (p.s >= kLdsQueries) {
             const int64_t gx = (p.s + kLdsQueries - 1) / kLdsQueries;

@@ -96,6 +96,40 @@ def test_indexer_against_oracle(sa, seed, b, s, h, d, n_pos, ratio, topk, intege
     _check_structure(idx, sc, topk, off)
 
 
+@pytest.mark.parametrize("seed,b,s,d,n_pos,ratio,integer,cand", [
+    (51, 1, 37, 128, 700, 4, False, False),   # 37 queries = 4 workgroups of 8 + 5; 700 = 10 x 64 + 60 positions
+    (52, 2, 20, 64, 333, 2, True, False),     # d 64, exact integer sums; 333 = 5 x 64 + 13
+    (53, 2, 17, 128, 129, 1, True, True),     # a candidate mask; 17 = 2 x 8 + 1: one live query in the last pair
+    (54, 1, 72, 128, 2048, 4, False, False),  # causal positions from -8: the first workgroup sees nothing
+])
+def test_indexer_32_heads_prefill(sa, seed, b, s, d, n_pos, ratio, integer, cand):
+    """32 index heads with 8 or more queries per sequence (the model's indexer shape in
+    prefill): ragged query groups and position tiles, d 64 and 128, a candidate mask,
+    workgroups with no visible position. Scores against the oracle (exact for integer
+    inputs), lists against the oracle's selection."""
+    _say("indexer 32 heads", seed, b, s, d, n_pos, ratio, "integer" if integer else "random", "cand" if cand else "")
+    h, topk, off = 32, 50, 128
+    q, k, w = _inputs(seed, b, s, h, d, n_pos, integer)
+    g = torch.Generator().manual_seed(seed + 100)
+    if seed == 54:
+        pos = (torch.arange(s, dtype=torch.int32) - 8)[None].repeat(b, 1)
+    else:
+        pos = torch.randint(0, ratio * n_pos + 20, (b, s), generator=g, dtype=torch.int32)
+    cm = (torch.rand(b, s, n_pos, generator=g) < 0.5).to(torch.uint8) if cand else None
+    sc, idx = sa.indexer_topk(q.cuda(), k.cuda(), w.cuda(), pos.cuda(), ratio, topk=topk, offset=off,
+                              cand=None if cm is None else cm.cuda())
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    ref = oracle.index_scores(_u16(q), _u16(k), w.numpy(), pos.numpy(), ratio, None if cm is None else cm.numpy())
+    assert np.array_equal(np.isneginf(sc), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    if integer:
+        assert np.array_equal(sc[fin], ref[fin])
+    else:
+        assert np.all(np.abs(sc[fin] - ref[fin]) <= _score_bound(q, k, w)[fin])
+    assert np.array_equal(idx, oracle.index_topk(sc, topk, off))
+    _check_structure(idx, sc, topk, off)
+
+
 def test_indexer_candidates_and_two_levels(sa):
     """The candidate source's scores give the level-one blocks; level two scores its own
     queries inside them. Each GPU result equals the oracle's on the same GPU inputs."""
