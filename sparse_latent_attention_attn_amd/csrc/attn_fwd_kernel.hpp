@@ -658,10 +658,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
     // each probability is exp2(fma(raw, scale, -m_ref)); otherwise the scores are scaled here
     // (skipped keys set to -inf again) and the returned scale is 1. At the first tile that
     // names a row the reference is taken (O is still zero then).
+    // (IEEE maximum, v_maximum3_f32: fmaxf in IEEE mode would first canonicalise every score
+    // with a max of its own; a NaN score, which only NaN or infinite inputs make, carries over)
     auto lane_max = [&](const f32x4 (&s_acc)[2][HPW], int hb) {
-        const float t0 = fmaxf(fmaxf(s_acc[0][hb][0], s_acc[0][hb][1]), fmaxf(s_acc[0][hb][2], s_acc[0][hb][3]));
-        const float t1 = fmaxf(fmaxf(s_acc[1][hb][0], s_acc[1][hb][1]), fmaxf(s_acc[1][hb][2], s_acc[1][hb][3]));
-        return fmaxf(t0, t1);
+        const auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+        const float t0 = mx(mx(s_acc[0][hb][0], s_acc[0][hb][1]), mx(s_acc[0][hb][2], s_acc[0][hb][3]));
+        const float t1 = mx(mx(s_acc[1][hb][0], s_acc[1][hb][1]), mx(s_acc[1][hb][2], s_acc[1][hb][3]));
+        return mx(t0, t1);
     };
     auto prepare = [&](f32x4 (&s_acc)[2][HPW], uint32_t valid) {
         if (valid != 0xffffffffu) {
@@ -677,16 +680,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         }
         float sc = p.scale_log2;
         if (!(sc > 0.0f)) {
-            const uint32_t lm = valid >> (4 * q4);
+            // skipped keys are -inf by now; they stay -inf (tested on the score rather than on
+            // the mask bits, which the compiler would otherwise extract for every tile)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool keep = (lm >> (16 * mb + r)) & 1u;
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int hb = 0; hb < HPW; ++hb)
-                        s_acc[mb][hb][r] = keep ? s_acc[mb][hb][r] * sc : -INFINITY;
-                }
+                        s_acc[mb][hb][r] = s_acc[mb][hb][r] == -INFINITY ? -INFINITY : s_acc[mb][hb][r] * sc;
             sc = 1.0f;
         }
         if (!have_ref && valid != 0) {
@@ -717,7 +719,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         } else if (k < 5 * HPW) {
             const int hb = k - 4 * HPW;
             const float lm = lane_max(s_acc, hb) * sc;
-            m_seen[hb] = fmaxf(m_seen[hb], lm);
+            m_seen[hb] = __builtin_elementwise_maximum(m_seen[hb], lm);
             over |= lm > m_ref[hb] + kSlack;
         } else if (k == 5 * HPW) {
 #pragma unroll
