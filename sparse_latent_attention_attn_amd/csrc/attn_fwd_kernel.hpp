@@ -68,12 +68,24 @@ struct Geo {
     static constexpr int kTileBytes = kTileKeys * kRowBytes;
 };
 
-// Direct-to-LDS gather of one key tile (bf16 storage). The tile's row indices are read
-// from the index stage in LDS (-1 = skip). Every wave issues exactly kInsts/NW loads per
-// tile, whatever the indices, so that waiting for the oldest tile in flight is an exact
-// vmcnt: a skipped row is loaded from an offset past the end of the buffer, for which the
-// buffer's range check returns zeros without a memory access, so it lands as a zero row (a
-// zero row can never turn a zero probability into a NaN).
+// What the index stage in LDS holds per column: with bf16 storage the row's byte offset in
+// the KV buffer (row * 2 D, which the host keeps below 2^31) or kBufferPastEnd for a skip,
+// so that a gather needs one OR per load; with fp8 storage the row, or -1 for a skip. Either
+// way a column names a row exactly when its word is below kBufferPastEnd.
+template <bool FP8, int D>
+__device__ __forceinline__ int stage_word(int row) {
+    if constexpr (FP8) return row;
+    else return row < 0 ? kBufferPastEnd : row * (2 * D);
+}
+__device__ __forceinline__ bool staged_row(int w) { return (uint32_t)w < (uint32_t)kBufferPastEnd; }
+
+// Direct-to-LDS gather of one key tile (bf16 storage). The tile's byte offsets are read
+// from the index stage in LDS. Every wave issues exactly kInsts/NW loads per tile, whatever
+// the indices, so that waiting for the oldest tile in flight is an exact vmcnt: a skipped
+// row is loaded from an offset past the end of the buffer (kBufferPastEnd with the lane's
+// chunk ORed into bits it already has set), for which the buffer's range check returns zeros
+// without a memory access, so it lands as a zero row (a zero row can never turn a zero
+// probability into a NaN).
 // Wave wid issues loads wid*kPer .. wid*kPer+kPer-1 of the tile; load j covers rows
 // j*kRowsPerInst .. +kRowsPerInst-1. All row indices are read before the first load issues.
 template <int D, int NW>
@@ -87,13 +99,13 @@ __device__ __forceinline__ void gather_tile_bf16(i32x4 rsrc, SA_LDS const int32_
     const int pc = lane % G::kChunks;           // physical chunk this lane fills
     int rows[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) rows[j] = tidx[(wid * kPer + j) * G::kRowsPerInst + sub];
+    for (int j = 0; j < kPer; ++j) rows[j] = tidx[(wid * kPer + j) * G::kRowsPerInst + sub];   // byte offsets
     const uint32_t base = lds_byte_addr(buf);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int r0 = (wid * kPer + j) * G::kRowsPerInst;
         const int r = r0 + sub;
-        const int voff = rows[j] < 0 ? kBufferPastEnd : rows[j] * G::kRowBytes + ((pc ^ swz<G::kChunks>(r)) << 4);
+        const int voff = rows[j] | ((pc ^ swz<G::kChunks>(r)) << 4);
         lds_dma16(rsrc, __builtin_amdgcn_readfirstlane(base + r0 * G::kRowBytes), voff);
     }
 }
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
             int row = c < ncols && c >= gen_end ? stage_v[u] : -1;
             if (row >= p.kv_rows) { err = 1; row = -1; }
             row = row < 0 ? -1 : row;
-            if (c < ncols_pad && c >= gen_end) istage[c] = row;
+            if (c < ncols_pad && c >= gen_end) istage[c] = stage_word<FP8, D>(row);
             if (row >= 0) last = c;
         }
     }
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int c = tid; c < gen_end; c += NW * kWave) {
             int row = win_list(col_begin + c);
             if (row >= p.kv_rows) { err = 1; row = -1; }
-            istage[c] = row;
+            istage[c] = stage_word<FP8, D>(row);
             if (row >= 0) last = max(last, c);
         }
     }
@@ -773,7 +785,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
         for (int it = 0; it < ntiles; ++it) {
             SA_LDS const int32_t* tidx = istage + it * kTileKeys;
             // which columns of this tile name a row (one bit per key)
-            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tidx[lane & 31] >= 0);
+            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && staged_row(tidx[lane & 31]));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (it + 1 < ntiles)
@@ -839,7 +851,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                 lds_sync();             // super tile su visible to all
                 if (NS > 1 && su + 1 < nsuper) gather_super(su + 1);
             }
-            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && tv >= 0);
+            const uint32_t valid = (uint32_t)__ballot(lane < kTileKeys && staged_row(tv));
             if (valid != 0) {
                 SA_LDS const uint8_t* cur = tile((su % NS) * KG + kg);
                 pin_offsets();
@@ -921,7 +933,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                     if (it + kAh < ntiles)
                         gather_tile_bf16<D, NW>(kv_rsrc, tidx + kAh * kTileKeys, tile((it + kAh) % NB), wid, lane);
                 }
-                valid = (uint32_t)__ballot(lane < kTileKeys && tv >= 0);
+                valid = (uint32_t)__ballot(lane < kTileKeys && staged_row(tv));
                 pin_offsets();
                 qk(cur, s_acc);
             } else {
