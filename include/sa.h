@@ -200,7 +200,8 @@ int sa_quant_kv_fp8(const void *kv, int64_t rows, int32_t d, uint8_t *e4m3_out,
  * The input rows are the normalised latent rows (after wkv and kv_norm). A row whose
  * position is negative, or >= max_pos with rope_dim > 0, is neither stored nor written to
  * rows_out; a linear destination outside [0, cache_rows) is not stored; with
- * SA_FLAG_CHECK_IDX either case ORs bit value 4 into *err_word. */
+ * SA_FLAG_CHECK_IDX either case ORs bit value 4 into *err_word. b * s >= 2^31 is
+ * SA_ERR_UNSUPPORTED. */
 typedef struct sa_kv_write_args {
     int32_t b, s, d;        /* sequences, rows per sequence, row width (64, 128, 256, 512) */
     int32_t rope_dim;       /* 0, or even and <= d */

@@ -65,31 +65,28 @@ __device__ __forceinline__ float pow2_ceil_f32(float v) {
     return bits_f32(e << 23);
 }
 
-// |a| <= 448 (already clamped), finite. e4m3fn: bias 7, 3 mantissa bits, subnormal step
-// 2^-9. Round to nearest, ties to even.
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-    const uint32_t sign = (f32_bits(x) >> 24) & 0x80u;
-    const float a = fminf(fabsf(x), 448.0f);
-    uint32_t code;
-    if (a < 0.015625f) {
-        // subnormal grid of 2^-9: a * 512 is exact, rint rounds half to even
-        code = (uint32_t)__builtin_rintf(a * 512.0f);          // 0..8; 8 is the code of 2^-6
-    } else {
-        // keep 3 mantissa bits: add half an ulp of the target (minus one if the kept lsb is
-        // 0) and truncate; a carry into the exponent is the correct rounding up
-        uint32_t u = f32_bits(a);
-        u += 0x7ffffu + ((u >> 20) & 1u);
-        u &= 0xfff00000u;
-        const uint32_t e = (u >> 23) - 127u + 7u;             // 1..15
-        code = (e << 3) | ((u >> 20) & 7u);
-    }
-    return sign | code;
+// e4m3fn codes of eight values |y| <= 448 into two words (code k in byte k % 4 of word k / 4):
+// v_cvt_pk_fp8_f32 rounds to nearest even, with the format's subnormals (step 2^-9), and
+// saturates at 448; its codes equal the exact encode on every bf16 value of magnitude up to
+// 448 (checked exhaustively), and the values here are bf16 values times a power of two.
+__device__ __forceinline__ u32x2 e4m3_pack8(const float (&y)[8]) {
+    u32x2 w;
+    w[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)w[0], true);
+    w[1] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    w[1] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)w[1], true);
+    return w;
 }
 
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float v = e == 0 ? (float)m * 0x1p-9f : bits_f32(((e + 120u) << 23) | (m << 20));
-    return (c & 0x80u) ? -v : v;
+// The bf16 round trip code * s of eight packed codes, s a power of two: exact (at most 4
+// significant bits), and a product past the bf16 range is inf, as the f32 product is.
+__device__ __forceinline__ u32x4 e4m3_roundtrip8(u32x2 w, float s) {
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], s, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], s, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], s, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], s, true));
+    return o;
 }
 
 // One block of 32 elements per 4 lanes (8 elements = 16 bytes each); 16 blocks per wave.
@@ -115,27 +112,13 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     // x / s: s is a power of two whose reciprocal is a normal f32 (2^-120 .. 2^22), so the
     // product with the exact reciprocal rounds exactly as the division would
     const float inv_s = 1.0f / s;
-    uint32_t c[8];
+    float y[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] * inv_s);
-    if (codes) {
-        u32x2 w;
-        w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        *(u32x2*)(codes + blk * 32 + part * 8) = w;
-    }
+    for (int k = 0; k < 8; ++k) y[k] = x[k] * inv_s;
+    const u32x2 w = e4m3_pack8(y);
+    if (codes) *(u32x2*)(codes + blk * 32 + part * 8) = w;
     if (scales && part == 0) scales[blk] = (uint8_t)((f32_bits(s) >> 23) & 0xffu);
-    if (rt) {
-        u32x4 o;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // value * 2^k has at most 4 significant bits: the upper f32 half is exact bf16
-            const uint32_t lo = f32_bits(e4m3_decode(c[2 * k]) * s) >> 16;
-            const uint32_t hi = f32_bits(e4m3_decode(c[2 * k + 1]) * s) >> 16;
-            o[k] = lo | (hi << 16);
-        }
-        *(u32x4*)(rt + blk * 32 + part * 8) = o;
-    }
+    if (rt) *(u32x4*)(rt + blk * 32 + part * 8) = e4m3_roundtrip8(w, s);
 }
 
 hipError_t launch_quant_fp8(const uint16_t* kv, int64_t rows, int32_t d, uint8_t* codes,
@@ -207,8 +190,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {
     const int64_t row = gtid / kLanesPerRow;
     const int part = (int)(gtid % kLanesPerRow);
     const bool live = row < (int64_t)p.b * p.s;
-    const int n = live ? (int)(row / p.s) : 0;
-    const int t = live ? (int)(row % p.s) : 0;
+    // b * s < 2^31 (checked on the host): a 32-bit division
+    const uint32_t r32 = live ? (uint32_t)row : 0u;
+    const int n = (int)(r32 / (uint32_t)p.s);
+    const int t = (int)(r32 - (uint32_t)n * (uint32_t)p.s);
     // the row's bytes and its position are loaded side by side (one memory round trip)
     u32x4 v = live ? *(const u32x4*)(p.x + (int64_t)n * p.x_seq_stride + (int64_t)t * D + 8 * part)
                    : u32x4{0, 0, 0, 0};
@@ -254,25 +239,17 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const KvWriteParams p) {
     if ((p.flags & 1u) && part == 0 && (!pos_ok || (dst != -2 && !store))) atomicOr(p.err_word, 4);
     if (!pos_ok) return;
     const float inv_sc = 1.0f / sc;                                  // exact (a power of two)
-    uint32_t c[8];
+    float y[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = e4m3_encode(x[k] * inv_sc);
-    u32x4 rt;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t lo = f32_bits(e4m3_decode(c[2 * k]) * sc) >> 16;
-        const uint32_t hi = f32_bits(e4m3_decode(c[2 * k + 1]) * sc) >> 16;
-        rt[k] = lo | (hi << 16);
-    }
+    for (int k = 0; k < 8; ++k) y[k] = x[k] * inv_sc;
+    const u32x2 w = e4m3_pack8(y);
+    const u32x4 rt = e4m3_roundtrip8(w, sc);
     if (p.rows_out) *(u32x4*)(p.rows_out + (int64_t)n * p.rows_out_seq_stride + (int64_t)t * D + 8 * part) = rt;
     if (!store) return;
     const int64_t off = (int64_t)n * p.cache_seq_stride + dst * D + 8 * part;
     if (p.cache_bf16) {
         *(u32x4*)(p.cache_bf16 + off) = rt;
     } else {
-        u32x2 w;
-        w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
         *(u32x2*)(p.cache_codes + off) = w;
         if ((part & 3) == 0)
             p.cache_scales[(int64_t)n * p.cache_scale_seq_stride + dst * (D / 32) + part / 4] =

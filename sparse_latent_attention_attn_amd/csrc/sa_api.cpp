@@ -341,6 +341,7 @@ SA_EXPORT int sa_kv_write(const sa_kv_write_args* a, void* stream) {
     if (!a) return SA_ERR_INVALID;
     if (a->b < 1 || a->s < 1 || a->cache_rows < 1 || a->window < 0) return SA_ERR_INVALID;
     if (a->d != 64 && a->d != 128 && a->d != 256 && a->d != 512) return SA_ERR_UNSUPPORTED;
+    if ((int64_t)a->b * a->s > INT32_MAX) return SA_ERR_UNSUPPORTED;      // rows split in 32 bits
     if (a->rope_dim < 0 || a->rope_dim > a->d || (a->rope_dim & 1)) return SA_ERR_INVALID;
     if (a->kv_format != SA_KV_BF16 && a->kv_format != SA_KV_FP8_E4M3_B32) return SA_ERR_INVALID;
     if ((a->flags & ~(uint32_t)SA_FLAG_CHECK_IDX) != 0) return SA_ERR_INVALID;

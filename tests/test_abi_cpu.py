@@ -171,6 +171,11 @@ def test_kv_write_rejects_before_any_hip_call(sa, field, value, status):
     assert sa.lib().sa_kv_write(C.byref(a), None) == status
 
 
+def test_kv_write_rejects_2_to_31_rows(sa):
+    """b * s >= 2^31 rows is outside what the kernel indexes (32-bit row split)."""
+    assert sa.lib().sa_kv_write(C.byref(_kv_args(sa, b=2, s=2 ** 30)), None) == -2
+
+
 def test_kv_write_linear_needs_row0(sa):
     assert sa.lib().sa_kv_write(C.byref(_kv_args(sa, window=0)), None) == -1
     assert sa.lib().sa_kv_write(None, None) == -1

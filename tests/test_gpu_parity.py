@@ -101,6 +101,31 @@ def test_quant_bit_exact(sa, rows, d):
     assert np.array_equal(u16(rt), y)
 
 
+@pytest.mark.parametrize("k", [0, -20, 30])
+def test_quant_every_bf16_value(sa, k):
+    """Every finite bf16 value of magnitude up to 448, times 2^k, in blocks whose first
+    element 448 * 2^k fixes the scale at 2^k: all of e4m3fn's normal, subnormal, tie and
+    saturating cases go through the kernel's encode and round trip, against the oracle."""
+    _say("quant every bf16 value, scale 2^", k)
+    u = np.arange(65536, dtype=np.uint32)
+    v = (u << 16).view(np.float32)
+    v = v[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    per = 31
+    nblk = -(-v.size // per)
+    vals = np.zeros(nblk * per, np.float32)
+    vals[:v.size] = v
+    blocks = np.concatenate([np.full((nblk, 1), 448.0, np.float32), vals.reshape(nblk, per)], axis=1)
+    rows = -(-nblk // 16)
+    x = np.zeros((rows * 16, 32), np.float32)
+    x[:nblk] = blocks
+    xt = (torch.from_numpy(x.reshape(rows, 512)) * 2.0 ** k).to(torch.bfloat16)   # exact unless it underflows
+    codes, scales, rt = sa.quant_kv_fp8(xt.cuda(), want=("codes", "scales", "roundtrip"))
+    y, c_ref, s_ref = oracle.act_quant(u16(xt))
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(u16(rt), y)
+
+
 def test_quant_in_place(sa):
     x = _lognormal(5, 16, 512)
     xd = x.cuda()
