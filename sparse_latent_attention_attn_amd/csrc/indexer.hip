@@ -3,8 +3,9 @@
 //   * index_scores_kernel: score[t] = sum_h w_h relu(q_h . k_t) per query, on bf16 MFMA with
 //     f32 accumulation; positions the query cannot see (and, for the second level, positions
 //     outside the candidate mask) are -inf;
-//   * index_topk_kernel: per query, the topk best finite scores by a bitwise threshold
-//     search over keys held in registers, listed in position order (ties: the lower position
+//   * index_topk_kernel: per query, the topk best finite scores by a threshold search over
+//     keys held in registers (bit by bit with one wave per query; with several, halving a key
+//     interval bracketed from a sample), listed in position order (ties: the lower position
 //     first), shifted by the offset and padded with -1;
 //   * candidate_wave_kernel (blocks of 4, 8 or 16 in rows of whole 16-byte mask pieces) and
 //     candidate_blocks_kernel (other shapes): per query, block maxima, the newest visible
@@ -672,10 +673,11 @@ __device__ __forceinline__ int query_sum(int v, SA_LDS int* red, int& gen, int& 
 
 // W waves per query hold its scores as keys in registers: wave w, row j, lane l holds
 // position (w * J + j) * 64 + l (positions past n_pos hold key 0, as -inf does). The k-th
-// largest key is built from the top bit down: a bit stays set when at least k keys are at or
-// above the candidate; a count is the popcount of one compare ballot per row, summed over the
-// query's waves through LDS. The search ends early at a candidate with exactly k keys at or
-// above it. One ordered pass over the same registers then lists the chosen positions in
+// largest key is found with counts, a count being the popcount of one compare ballot per row,
+// summed over the query's waves through LDS: one wave builds it from the top bit down; several
+// waves (whose counts each end at a barrier) halve an interval of keys that starts between a
+// bracket taken from 64 sampled keys (each end checked by its count) or the query's largest
+// key. Both end early at a key with exactly k keys at or above it. One ordered pass over the same registers then lists the chosen positions in
 // ascending order (which is also the order the page re-sorts them into), shifted by the
 // offset; among keys equal to the threshold the lower positions are taken first. W = 1: four
 // queries per workgroup, one per wave, with no barriers at all.
@@ -705,12 +707,31 @@ __global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const
         int before;
         return block_sum(cnt, before);
     };
-    const int selectable = count_ge(1u);
+    // W > 1: the query's largest key and a sample of 64 of its keys (sample m from wave m % W,
+    // lane m, row (m + wave) % J), exchanged through LDS ahead of the first count's barrier
+    __shared__ uint32_t samp_s[64], kmax_s[W];
+    uint32_t mine = 0;
+    if constexpr (W > 1) {
+        uint32_t kmax = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            kmax = max(kmax, key[j]);
+            mine = (lane + w) % J == j ? key[j] : mine;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+        if (lane % W == w) samp_s[lane] = mine;
+        if (lane == 0) kmax_s[w] = kmax;
+    }
+    const int selectable = count_ge(1u);                         // (the barrier for those writes)
     const int k = min(p.topk, selectable);
     // chosen: key > thr, or key == thr among the first `ties` such positions
     uint32_t thr = 0;
     int ties = 0;
-    if (k > 0 && k < selectable) {
+    if (k > 0 && k < selectable && W == 1) {
+        // One wave per query: a count costs no barrier, and the k-th largest key is built from
+        // the top bit down (a bit stays set when at least k keys are at or above the
+        // candidate), ending early at a candidate with exactly k keys at or above it.
         uint32_t lo = 0;                                         // count_ge(lo) >= k throughout
         bool exact = false;
         for (int bit = 31; bit >= 0; --bit) {
@@ -727,6 +748,62 @@ __global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const
             // lo is the k-th largest key; the keys above it are fewer than k
             thr = lo;
             ties = k - (lo == 0xffffffffu ? 0 : count_ge(lo + 1));
+        }
+    } else if (k > 0 && k < selectable) {
+        // Several waves per query: every count ends at a barrier, so counts are saved by
+        // starting from a narrow interval.
+        const uint32_t samp = samp_s[lane];
+        uint32_t kmax_q = 0;
+#pragma unroll
+        for (int u = 0; u < W; ++u) kmax_q = max(kmax_q, kmax_s[u]);
+        // the r-th largest sample: the largest key with at least r samples at or above it
+        auto sample_kth = [&](int r) {
+            uint32_t v = 0;
+            for (int bit = 31; bit >= 0; --bit) {
+                const uint32_t c = v | (1u << bit);
+                if (__builtin_popcountll(__ballot(samp >= c)) >= r) v = c;
+            }
+            return v;
+        };
+        // [lo, hi) in key space with count_ge(lo) >= k > count_ge(hi) = c_hi; each count
+        // narrows it, and one of exactly k ends the search
+        uint32_t lo = 1;                                         // count_ge(1) = selectable > k
+        uint64_t hi = (uint64_t)kmax_q + 1;                      // no key above the largest
+        int c_hi = 0;
+        bool exact = false;
+        auto probe = [&](uint32_t c) {
+            const int cnt = count_ge(c);
+            if (cnt >= k) {
+                lo = c;
+                exact = cnt == k;
+            } else {
+                hi = c;
+                c_hi = cnt;
+            }
+        };
+        // A bracket from the sample: of the 64 samples, 64 k / N are expected at or above the
+        // k-th largest key (N = 64 W J key slots); the ranks 3 standard deviations and one more
+        // to either side give a key expected above it and one expected below it. Each is
+        // checked by its count, so a poor sample only leaves the interval wider.
+        const float q = (float)k / (float)(64 * W * J);
+        const float mu = 64.0f * q, sd = __builtin_sqrtf(64.0f * q * (1.0f - q));
+        const int r_above = (int)(mu - 3.0f * sd) - 1, r_below = (int)(mu + 3.0f * sd) + 2;
+        if (r_above >= 1) {
+            const uint32_t c = sample_kth(r_above);
+            if (c > lo && c < hi) probe(c);
+        }
+        if (!exact && r_below <= 64) {
+            const uint32_t c = sample_kth(r_below);
+            if (c > lo && c < hi) probe(c);
+        }
+        // then halve the interval (uniform in every wave: the same counts, the same barriers)
+        while (!exact && hi - lo > 1) probe(lo + (uint32_t)((hi - lo) >> 1));
+        if (exact) {
+            thr = lo - 1;                                        // the k keys >= lo (lo >= 1)
+        } else {
+            // lo is the k-th largest key: count_ge(lo) >= k > count_ge(lo + 1) = c_hi
+            thr = lo;
+            ties = k - c_hi;
         }
     }
     // ties met before this wave's positions
