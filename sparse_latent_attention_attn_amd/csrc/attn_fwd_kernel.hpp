@@ -203,20 +203,23 @@ struct RawGather {
         constexpr int kScRows = kTileKeys / NW;
         const int sc_row = tidx[wid * kScRows + (lane & (kScRows - 1))];
         const uint32_t base = lds_byte_addr(slot);
+        // a skipped row (-1) is loaded from past the end of the buffer: zero codes and a zero
+        // scale byte, which the conversion turns into a zero row by itself
 #pragma unroll
         for (int j = 0; j < kCodeLoads; ++j)
             lds_dma16(codes_rsrc, __builtin_amdgcn_readfirstlane(base + 2 * (wid * kCodeLoads + j) * D),
-                  max(rows[j], 0) * D + 16 * pc);
+                  rows[j] < 0 ? kBufferPastEnd : rows[j] * D + 16 * pc);
         if (lane < kScRows)
             lds_dma16(sc_rsrc, __builtin_amdgcn_readfirstlane(base + RawSlot<D>::kCodes + wid * kScRows * (D / 32)),
-                  max(sc_row, 0) * (D / 32));
+                  sc_row < 0 ? kBufferPastEnd : sc_row * (D / 32));
     }
 };
 
 // Codes of a landed raw slot -> the bf16 tile (same layout and swizzle as a gathered bf16
 // tile), on v_cvt_scalef32_pk_bf16_fp8: each code times its block's scale 2^(e - 127), which
 // is exact in bf16 (the stored values are bf16 values). A lane converts 8 codes (one 16-byte
-// bf16 chunk) per step, a wave one row; skipped columns become zero rows.
+// bf16 chunk) per step, a wave one row; skipped columns, gathered as zero codes with a zero
+// scale, become zero rows.
 template <int D, int NW>
 __device__ __forceinline__ void convert_raw_fp8(SA_LDS const uint8_t* slot, SA_LDS const int32_t* tidx,
                                                 SA_LDS uint8_t* buf, int wid, int lane) {
@@ -231,13 +234,11 @@ __device__ __forceinline__ void convert_raw_fp8(SA_LDS const uint8_t* slot, SA_L
     for (int j0 = 0; j0 < kSteps; j0 += kBatch) {
         u32x2 codes[kBatch];
         uint32_t sbyte[kBatch];
-        bool skip[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int r = (j0 + u) * NW + wid;
             codes[u] = *(SA_LDS const u32x2*)(slot + r * D + 8 * lane);
             sbyte[u] = slot[RawSlot<D>::kCodes + r * (D / 32) + (lane >> 2)];
-            skip[u] = tidx[r] < 0;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -248,7 +249,6 @@ __device__ __forceinline__ void convert_raw_fp8(SA_LDS const uint8_t* slot, SA_L
             o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][0], sc, true));
             o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][1], sc, false));
             o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[u][1], sc, true));
-            if (skip[u]) o = u32x4{0, 0, 0, 0};
             *(SA_LDS u32x4*)(buf + r * G::kRowBytes + ((lane ^ swz<G::kChunks>(r)) << 4)) = o;
         }
     }
