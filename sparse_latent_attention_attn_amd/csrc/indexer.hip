@@ -440,14 +440,27 @@ __global__ __launch_bounds__(256) void index_scores_h32_kernel(const IdxParams p
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+            u32x4 kb[KS];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) kb[kk] = *(SA_LDS const u32x4*)(tile + 32 * nb * RB + 32 * kk);
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const u32x4 kb = *(SA_LDS const u32x4*)(tile + 32 * nb * RB + 32 * kk);
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, qa[j][kk]), __builtin_bit_cast(bf16x8, kb), acc[j], 0, 0, 0);
+                        __builtin_bit_cast(bf16x8, qa[j][kk]), __builtin_bit_cast(bf16x8, kb[kk]), acc[j], 0, 0, 0);
             }
+            // Schedule: the B operands two k-steps ahead of their products (left to itself the
+            // compiler reads each just before its use and waits for it); the compiler then also
+            // runs this block's products beside the previous block's relu/weight work. 207
+            // registers, two waves per SIMD: 73.4 -> 69.4 us on 8192 queries x 2048 positions.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < KS - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             float part[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
