@@ -130,6 +130,45 @@ def test_indexer_32_heads_prefill(sa, seed, b, s, d, n_pos, ratio, integer, cand
     _check_structure(idx, sc, topk, off)
 
 
+@pytest.mark.parametrize("n_pos", [5000, 16384])
+@pytest.mark.parametrize("shape", ["all_equal", "tie_at_threshold", "outliers", "few_selectable"])
+def test_indexer_topk_adversarial_scores(sa, n_pos, shape):
+    """Score distributions that defeat a sampled bracket, for the several-waves-per-query
+    search (4 and 16 waves): every query's q_h is the first unit vector and the weights sum
+    to 1, so score_t = relu(k_t[0]) exactly. Lists bit for bit against the oracle's selection
+    on the oracle's scores."""
+    _say("indexer top-k", shape, n_pos)
+    b, s, h, d, topk = 2, 1, 32, 64, 512
+    g = torch.Generator().manual_seed(n_pos)
+    q = torch.zeros(b, s, h, d)
+    q[..., 0] = 1.0
+    w = torch.full((b, s, h), 1.0 / h)
+    k0 = torch.ones(b, n_pos)
+    if shape == "tie_at_threshold":        # 300 higher keys, then a tie across the rest
+        k0[:, torch.randperm(n_pos, generator=g)[:300]] = 2.0
+    elif shape == "outliers":              # 5 far above (a sample of 64 misses them), a band, the rest equal
+        k0[:, torch.randperm(n_pos, generator=g)[:5]] = 4096.0
+        k0[:, torch.arange(n_pos) % 7 == 0] = 3.0
+    elif shape == "few_selectable":        # most scores 0 (relu of a negative key), a band of small ones
+        k0 = -torch.ones(b, n_pos)
+        k0[:, torch.randperm(n_pos, generator=g)[:700]] = torch.randint(1, 9, (700,), generator=g).float()
+    k = torch.zeros(b, n_pos, d)
+    k[..., 0] = k0
+    k[..., 1:] = torch.randint(-3, 4, (b, n_pos, d - 1), generator=g).float()   # no effect on the score
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    pos = torch.full((b, s), 4 * n_pos + 3, dtype=torch.int32)
+    if shape == "few_selectable":
+        pos[1, 0] = 4 * 300 - 1             # sequence 1 sees 300 positions: fewer than topk
+    sc, idx = sa.indexer_topk(q.cuda(), k.cuda(), w.cuda(), pos.cuda(), 4, topk=topk, offset=0)
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    ref = oracle.index_scores(_u16(q), _u16(k), w.numpy(), pos.numpy(), 4)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(sc), np.isneginf(ref))
+    assert np.array_equal(sc[fin], ref[fin])
+    assert np.array_equal(idx, oracle.index_topk(ref, topk, 0))
+    _check_structure(idx, sc, topk, 0)
+
+
 def test_indexer_candidates_and_two_levels(sa):
     """The candidate source's scores give the level-one blocks; level two scores its own
     queries inside them. Each GPU result equals the oracle's on the same GPU inputs."""
