@@ -713,29 +713,23 @@ __global__ __launch_bounds__(W == 1 ? 256 : W * 64) void index_topk_kernel(const
     for (int j = 0; j < J; ++j) key[j] = score_key(v[j]) & (base + 64 * j + lane < p.n_pos ? ~0u : 0u);
     int gen = 0;
     auto block_sum = [&](int v, int& before) { return query_sum<W>(v, (SA_LDS int*)&red[0][0], gen, before); };
+    // A count: each lane counts its keys, DPP adds the lanes up (row shifts 1, 2, 4, 8 leave
+    // each row's total in its last lane, the row broadcasts of lanes 15 and 31 carry them on,
+    // lane 63 ends with the wave's sum), and with several waves LDS adds the waves up. Vector
+    // work only, where a compare ballot per row would add a scalar popcount and a scalar add
+    // after each compare.
     auto count_ge = [&](uint32_t c) {
-        if constexpr (W == 1) {
-            // one wave: each lane counts its keys, and DPP adds the lanes up (row shifts 1, 2,
-            // 4, 8 leave each row's total in its last lane, the row broadcasts of lanes 15 and
-            // 31 carry them on, lane 63 ends with the sum): vector work only, where a compare
-            // ballot per row would add a scalar popcount and a scalar add after each compare
-            int v = 0;
+        int v = 0;
 #pragma unroll
-            for (int j = 0; j < J; ++j) v += key[j] >= c ? 1 : 0;
-            v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
-            v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
-            v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
-            v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
-            v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
-            v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
-            return __builtin_amdgcn_readlane(v, 63);
-        } else {
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < J; ++j) cnt += __builtin_popcountll(__ballot(key[j] >= c));
-            int before;
-            return block_sum(cnt, before);
-        }
+        for (int j = 0; j < J; ++j) v += key[j] >= c ? 1 : 0;
+        v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+        v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+        v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+        v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+        v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+        v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+        int before;
+        return block_sum(__builtin_amdgcn_readlane(v, 63), before);
     };
     // W > 1: the query's largest key and a sample of 64 of its keys (sample m from wave m % W,
     // lane m, row (m + wave) % J), exchanged through LDS ahead of the first count's barrier
