@@ -435,7 +435,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_kernel(const KParams p) {
                  "s"(p.s), "s"(p.h), "s"(p.topk), "s"(p.kv_rows), "s"(p.rope_dim), "s"(p.splits),
                  "s"(p.cols_per_split), "s"(p.head_blocks));
     const int tid = threadIdx.x;
-    const int wid = tid / kWave;
+    // the wave index in a scalar register: what derives from it (key group, head group, the
+    // gather's LDS destinations) is then uniform to the compiler too
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int kg = wid / HB;                    // this wave's key group
     const int hbw = wid % HB;                   // and head group
