@@ -848,7 +848,7 @@ def main():
         pmc_summary(args.workload, args.kv, *args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(sparse_attn would shard over heads with no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")

@@ -94,7 +94,7 @@ def test_device_code(src, tmp_path):
 
 
 def test_audit_catches_a_planted_hazard():
-    # the checker itself: a VGPR write right before the MFMA and an early read of the result
+    # the audit function itself: a VGPR write right before the MFMA and an early read of the result
     lines = [";;#ASMSTART", "v_mfma_f32_16x16x32_bf16 v[0:3], v[4:7], v[8:11], 0", ";;#ASMEND",
              "v_mov_b32_e32 v20, v1", "s_nop 7"]
     assert len(audit_inline_mfma(lines)[1]) == 1
