@@ -21,10 +21,18 @@ Timing:
     device synchronisations, after W warm-up steps. The steps walk through enough distinct
     input sets (each its own q, kv, index and output buffers) that together they exceed
     twice the 256 MB Infinity Cache, and a pass over every set runs before the warm-up, so
-    the timed steps read their inputs from HBM.
+    the timed steps read their inputs from HBM. For the prefill records, ~20 ms of plain
+    device copies stream through HBM ahead of that pass (hbm_prewarm): after the idle set-up
+    the first ~40 steps of the window prefill ran up to 11% slower than its steady state (200
+    against 179 us per step), and a GPU spin that moves no memory did not change that, while
+    the copies did; with the pre-warm, W = 5 gives the step times that 50 warm-up steps of the
+    workload itself give. The decode records are short launches that 50 warm-up steps leave
+    unchanged and that such traffic slows (the 64-row KV write 3.0 -> 3.4 us), so they run
+    without it.
   * roofline: the attention kernel's own duration, from HIP events recorded on the launch
     stream around batches of back-to-back calls, after a GPU spin that lets the host enqueue
-    every launch first (no host gaps inside the intervals). achieved = algorithmic bytes
+    every launch first (no host gaps inside the intervals), then, for the prefill records,
+    the same HBM pre-warm (the spin itself moves no memory). achieved = algorithmic bytes
     (HBM-bound workloads: both decodes and the window-only prefill) or flops (the long
     prefill) per call / average duration. traffic = HBM bytes per call from the committed
     FETCH_SIZE / WRITE_SIZE counter summary of the same kernel sources
@@ -54,6 +62,7 @@ import sparse_latent_attention_attn_amd as sa  # noqa: E402
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 MALL_BYTES = 256 << 20
+PREWARM_S = 0.02                 # HBM streaming ahead of measured launches, seconds
 
 DECODE = {"decode_window", "decode_compress"}
 # The window lists are generated inside sparse_attn from the query positions (its fused
@@ -164,11 +173,27 @@ def _capture(stream, calls):
     return g
 
 
-def time_steps(sets, steps: int, warmup: int):
-    """Exactly `steps` timed steps, replayed from one captured HIP graph. Before them: one
-    pass over every input set (so each timed step's set was last touched more than twice the
-    Infinity Cache ago), then `warmup` steps on the sets the timed steps use last. Returns
-    ms per step."""
+_PREWARM_BUFS = []
+
+
+def hbm_prewarm(seconds: float = PREWARM_S):
+    """Copies between two 256 MiB device buffers, about `seconds` of HBM streaming at ~5 TB/s,
+    enqueued on the current stream ahead of measured launches: the memory clocks are then in
+    their loaded state, as in a serving loop, rather than ramping up during the measurement.
+    No step's input or output is touched."""
+    if not _PREWARM_BUFS:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        _PREWARM_BUFS.extend([a, torch.empty_like(a)])
+    a, b = _PREWARM_BUFS
+    for i in range(max(1, int(seconds / 1e-4))):        # 512 MiB of traffic per copy
+        (b if i % 2 == 0 else a).copy_(a if i % 2 == 0 else b)
+
+
+def time_steps(sets, steps: int, warmup: int, prewarm: bool = False):
+    """Exactly `steps` timed steps, replayed from one captured HIP graph. Before them: the HBM
+    pre-warm (if asked for), one pass over every input set (so each timed step's set was last touched more
+    than twice the Infinity Cache ago), then `warmup` steps on the sets the timed steps use
+    last. Returns ms per step."""
     n = len(sets)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -181,6 +206,8 @@ def time_steps(sets, steps: int, warmup: int):
     g_warm = _capture(stream, [sets[(n - 1 - i) % n].run for i in range(warmup)]) if warmup > 0 else None
     g_timed = _capture(stream, [sets[i % n].run for i in range(steps)])
     torch.cuda.synchronize()
+    if prewarm:
+        hbm_prewarm()
     g_all.replay()
     if g_warm is not None:
         g_warm.replay()
@@ -192,10 +219,10 @@ def time_steps(sets, steps: int, warmup: int):
     return dt * 1e3 / steps
 
 
-def time_kernel(sets, calls: int):
+def time_kernel(sets, calls: int, prewarm: bool = False):
     """Average duration of one sparse_attn call: events on its stream around `calls`
     back-to-back calls over the input sets, after a GPU spin that lets the host enqueue them
-    all first (so no host gap lands inside the interval). Returns (mean ms, mean ms of the
+    all first (so no host gap lands inside the interval) and, if asked for, the HBM pre-warm. Returns (mean ms, mean ms of the
     fastest of 5 such batches)."""
     st = torch.cuda.current_stream()
     # the spin must outlast the host's enqueueing of the whole batch (slower under a kernel
@@ -212,6 +239,8 @@ def time_kernel(sets, calls: int):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * spin_s))       # GPU spin while the host enqueues
+        if prewarm:
+            hbm_prewarm()
         e0.record(st)
         for i in range(calls):
             sets[i % len(sets)].attend()
@@ -475,8 +504,9 @@ def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool
             cpu_budget_s: float | None):
     """One record: step rate, kernel roofline and CPU baseline of workload w with storage kv."""
     alg, sets = prepare(w, kv, dev, epilogue)
-    ms_step = time_steps(sets, steps, warmup)
-    k_mean, k_best = time_kernel(sets, calls=min(400, max(50, steps * 5 if w.name in DECODE else steps)))
+    pw = w.name not in DECODE
+    ms_step = time_steps(sets, steps, warmup, prewarm=pw)
+    k_mean, k_best = time_kernel(sets, calls=min(400, max(50, steps * 5 if w.name in DECODE else steps)), prewarm=pw)
     if w.name in DECODE:
         value = alg["kv_bytes"] / (ms_step * 1e-3) / 1e9
         metric, unit = "sparse_attn KV GB/s (decode)", "GB/s"
@@ -517,9 +547,10 @@ def measure(w: W.Workload, kv: str, dev, steps: int, warmup: int, epilogue: bool
 
 
 # ------------------------------------------------------------------ other steps of the path
-def time_launches(fns, calls: int):
+def time_launches(fns, calls: int, prewarm: bool = False):
     """Average duration of one launch of fns[i % len(fns)]: HIP events on the current stream
-    around `calls` back-to-back launches after a GPU spin (as time_kernel). Returns (mean ms,
+    around `calls` back-to-back launches after a GPU spin and, if asked for, the HBM
+    pre-warm (as time_kernel). Returns (mean ms,
     best-batch ms)."""
     st = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -533,6 +564,8 @@ def time_launches(fns, calls: int):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * spin_s))
+        if prewarm:
+            hbm_prewarm()
         e0.record(st)
         for i in range(calls):
             fns[i % len(fns)]()
@@ -542,9 +575,9 @@ def time_launches(fns, calls: int):
     return float(np.mean(per)), float(np.min(per))
 
 
-def time_graph_steps(fns, steps: int, warmup: int):
-    """Exactly `steps` launches replayed from one captured graph after a pass over every input
-    set and `warmup` launches; ms per launch."""
+def time_graph_steps(fns, steps: int, warmup: int, prewarm: bool = False):
+    """Exactly `steps` launches replayed from one captured graph after the HBM pre-warm (if asked
+    for), a pass over every input set and `warmup` launches; ms per launch."""
     n = len(fns)
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -557,6 +590,8 @@ def time_graph_steps(fns, steps: int, warmup: int):
     g_warm = _capture(stream, [fns[(n - 1 - i) % n] for i in range(warmup)]) if warmup > 0 else None
     g_timed = _capture(stream, [fns[i % n] for i in range(steps)])
     torch.cuda.synchronize()
+    if prewarm:
+        hbm_prewarm()
     g_all.replay()
     if g_warm is not None:
         g_warm.replay()
@@ -616,8 +651,8 @@ def measure_kv_write(name: str, dev, steps: int, warmup: int, cpu: bool, profile
     if profile_calls:
         run_eager(fns, profile_calls)
         return None
-    ms_step = time_graph_steps(fns, steps, warmup)
-    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
+    ms_step = time_graph_steps(fns, steps, warmup, prewarm=want_rows)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)), prewarm=want_rows)
     achieved = alg_bytes / (k_mean * 1e-3) / 1e9
     rec = {
         "metric": "kv_write GB/s", "value": alg_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
@@ -686,9 +721,10 @@ def measure_indexer(name: str, dev, steps: int, warmup: int, cpu: bool, profile_
         run_eager(fns, profile_calls)
         run_eager(cand_fns, profile_calls)
         return None
-    ms_step = time_graph_steps(fns, steps, warmup)
-    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)))
-    c_mean, _ = time_launches(cand_fns, calls=min(400, max(50, 5 * steps)))
+    pw = kind == "prefill"
+    ms_step = time_graph_steps(fns, steps, warmup, prewarm=pw)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(50, 5 * steps)), prewarm=pw)
+    c_mean, _ = time_launches(cand_fns, calls=min(400, max(50, 5 * steps)), prewarm=pw)
     if kind == "decode":
         achieved = alg_bytes / (k_mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -768,8 +804,8 @@ def measure_proj(name: str, dev, steps: int, warmup: int, cpu: bool, profile_cal
     if profile_calls:
         run_eager(fns, profile_calls)
         return None
-    ms_step = time_graph_steps(fns, steps, warmup)
-    k_mean, k_best = time_launches(fns, calls=min(400, max(20, 5 * steps)))
+    ms_step = time_graph_steps(fns, steps, warmup, prewarm=m > 64)
+    k_mean, k_best = time_launches(fns, calls=min(400, max(20, 5 * steps)), prewarm=m > 64)
     if m <= 64:
         achieved = alg_bytes / (k_mean * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
