@@ -85,6 +85,7 @@ def test_ring_sequence_write_then_attend(sa, fmt):
 @pytest.mark.parametrize("seed,name,b,s,d,rd,window,fmt", [
     (21, "prefill chunk of 4096 tokens", 1, 4096, 512, 64, 128, "bf16"),
     (22, "prefill chunk of 4096 tokens, fp8", 1, 4096, 512, 64, 128, "fp8"),
+    (27, "the long prefill's 8192 tokens", 1, 8192, 512, 64, 128, "bf16"),
     (23, "decode, 64 sequences", 64, 1, 512, 64, 128, "bf16"),
     (24, "decode, 64 sequences, fp8", 64, 1, 512, 64, 128, "fp8"),
     (25, "short chunks, d 128", 3, 37, 128, 32, 16, "bf16"),
