@@ -154,3 +154,25 @@ def test_linear_store_and_reported_rows(sa):
     sa.kv_write(x[:3].cuda(), ok[:3].cuda(), cache[:3], rope=table, window=0, row0=row0[:3].cuda(),
                 err_word=err, check_idx=True)
     assert int(err.item()) == 0
+
+
+def test_decode_write_at_the_last_table_row(sa):
+    """64 decode rows at position 65535, the last row of a 65536-row (cos, sin) table, into
+    slot 65535 mod 128 = 127 of each ring: rows and ring bit for bit against the oracle."""
+    b, s, d, rd, window, p = 64, 1, 512, 64, 128, 65535
+    _say("kv write at the last table row", b, p)
+    x = _rows(28, b, s, d)
+    pos = torch.full((b, s), p, dtype=torch.int32)
+    table = sa.rope_table(rd, p + 1, 10000.0, "cuda")
+    cs = oracle.freqs_cis(rd, p + 1, 10000.0)
+    init = torch.randn(b, window, d, generator=torch.Generator().manual_seed(10)).to(torch.bfloat16)
+    ring = init.cuda()
+    rows = torch.empty(b, s, d, dtype=torch.bfloat16, device="cuda")
+    sa.kv_write(x.cuda(), pos.cuda(), ring, rope=table, window=window, rows_out=rows)
+    o_ring = u16(init).copy()
+    o_rows = oracle.kv_write(u16(x), pos.numpy(), rd, cs, window, window, cache_bf16=o_ring)
+    assert np.array_equal(u16(ring), o_ring)
+    assert np.array_equal(u16(rows), o_rows)
+    # only slot 127 of each ring changed
+    changed = (u16(ring) != u16(init)).any(axis=2)
+    assert not changed[:, :127].any()
